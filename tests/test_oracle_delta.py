@@ -1,0 +1,253 @@
+"""Pins for the linear-attention oracle (CPU only).
+
+Each test checks the oracle against something other than itself: a hand-worked
+example, a closed form of the delta rule, an independent matrix formulation of the
+recurrence, or a brute-force re-run over each node's root path.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+from oracle import lin_tree_verify, lin_commit_replay, lin_chain_recurrence, root_path
+from oracle.delta import bf16_bits_to_f64
+from workloads import (tree_small, tree_ddtree, tree_chain, random_root_leaf_path, rng_for,
+                       gen_lin, trees_for, f32_to_bf16_bits, pad_trees, pad_paths)
+
+
+def _handworked(golden_dir):
+    with open(os.path.join(golden_dir, "delta_handworked.json")) as f:
+        return json.load(f)
+
+
+def _single(gj):
+    """Pack the hand-worked tree as a B=1, one-head f32 problem."""
+    k = np.array(gj["k"], np.float32)[None, :, None, :]
+    q = np.array(gj["q"], np.float32)[None, :, None, :]
+    v = np.array(gj["v"], np.float32)[None, :, None, :]
+    g = np.array(gj["g"], np.float32)[None, :, None]
+    b = np.array(gj["beta"], np.float32)[None, :, None]
+    S0 = np.array(gj["S0_rc"], np.float32)
+    state = S0.T[None, None]                           # [c][r] layout
+    parent = np.array(gj["parent"], np.int32)[None]
+    return q, k, v, g, b, state, parent, np.array([3], np.int32)
+
+
+def test_handworked_tree(golden_dir):
+    gj = _handworked(golden_dir)
+    q, k, v, g, b, state, parent, n = _single(gj)
+    out, delta, states = lin_tree_verify(q, k, v, g, b, state, parent, n, 1.0, "f32", return_states=True)
+    # inputs 0.6/0.8 are fp32-rounded, so compare to the exact fractions at fp32 input precision
+    np.testing.assert_allclose(out[0, :, 0], gj["expect_out"], atol=1e-6)
+    np.testing.assert_allclose(delta[0, :, 0], gj["expect_delta"], atol=1e-6)
+    for i in range(3):
+        np.testing.assert_allclose(states[0][0][i], gj["expect_state_rc"][i], atol=1e-6)
+
+
+def test_handworked_commit(golden_dir):
+    gj = _handworked(golden_dir)
+    q, k, v, g, b, state, parent, n = _single(gj)
+    for c in gj["commit"]:
+        path = np.array(c["path"], np.int32)[None]
+        L = np.array([len(c["path"])], np.int32)
+        new = lin_commit_replay(state, path, L, k, v, g, b, parent, n, "f32")
+        np.testing.assert_allclose(new[0, 0].T, c["expect_state_rc"], atol=1e-6)
+
+
+def _random_problem(seed, n=8, Hk=2, Hv=4, dk=8, dv=6, kind="small"):
+    rng = np.random.default_rng(seed)
+    if kind == "small":
+        parent = tree_small(rng)[:n]
+    elif kind == "chain":
+        parent = tree_chain(n)
+    else:
+        parent = tree_ddtree(rng, budget=n)
+        n = len(parent)
+    q = rng.standard_normal((1, n, Hk, dk)).astype(np.float32)
+    k = rng.standard_normal((1, n, Hk, dk)).astype(np.float32)
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    q /= np.linalg.norm(q, axis=-1, keepdims=True)
+    v = rng.standard_normal((1, n, Hv, dv)).astype(np.float32)
+    g = rng.uniform(0.2, 1.0, (1, n, Hv)).astype(np.float32)
+    b = rng.uniform(0.0, 1.0, (1, n, Hv)).astype(np.float32)
+    state = rng.normal(0, 0.5, (1, Hv, dv, dk)).astype(np.float32)
+    return q, k, v, g, b, state, parent[None].astype(np.int32), np.array([n], np.int32)
+
+
+def test_identity_gate_keeps_state():
+    """g = 1, beta = 0: no update, so o_i = scale * S0^T q_i and commit leaves S0 exactly."""
+    q, k, v, g, b, state, parent, n = _random_problem(1)
+    g[:] = 1.0
+    b[:] = 0.0
+    out, delta = lin_tree_verify(q, k, v, g, b, state, parent, n, 0.5)
+    Hk, Hv = q.shape[2], v.shape[2]
+    for h in range(Hv):
+        kh = h // (Hv // Hk)
+        S0 = state[0, h].T.astype(np.float64)
+        np.testing.assert_allclose(out[0, :, h], 0.5 * q[0, :, kh].astype(np.float64) @ S0, atol=1e-12)
+    assert np.all(delta == 0)
+    path = np.array([root_path(parent[0], 5)], np.int32)
+    new = lin_commit_replay(state, path, np.array([path.shape[1]], np.int32), k, v, g, b, parent, n)
+    assert np.array_equal(new, state.astype(np.float64))
+
+
+def test_zero_gate_forgets_parent():
+    """g = 0: S_i = k_i (beta_i v_i)^T, so o_i = scale * beta_i (k_i . q_i) v_i."""
+    q, k, v, g, b, state, parent, n = _random_problem(2)
+    g[:] = 0.0
+    out, delta = lin_tree_verify(q, k, v, g, b, state, parent, n, 0.25)
+    Hk, Hv = q.shape[2], v.shape[2]
+    for i in range(int(n[0])):
+        for h in range(Hv):
+            kh = h // (Hv // Hk)
+            kq = float(k[0, i, kh].astype(np.float64) @ q[0, i, kh].astype(np.float64))
+            want = 0.25 * float(b[0, i, h]) * kq * v[0, i, h].astype(np.float64)
+            np.testing.assert_allclose(out[0, i, h], want, atol=1e-12)
+
+
+def test_one_hot_key_writes_row():
+    """k = e_r and beta = 1: row r of S_i becomes v_i; the other rows are g_i times the parent's."""
+    q, k, v, g, b, state, parent, n = _random_problem(3, dk=5, dv=7)
+    rng = np.random.default_rng(3)
+    k[:] = 0
+    rows = rng.integers(0, 5, size=k.shape[:3])
+    for i in range(k.shape[1]):
+        for kh in range(k.shape[2]):
+            k[0, i, kh, rows[0, i, kh]] = 1.0
+    b[:] = 1.0
+    _, _, states = lin_tree_verify(q, k, v, g, b, state, parent, n, 1.0, return_states=True)
+    Hk, Hv = q.shape[2], v.shape[2]
+    for h in range(Hv):
+        kh = h // (Hv // Hk)
+        for i in range(int(n[0])):
+            p = int(parent[0, i])
+            Sp = state[0, h].T.astype(np.float64) if p < 0 else states[0][h][p]
+            r = rows[0, i, kh]
+            Si = states[0][h][i]
+            np.testing.assert_allclose(Si[r], v[0, i, h], atol=1e-12)
+            others = [x for x in range(5) if x != r]
+            np.testing.assert_allclose(Si[others], g[0, i, h] * Sp[others], atol=1e-12)
+
+
+def test_delta_rule_identity():
+    """For every node: S_i^T k_i = (1 - beta |k|^2) g S_p^T k_i + beta |k|^2 v_i (the state
+    moves its prediction for k_i a fraction beta|k|^2 of the way to v_i)."""
+    q, k, v, g, b, state, parent, n = _random_problem(4, n=8)
+    k *= np.float32(1.3)   # not unit norm, so the |k|^2 factor matters
+    _, _, states = lin_tree_verify(q, k, v, g, b, state, parent, n, 1.0, return_states=True)
+    Hk, Hv = q.shape[2], v.shape[2]
+    for h in range(Hv):
+        kh = h // (Hv // Hk)
+        for i in range(int(n[0])):
+            p = int(parent[0, i])
+            Sp = state[0, h].T.astype(np.float64) if p < 0 else states[0][h][p]
+            ki = k[0, i, kh].astype(np.float64)
+            kk = ki @ ki
+            bb, gg = float(b[0, i, h]), float(g[0, i, h])
+            want = (1 - bb * kk) * gg * (Sp.T @ ki) + bb * kk * v[0, i, h]
+            np.testing.assert_allclose(states[0][h][i].T @ ki, want, atol=1e-12)
+
+
+def test_chain_matches_transition_matrix_form():
+    """A chain is a degenerate tree (PR #606, "Paper mapping").  Along a chain the state is
+    S_t = A_t S_{t-1} + beta_t k_t v_t^T with A_t = g_t (I - beta_t k_t k_t^T); this
+    product-of-transitions form is computed here with explicit dk x dk matrices."""
+    n = 7
+    q, k, v, g, b, state, parent, nn = _random_problem(5, n=n, kind="chain")
+    out, _, states = lin_tree_verify(q, k, v, g, b, state, parent, nn, 0.7, return_states=True)
+    Hk, Hv, dk = q.shape[2], v.shape[2], q.shape[3]
+    for h in range(Hv):
+        kh = h // (Hv // Hk)
+        S = state[0, h].T.astype(np.float64)
+        for t in range(n):
+            kt = k[0, t, kh].astype(np.float64)
+            A = g[0, t, h] * (np.eye(dk) - b[0, t, h] * np.outer(kt, kt))
+            S = A @ S + b[0, t, h] * np.outer(kt, v[0, t, h])
+            np.testing.assert_allclose(states[0][h][t], S, atol=1e-12)
+            np.testing.assert_allclose(out[0, t, h], 0.7 * S.T @ q[0, t, kh], atol=1e-12)
+
+
+@pytest.mark.parametrize("seed,kind", [(6, "small"), (7, "ddtree"), (8, "ddtree")])
+def test_tree_equals_per_path_replay(seed, kind):
+    """Brute force: node i's output equals the chain recurrence replayed over root_path(i)."""
+    q, k, v, g, b, state, parent, n = _random_problem(seed, n=22 if kind == "ddtree" else 8, kind=kind)
+    out, delta = lin_tree_verify(q, k, v, g, b, state, parent, n, 0.3)
+    Hk, Hv = q.shape[2], v.shape[2]
+    f = lambda a: a.astype(np.float64)
+    for i in range(int(n[0])):
+        path = root_path(parent[0], i)
+        for h in range(Hv):
+            kh = h // (Hv // Hk)
+            o, _ = lin_chain_recurrence(f(q[0, path, kh]), f(k[0, path, kh]), f(v[0, path, h]),
+                                        f(g[0, path, h]), f(b[0, path, h]), f(state[0, h].T), 0.3)
+            np.testing.assert_allclose(out[0, i, h], o[-1], atol=1e-12)
+
+
+def test_relabeling_invariance():
+    """Numbering the same tree in another topological order permutes the outputs."""
+    q, k, v, g, b, state, parent, n = _random_problem(9, n=22, kind="ddtree")
+    n0 = int(n[0])
+    # breadth-first renumbering of the same tree
+    children = [[] for _ in range(n0)]
+    for i in range(1, n0):
+        children[parent[0, i]].append(i)
+    order, frontier = [0], [0]
+    while frontier:
+        nxt = []
+        for x in frontier:
+            nxt.extend(sorted(children[x], reverse=True))
+        order.extend(nxt)
+        frontier = nxt
+    order = np.array(order)
+    new_of = np.empty(n0, int)
+    new_of[order] = np.arange(n0)
+    parent2 = np.array([[-1] + [new_of[parent[0, o]] for o in order[1:]]], np.int32)
+    out1, d1 = lin_tree_verify(q, k, v, g, b, state, parent, n, 0.5)
+    out2, d2 = lin_tree_verify(q[:, order], k[:, order], v[:, order], g[:, order], b[:, order],
+                               state, parent2, n, 0.5)
+    np.testing.assert_allclose(out2, out1[:, order], atol=1e-12)
+    np.testing.assert_allclose(d2, d1[:, order], atol=1e-12)
+
+
+def test_commit_equals_verify_state_at_path_end():
+    """Committing a root path gives the state verify reached at its last node."""
+    q, k, v, g, b, state, parent, n = _random_problem(10, n=22, kind="ddtree")
+    _, _, states = lin_tree_verify(q, k, v, g, b, state, parent, n, 1.0, return_states=True)
+    rng = np.random.default_rng(10)
+    for _ in range(4):
+        path = random_root_leaf_path(rng, parent[0], int(n[0]))
+        for L in range(1, len(path) + 1):
+            new = lin_commit_replay(state, path[None, :L], np.array([L], np.int32), k, v, g, b, parent, n)
+            for h in range(v.shape[2]):
+                np.testing.assert_allclose(new[0, h].T, states[0][h][path[L - 1]], atol=1e-12)
+
+
+def test_head_grouping():
+    """Contiguous grouping: value head h reads key head h // (Hv/Hk); tiled: h % Hk."""
+    q, k, v, g, b, state, parent, n = _random_problem(11, Hk=2, Hv=6)
+    for mode, kh_of in (("contiguous", lambda h: h // 3), ("tiled", lambda h: h % 2)):
+        out, _ = lin_tree_verify(q, k, v, g, b, state, parent, n, 1.0, head_group=mode)
+        for h in range(6):
+            kh = kh_of(h)
+            o1, _ = lin_tree_verify(q[:, :, kh:kh + 1], k[:, :, kh:kh + 1], v[:, :, h:h + 1],
+                                    g[:, :, h:h + 1], b[:, :, h:h + 1], state[:, h:h + 1], parent, n, 1.0)
+            np.testing.assert_allclose(out[:, :, h], o1[:, :, 0], atol=1e-12)
+
+
+def test_bf16_inputs_decode_exactly():
+    x = np.array([1.0, -2.5, 3.140625, 1e-3, 65504.0], np.float32)
+    bits = f32_to_bf16_bits(x)
+    got = bf16_bits_to_f64(bits)
+    # bf16 keeps 8 significant bits; these values are exact or within half an ulp
+    np.testing.assert_allclose(got, x, rtol=2 ** -8)
+    assert got[0] == 1.0 and got[1] == -2.5 and got[2] == 3.140625
+
+
+def test_generated_workload_runs():
+    parents, paths = trees_for(1, 2, "ddtree")
+    L = gen_lin(1, parents, paths, 2, 6, 16, 16, "bf16")
+    out, delta = lin_tree_verify(L.q, L.k, L.v, L.g, L.beta, L.state, L.parent, L.n_nodes, L.scale, "bf16")
+    assert np.isfinite(out).all() and np.isfinite(delta).all()
+    new = lin_commit_replay(L.state, L.path, L.path_len, L.k, L.v, L.g, L.beta, L.parent, L.n_nodes, "bf16")
+    assert np.isfinite(new).all()
