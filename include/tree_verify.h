@@ -1,0 +1,208 @@
+/*
+ * tree_verify.h -- C ABI of libtreeverify.so: the tree-verify step of a DFlash/DDTree
+ * speculative decoder on AMD Instinct MI355X (gfx950).
+ *
+ * One verify step scores every node of a draft tree (given as parent indices) through
+ * each layer of a hybrid model in one pass.  Three calls cover it:
+ *
+ *   lin_tree_verify   gated delta-rule (linear attention) layer: runs the recurrence along
+ *                     every node's root path from the committed state and captures the
+ *                     per-node factors needed to commit later;
+ *   lin_tree_commit   after acceptance, moves the committed state in place to the end of
+ *                     the accepted root path, using the captured factors;
+ *   attn_tree_verify  full-attention layer: tree-masked softmax attention over a Q8_0 /
+ *                     Q4_0 quantised KV cache with an optional sliding window.
+ *
+ * Sources (page title, section):
+ *   "Luce DFlash" server README -- "How it works" (DDTree tree verify: one forward scores
+ *     the whole tree through a mask derived from parent pointers; per-step rollback of the
+ *     recurrent state and KV cache to the committed prefix; tree-mode gated-delta-net
+ *     kernels), "Architecture note" (Gated DeltaNet layers with a recurrent state cache;
+ *     attention layers with 24 query / 4 KV heads of length 256), "Asymmetric K/V
+ *     quantization" (per-side KV types, q8_0 default; unsupported pairs are refused with
+ *     the list of supported ones) and the long-context table and flags (sliding-window
+ *     flash attention, --fa-window N, 0 = full attention).
+ *   PR #606 "perf(qwen36): add SpecLA factor-capture speculative decoding" -- "Paper
+ *     mapping" (the method consumes scored candidates plus parent topology; a chain is a
+ *     degenerate tree), "CLI" (options are validated up front; invalid combinations are
+ *     rejected, not silently changed) and the review comment naming the commit routines
+ *     (factor capture during verify, flush into the raw state on commit).
+ *
+ * Conventions for every call
+ *   - All tensors are row-major with the innermost dimension last, laid out exactly as
+ *     stated per argument.  "device" pointers are HIP device memory (or managed memory);
+ *     "host" pointers are ordinary host memory.
+ *   - The caller owns every buffer.  The library allocates nothing, keeps no state between
+ *     calls (apart from the thread-local error message) and never synchronises: work is
+ *     enqueued on `stream` (a hipStream_t; NULL = the null stream) and may run after the
+ *     call returns.  The calls can therefore be captured into a HIP graph.
+ *   - Return value: TV_OK, or an error code with a message readable through
+ *     tv_last_error().  Errors are detected on the host, before anything is enqueued; a
+ *     call that returns an error has enqueued nothing (TV_EDEVICE excepted: the launch
+ *     itself failed).
+ *   - Tree metadata lives in device memory and is not read back.  Kernels clamp every
+ *     index taken from it (parent, n_nodes, path, path_len, n_past) into range, so a
+ *     malformed tree or path can give wrong numbers but never an out-of-bounds access.
+ *     Use tv_validate_tree / tv_validate_path on host copies to check them exactly.
+ *
+ * Tree representation (both layer types)
+ *   parent  [B][N] int32, device.  parent[b][0] = -1 (node 0 is the root: the last
+ *           committed token, not yet processed); for 0 < i < n_nodes[b],
+ *           0 <= parent[b][i] < i (any topological numbering).  Entries at or beyond
+ *           n_nodes[b] are ignored.
+ *   n_nodes [B] int32, device.  1 <= n_nodes[b] <= N; N <= 64.  Rows at or beyond
+ *           n_nodes[b] of every output are left untouched.
+ *   depth(0) = 0, depth(i) = depth(parent[i]) + 1.
+ */
+#ifndef TREE_VERIFY_H
+#define TREE_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TV_ABI_VERSION 1
+#define TV_MAX_NODES 64
+
+typedef enum {
+    TV_OK = 0,
+    TV_EINVAL = 1,        /* null pointer, non-positive size, window < 0, non-finite scale */
+    TV_EUNSUPPORTED = 2,  /* dtype, head size or K/V type pair not built (message lists them) */
+    TV_ERANGE = 3,        /* N > 64, Lmax > N, workspace too small, size overflow */
+    TV_ETOPO = 4,         /* tv_validate_tree: not a rooted topological parent array */
+    TV_EPATH = 5,         /* tv_validate_path: not a root path of the tree */
+    TV_EDEVICE = 6        /* a kernel launch failed (message carries the HIP error) */
+} tv_status;
+
+typedef enum { TV_F32 = 0, TV_BF16 = 1 } tv_dtype;
+
+/* Which key head a value head reads (linear layer, Hv a multiple of Hk).
+ * CONTIGUOUS: value head h reads key head h / (Hv / Hk)   (default)
+ * TILED:      value head h reads key head h % Hk                      */
+typedef enum { TV_HEADS_CONTIGUOUS = 0, TV_HEADS_TILED = 1 } tv_head_group;
+
+/* KV cache block formats (GGUF block convention, 32 elements per block):
+ * Q8_0: 34 bytes {fp16 d (little-endian); int8 q[32]}, x[e] = d * q[e].
+ * Q4_0: 18 bytes {fp16 d; uint8 qs[16]}, x[e] = d * ((qs[e] & 15) - 8) for e < 16 and
+ *       x[e + 16] = d * ((qs[e] >> 4) - 8).                                          */
+typedef enum { TV_Q8_0 = 0, TV_Q4_0 = 1 } tv_kv_type;
+
+/*
+ * lin_tree_verify -- one gated delta-rule layer over the draft tree.
+ * ("Luce DFlash" README, "How it works" and "Architecture note"; PR #606, "Paper mapping".)
+ *
+ * For sequence b, value head h (key head kh per head_group) and node i with parent p, with
+ * S_{-1} the committed state S0 (a dk x dv matrix mapping keys to values):
+ *     u_i     = S_p^T k_i
+ *     delta_i = beta_i * (v_i - g_i * u_i)
+ *     S_i     = g_i * S_p + k_i delta_i^T
+ *     out_i   = scale * S_i^T q_i
+ * Per-node states S_i are never materialised and `state` is not modified: rolling back is
+ * free.  delta_i is written to cap_delta for lin_tree_commit.
+ *
+ *   B, N       sequences; tree rows per sequence (1 <= N <= 64)
+ *   Hk, Hv     key heads, value heads (Hv % Hk == 0)
+ *   dk, dv     head sizes, each one of 16, 32, 64, 128
+ *   dtype      TV_F32 or TV_BF16: element type of q, k, v, g, beta
+ *   head_group tv_head_group
+ *   scale      output scale (usually 1/sqrt(dk)); finite
+ *   parent, n_nodes   device, see "Tree representation"
+ *   q, k       device, [B][N][Hk][dk]   (already normalised by the caller)
+ *   v          device, [B][N][Hv][dv]
+ *   g, beta    device, [B][N][Hv]       (g: multiplicative decay in (0, 1])
+ *   state      device, fp32 [B][Hv][dv][dk]: state[b][h][c][r] = S0[r][c] (one row of dk
+ *              keys per value channel c).  Read only.
+ *   out        device, fp32 [B][N][Hv][dv]
+ *   cap_delta  device, fp32 [B][N][Hv][dv]: delta_i, consumed by lin_tree_commit
+ */
+int lin_tree_verify(int B, int N, int Hk, int Hv, int dk, int dv, int dtype, int head_group,
+                    float scale, const int32_t* parent, const int32_t* n_nodes,
+                    const void* q, const void* k, const void* v, const void* g, const void* beta,
+                    const float* state, float* out, float* cap_delta, void* stream);
+
+/*
+ * lin_tree_commit -- move the committed state to the end of the accepted root path.
+ * ("Luce DFlash" README, "How it works": after accept, the recurrent state is the
+ * committed prefix; PR #606 review comment: captured factors are flushed into the raw
+ * state on commit.)
+ *
+ * With accepted path a_0 = 0, a_1, ..., a_{L-1} (each a child of the previous) and
+ * c_m = prod_{m < m' < L} g_{a_m'} (empty product = 1):
+ *     S <- (prod_{m < L} g_{a_m}) * S0 + sum_m c_m * k_{a_m} delta_{a_m}^T
+ * which equals replaying the recurrence over the accepted tokens alone.  path_len[b] = 0
+ * leaves sequence b's state unchanged.
+ *
+ *   B, N, Hk, Hv, dk, dv, dtype, head_group   as for lin_tree_verify (same call's values)
+ *   path       device, int32 [B][Lmax]; entries at or beyond path_len[b] are ignored
+ *   path_len   device, int32 [B]; 0 <= path_len[b] <= min(Lmax, n_nodes[b])
+ *   Lmax       1 <= Lmax <= N
+ *   k          device, [B][N][Hk][dk] (the tensor given to lin_tree_verify)
+ *   g          device, [B][N][Hv]
+ *   cap_delta  device, fp32 [B][N][Hv][dv], written by lin_tree_verify
+ *   state      device, fp32 [B][Hv][dv][dk], updated in place
+ */
+int lin_tree_commit(int B, int N, int Hk, int Hv, int dk, int dv, int dtype, int head_group,
+                    const int32_t* path, const int32_t* path_len, int Lmax,
+                    const void* k, const void* g, const float* cap_delta, float* state,
+                    void* stream);
+
+/*
+ * attn_tree_workspace_bytes -- device workspace attn_tree_verify needs for these sizes
+ * (0 if the sizes are invalid).  The workspace holds per-split partial results.
+ */
+size_t attn_tree_workspace_bytes(int B, int N, int Hq, int Hkv, int D, int Tcap, int window);
+
+/*
+ * attn_tree_verify -- one full-attention layer over the draft tree.
+ * ("Luce DFlash" README, "How it works", "Architecture note", the FA-window flag and
+ * "Asymmetric K/V quantization".)
+ *
+ * Sequence b has T = n_past[b] committed slots; tree node j's K/V are in slot T + j.
+ * Committed slot t sits at position t and tree node j at T + depth(j).  Query node i (at
+ * position T + depth(i)) attends to committed slot t iff window == 0 or
+ * T + depth(i) - t < window, and to tree slot T + j iff j is on i's root path (itself
+ * included) and (window == 0 or depth(i) - depth(j) < window).  Query head h reads KV
+ * head h / (Hq / Hkv).
+ *     out[b][i][h] = sum_t softmax_t(scale * <q, K_t>) V_t        lse = log sum_t exp(...)
+ *
+ *   B, N       sequences; tree rows per sequence (1 <= N <= 64)
+ *   Hq, Hkv    query heads, KV heads (Hq % Hkv == 0, Hq / Hkv <= 8)
+ *   D          head size: 256 (also 128)
+ *   Tcap       slots per (sequence, KV head) row of the cache; n_past[b] + n_nodes[b] <= Tcap
+ *   k_type, v_type   tv_kv_type of each cache ({Q8_0, Q4_0} x {Q8_0, Q4_0})
+ *   window     0 = full attention, else the window W > 0
+ *   scale      score scale (usually 1/sqrt(D)); finite
+ *   parent, n_nodes  device, see "Tree representation"
+ *   n_past     device, int32 [B]
+ *   q          device, bf16 [B][N][Hq][D]; |q| must stay below 65504 (converted to fp16)
+ *   k_cache    device, bytes [B][Hkv][Tcap][D/32 blocks of k_type]
+ *   v_cache    device, bytes [B][Hkv][Tcap][D/32 blocks of v_type]
+ *   out        device, fp32 [B][N][Hq][D]
+ *   lse        device, fp32 [B][N][Hq] (natural log) or NULL
+ *   workspace  device, >= attn_tree_workspace_bytes(...) bytes, 256-byte aligned; its
+ *              contents need no initialisation and are garbage afterwards
+ */
+int attn_tree_verify(int B, int N, int Hq, int Hkv, int D, int Tcap, int k_type, int v_type,
+                     int window, float scale, const int32_t* parent, const int32_t* n_nodes,
+                     const int32_t* n_past, const void* q, const void* k_cache,
+                     const void* v_cache, float* out, float* lse, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
+/* Host-side checks of tree metadata (host pointers).  TV_OK or TV_ETOPO / TV_EPATH /
+ * TV_EINVAL / TV_ERANGE with a message naming the first offending entry. */
+int tv_validate_tree(const int32_t* parent, const int32_t* n_nodes, int B, int N);
+int tv_validate_path(const int32_t* parent, const int32_t* n_nodes, const int32_t* path,
+                     const int32_t* path_len, int B, int N, int Lmax);
+
+/* Message of the last error on the calling thread ("" if none).  Valid until the next
+ * call from the same thread. */
+const char* tv_last_error(void);
+int tv_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TREE_VERIFY_H */

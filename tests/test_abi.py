@@ -1,0 +1,133 @@
+"""The C ABI without a GPU: the library loads, exports every declared symbol, and every
+argument error is reported on the host before anything is launched."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import tree_verify_linear_amd as tvl
+from workloads import trees_for, pad_trees, pad_paths
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _header_functions():
+    src = open(os.path.join(ROOT, "include", "tree_verify.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(\w+)\s*\(", src, flags=re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _header_functions()
+    assert {"lin_tree_verify", "lin_tree_commit", "attn_tree_verify", "attn_tree_workspace_bytes",
+            "tv_validate_tree", "tv_validate_path", "tv_last_error", "tv_abi_version"} <= set(names)
+    L = tvl.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(tvl.EXPORTS), "binding and header disagree"
+    assert tvl.abi_version() == 1
+
+
+def _fake():
+    return ctypes.c_void_p(4096)  # never dereferenced: every call below fails its host checks
+
+
+def _verify_call(**kw):
+    a = dict(B=1, N=8, Hk=1, Hv=1, dk=16, dv=16, dtype=0, head_group=0, scale=0.25)
+    a.update(kw)
+    f = _fake()
+    return tvl.lib().lin_tree_verify(a["B"], a["N"], a["Hk"], a["Hv"], a["dk"], a["dv"], a["dtype"],
+                                     a["head_group"], a["scale"], *([kw.get("ptr", f)] * 11))
+
+
+def test_verify_argument_errors():
+    L = tvl.lib()
+    assert _verify_call(B=0) == tvl.TV_EINVAL
+    assert b"positive" in L.tv_last_error()
+    assert _verify_call(N=65) == tvl.TV_ERANGE
+    assert _verify_call(dk=48) == tvl.TV_EUNSUPPORTED
+    assert b"16, 32, 64, 128" in L.tv_last_error()
+    assert _verify_call(dv=256) == tvl.TV_EUNSUPPORTED
+    assert _verify_call(dtype=7) == tvl.TV_EUNSUPPORTED
+    assert _verify_call(Hk=2, Hv=3) == tvl.TV_EINVAL
+    assert _verify_call(head_group=5) == tvl.TV_EINVAL
+    assert _verify_call(scale=float("nan")) == tvl.TV_EINVAL
+    assert _verify_call(ptr=None) == tvl.TV_EINVAL
+    assert b"null" in L.tv_last_error()
+    assert _verify_call(ptr=ctypes.c_void_p(18)) == tvl.TV_EINVAL      # misaligned
+    assert b"aligned" in L.tv_last_error()
+
+
+def test_commit_argument_errors():
+    L = tvl.lib()
+    f = _fake()
+    assert L.lin_tree_commit(1, 8, 1, 1, 16, 16, 0, 0, f, f, 0, f, f, f, f, f) == tvl.TV_ERANGE   # Lmax 0
+    assert L.lin_tree_commit(1, 8, 1, 1, 16, 16, 0, 0, f, f, 9, f, f, f, f, f) == tvl.TV_ERANGE   # Lmax > N
+    assert L.lin_tree_commit(1, 8, 1, 1, 16, 16, 0, 0, None, f, 4, f, f, f, f, f) == tvl.TV_EINVAL
+    assert L.lin_tree_commit(1, 8, 1, 1, 12, 16, 0, 0, f, f, 4, f, f, f, f, f) == tvl.TV_EUNSUPPORTED
+
+
+def test_attention_argument_errors():
+    L = tvl.lib()
+    f = _fake()
+    base = [1, 22, 24, 4, 256, 4200, 0, 0, 2048, 0.0625]
+
+    def call(**kw):
+        a = list(base)
+        for i, key in enumerate(["B", "N", "Hq", "Hkv", "D", "Tcap", "kt", "vt", "W", "scale"]):
+            if key in kw:
+                a[i] = kw[key]
+        ws = kw.get("ws", 1 << 30)
+        return L.attn_tree_verify(*a, *([kw.get("ptr", f)] * 8), f, ws, None)
+
+    assert call(Hq=25) == tvl.TV_EINVAL
+    assert call(Hq=40, Hkv=4) == tvl.TV_EUNSUPPORTED              # 10 query heads per KV head
+    assert call(D=192) == tvl.TV_EUNSUPPORTED
+    assert call(kt=2) == tvl.TV_EUNSUPPORTED
+    assert b"supported pairs" in L.tv_last_error()
+    assert call(W=-1) == tvl.TV_EINVAL
+    assert call(N=65) == tvl.TV_ERANGE
+    assert call(scale=float("inf")) == tvl.TV_EINVAL
+    assert call(ptr=None) == tvl.TV_EINVAL
+    need = tvl.attn_tree_workspace_bytes(1, 22, 24, 4, 256, 4200, 2048)
+    assert need > 0
+    assert call(ws=need - 1) == tvl.TV_ERANGE
+    assert b"workspace" in L.tv_last_error()
+    assert tvl.attn_tree_workspace_bytes(1, 22, 24, 5, 256, 4200, 2048) == 0
+
+
+def test_validate_tree_and_path():
+    parents, paths = trees_for(1, 3, "ddtree")
+    parent, n = pad_trees(parents)
+    path, L = pad_paths(paths)
+    tvl.validate_tree(parent, n)
+    tvl.validate_path(parent, n, path, L)
+
+    bad = parent.copy(); bad[1, 5] = 7                       # a later node
+    with pytest.raises(tvl.TreeVerifyError) as e:
+        tvl.validate_tree(bad, n)
+    assert e.value.code == tvl.TV_ETOPO and "parent[1][5]=7" in str(e.value)
+    bad = parent.copy(); bad[0, 0] = 0
+    with pytest.raises(tvl.TreeVerifyError):
+        tvl.validate_tree(bad, n)
+    with pytest.raises(tvl.TreeVerifyError):
+        tvl.validate_tree(parent, np.array([22, 0, 22], np.int32))
+    with pytest.raises(tvl.TreeVerifyError):
+        tvl.validate_tree(parent, np.array([22, 23, 22], np.int32))
+
+    badp = path.copy(); badp[0, 0] = 1
+    with pytest.raises(tvl.TreeVerifyError) as e:
+        tvl.validate_path(parent, n, badp, L)
+    assert e.value.code == tvl.TV_EPATH
+    # a node that is not the child of its predecessor
+    badp = path.copy()
+    sib = [i for i in range(1, 22) if parent[2, i] != path[2, 0] and i != path[2, 1]][0]
+    badp[2, 1] = sib
+    with pytest.raises(tvl.TreeVerifyError):
+        tvl.validate_path(parent, n, badp, L)
+    with pytest.raises(tvl.TreeVerifyError):
+        tvl.validate_path(parent, n, path, L + 30)
+    ok0 = np.zeros_like(L)
+    tvl.validate_path(parent, n, path, ok0)                # empty paths are allowed

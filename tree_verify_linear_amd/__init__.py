@@ -1,0 +1,195 @@
+"""Python binding of libtreeverify.so -- argument marshalling only.
+
+Every step of the tree-verify path runs in the library's HIP kernels; this module only
+checks tensor shapes/dtypes, allocates outputs with PyTorch when the caller does not
+pass them, and forwards raw device pointers and the current HIP stream.  If the library
+is not built, every call raises: there is no fallback.
+
+Layouts (row-major, innermost last) are those of ``include/tree_verify.h``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = ["TreeVerifyError", "lib", "lib_path", "lin_tree_verify", "lin_tree_commit",
+           "attn_tree_verify", "attn_tree_workspace_bytes", "validate_tree", "validate_path",
+           "abi_version", "KV_TYPES", "EXPORTS"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+TV_OK, TV_EINVAL, TV_EUNSUPPORTED, TV_ERANGE, TV_ETOPO, TV_EPATH, TV_EDEVICE = range(7)
+TV_F32, TV_BF16 = 0, 1
+HEAD_GROUPS = {"contiguous": 0, "tiled": 1}
+KV_TYPES = {"q8_0": 0, "q4_0": 1}
+KV_BLOCK_BYTES = {"q8_0": 34, "q4_0": 18}
+
+_i, _f, _p, _sz = ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
+EXPORTS = {
+    "lin_tree_verify": (_i, [_i, _i, _i, _i, _i, _i, _i, _i, _f, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p]),
+    "lin_tree_commit": (_i, [_i, _i, _i, _i, _i, _i, _i, _i, _p, _p, _i, _p, _p, _p, _p, _p]),
+    "attn_tree_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
+    "attn_tree_verify": (_i, [_i, _i, _i, _i, _i, _i, _i, _i, _i, _f, _p, _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
+    "tv_validate_tree": (_i, [_p, _p, _i, _i]),
+    "tv_validate_path": (_i, [_p, _p, _p, _p, _i, _i, _i]),
+    "tv_last_error": (ctypes.c_char_p, []),
+    "tv_abi_version": (_i, []),
+}
+
+
+class TreeVerifyError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"[tv status {code}] {message}")
+        self.code = code
+
+
+def lib_path() -> str:
+    return os.path.join(_HERE, "libtreeverify.so")
+
+
+def lib() -> ctypes.CDLL:
+    global _LIB
+    if _LIB is None:
+        path = lib_path()
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is not built; run `python -m tree_verify_linear_amd.build`")
+        L = ctypes.CDLL(path)
+        for name, (res, args) in EXPORTS.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _LIB = L
+    return _LIB
+
+
+def _check(code: int) -> None:
+    if code != TV_OK:
+        raise TreeVerifyError(code, lib().tv_last_error().decode())
+
+
+def abi_version() -> int:
+    return lib().tv_abi_version()
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor (got {t.device})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t
+
+
+def _in_dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return TV_BF16
+    if t.dtype == torch.float32:
+        return TV_F32
+    raise TypeError(f"inputs must be bfloat16 or float32, got {t.dtype}")
+
+
+def lin_tree_verify(q, k, v, g, beta, state, parent, n_nodes, scale: float, head_group: str = "contiguous",
+                    out=None, cap_delta=None):
+    """Gated delta-rule layer over the draft tree.  Returns ``(out, cap_delta)``, fp32
+    ``[B][N][Hv][dv]``.  ``state`` (fp32 ``[B][Hv][dv][dk]``) is read, never written."""
+    B, N, Hk, dk = q.shape
+    Hv, dv = v.shape[2], v.shape[3]
+    dt = q.dtype
+    _dev(q, "q", dt); _dev(k, "k", dt, (B, N, Hk, dk)); _dev(v, "v", dt, (B, N, Hv, dv))
+    _dev(g, "g", dt, (B, N, Hv)); _dev(beta, "beta", dt, (B, N, Hv))
+    _dev(state, "state", torch.float32, (B, Hv, dv, dk))
+    _dev(parent, "parent", torch.int32, (B, N)); _dev(n_nodes, "n_nodes", torch.int32, (B,))
+    if out is None:
+        out = torch.empty((B, N, Hv, dv), dtype=torch.float32, device=q.device)
+    if cap_delta is None:
+        cap_delta = torch.empty((B, N, Hv, dv), dtype=torch.float32, device=q.device)
+    _dev(out, "out", torch.float32, (B, N, Hv, dv)); _dev(cap_delta, "cap_delta", torch.float32, (B, N, Hv, dv))
+    _check(lib().lin_tree_verify(B, N, Hk, Hv, dk, dv, _in_dtype(q), HEAD_GROUPS[head_group], float(scale),
+                                 _ptr(parent), _ptr(n_nodes), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                 _ptr(state), _ptr(out), _ptr(cap_delta), _stream(q.device)))
+    return out, cap_delta
+
+
+def lin_tree_commit(state, path, path_len, k, g, cap_delta, head_group: str = "contiguous"):
+    """Move ``state`` in place to the end of each sequence's accepted root path."""
+    B, Hv, dv, dk = state.shape
+    N, Hk = k.shape[1], k.shape[2]
+    Lmax = path.shape[1]
+    _dev(state, "state", torch.float32)
+    _dev(k, "k", (torch.bfloat16, torch.float32), (B, N, Hk, dk)); _dev(g, "g", k.dtype, (B, N, Hv))
+    _dev(cap_delta, "cap_delta", torch.float32, (B, N, Hv, dv))
+    _dev(path, "path", torch.int32, (B, Lmax)); _dev(path_len, "path_len", torch.int32, (B,))
+    _check(lib().lin_tree_commit(B, N, Hk, Hv, dk, dv, _in_dtype(k), HEAD_GROUPS[head_group], _ptr(path),
+                                 _ptr(path_len), Lmax, _ptr(k), _ptr(g), _ptr(cap_delta), _ptr(state),
+                                 _stream(state.device)))
+    return state
+
+
+def attn_tree_workspace_bytes(B: int, N: int, Hq: int, Hkv: int, D: int, Tcap: int, window: int) -> int:
+    return int(lib().attn_tree_workspace_bytes(B, N, Hq, Hkv, D, Tcap, window))
+
+
+def attn_tree_verify(q, k_cache, v_cache, k_type: str, v_type: str, n_past, parent, n_nodes, window: int,
+                     scale: float, out=None, lse=None, workspace=None, want_lse: bool = True):
+    """Tree-masked attention over the quantised cache.  Returns ``(out, lse)``: fp32
+    ``[B][N][Hq][D]`` and ``[B][N][Hq]`` (``lse`` is None when ``want_lse`` is False)."""
+    B, N, Hq, D = q.shape
+    Hkv, Tcap = k_cache.shape[1], k_cache.shape[2]
+    _dev(q, "q", torch.bfloat16)
+    _dev(k_cache, "k_cache", torch.uint8, (B, Hkv, Tcap, D // 32 * KV_BLOCK_BYTES[k_type]))
+    _dev(v_cache, "v_cache", torch.uint8, (B, Hkv, Tcap, D // 32 * KV_BLOCK_BYTES[v_type]))
+    _dev(n_past, "n_past", torch.int32, (B,))
+    _dev(parent, "parent", torch.int32, (B, N)); _dev(n_nodes, "n_nodes", torch.int32, (B,))
+    if out is None:
+        out = torch.empty((B, N, Hq, D), dtype=torch.float32, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, N, Hq), dtype=torch.float32, device=q.device)
+    _dev(out, "out", torch.float32, (B, N, Hq, D))
+    if lse is not None:
+        _dev(lse, "lse", torch.float32, (B, N, Hq))
+    need = attn_tree_workspace_bytes(B, N, Hq, Hkv, D, Tcap, window)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    _dev(workspace, "workspace", torch.uint8)
+    _check(lib().attn_tree_verify(B, N, Hq, Hkv, D, Tcap, KV_TYPES[k_type], KV_TYPES[v_type], int(window),
+                                  float(scale), _ptr(parent), _ptr(n_nodes), _ptr(n_past), _ptr(q), _ptr(k_cache),
+                                  _ptr(v_cache), _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
+                                  _stream(q.device)))
+    return out, lse
+
+
+def _host_i32(a, name):
+    t = torch.as_tensor(a, dtype=torch.int32).contiguous()
+    if t.device.type != "cpu":
+        raise ValueError(f"{name} must be a host array for validation")
+    return t
+
+
+def validate_tree(parent, n_nodes) -> None:
+    """Exact host-side check of tree metadata; raises TreeVerifyError (TV_ETOPO, ...)."""
+    p, n = _host_i32(parent, "parent"), _host_i32(n_nodes, "n_nodes")
+    B, N = p.shape
+    _check(lib().tv_validate_tree(_ptr(p), _ptr(n), B, N))
+
+
+def validate_path(parent, n_nodes, path, path_len) -> None:
+    p, n = _host_i32(parent, "parent"), _host_i32(n_nodes, "n_nodes")
+    a, L = _host_i32(path, "path"), _host_i32(path_len, "path_len")
+    B, N = p.shape
+    _check(lib().tv_validate_path(_ptr(p), _ptr(n), _ptr(a), _ptr(L), B, N, a.shape[1]))

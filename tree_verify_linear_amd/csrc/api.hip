@@ -1,0 +1,176 @@
+// C entry points of libtreeverify.so: argument checks, error reporting, dispatch.
+// Every check runs on the host before anything is enqueued; see include/tree_verify.h.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "tv_internal.h"
+
+namespace tv {
+
+static thread_local char g_err[512] = "";
+
+int set_error(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+void clear_error() { g_err[0] = '\0'; }
+
+int launch_status(const char* what) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return set_error(TV_EDEVICE, "%s: launch failed: %s", what, hipGetErrorString(e));
+    return TV_OK;
+}
+
+static bool aligned(const void* p, size_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+static bool head_size_ok(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+
+static int check_common_lin(const char* fn, int B, int N, int Hk, int Hv, int dk, int dv, int dtype,
+                            int head_group) {
+    if (B <= 0 || N <= 0 || Hk <= 0 || Hv <= 0 || dk <= 0 || dv <= 0)
+        return set_error(TV_EINVAL, "%s: sizes must be positive (B=%d N=%d Hk=%d Hv=%d dk=%d dv=%d)", fn, B, N,
+                         Hk, Hv, dk, dv);
+    if (N > TV_MAX_NODES) return set_error(TV_ERANGE, "%s: N=%d exceeds %d tree nodes", fn, N, TV_MAX_NODES);
+    if (Hv % Hk != 0) return set_error(TV_EINVAL, "%s: Hv=%d is not a multiple of Hk=%d", fn, Hv, Hk);
+    if (!head_size_ok(dk) || !head_size_ok(dv))
+        return set_error(TV_EUNSUPPORTED, "%s: dk=%d dv=%d not built; supported head sizes: 16, 32, 64, 128", fn,
+                         dk, dv);
+    if (dtype != TV_F32 && dtype != TV_BF16)
+        return set_error(TV_EUNSUPPORTED, "%s: dtype %d not built; supported: TV_F32, TV_BF16", fn, dtype);
+    if (head_group != TV_HEADS_CONTIGUOUS && head_group != TV_HEADS_TILED)
+        return set_error(TV_EINVAL, "%s: head_group %d is not TV_HEADS_CONTIGUOUS or TV_HEADS_TILED", fn,
+                         head_group);
+    const double elems = static_cast<double>(B) * N * (Hv > Hk ? Hv : Hk) * (dk > dv ? dk : dv);
+    if (elems > 9.0e15) return set_error(TV_ERANGE, "%s: tensor sizes overflow", fn);
+    return TV_OK;
+}
+
+}  // namespace tv
+
+using namespace tv;
+
+extern "C" {
+
+int tv_abi_version(void) { return TV_ABI_VERSION; }
+
+const char* tv_last_error(void) { return g_err; }
+
+int tv_validate_tree(const int32_t* parent, const int32_t* n_nodes, int B, int N) {
+    clear_error();
+    if (!parent || !n_nodes) return set_error(TV_EINVAL, "tv_validate_tree: null pointer");
+    if (B <= 0 || N <= 0) return set_error(TV_EINVAL, "tv_validate_tree: B=%d N=%d must be positive", B, N);
+    if (N > TV_MAX_NODES) return set_error(TV_ERANGE, "tv_validate_tree: N=%d exceeds %d", N, TV_MAX_NODES);
+    for (int b = 0; b < B; ++b) {
+        const int n = n_nodes[b];
+        if (n < 1 || n > N) return set_error(TV_ETOPO, "tv_validate_tree: n_nodes[%d]=%d not in [1, %d]", b, n, N);
+        const int32_t* p = parent + static_cast<size_t>(b) * N;
+        if (p[0] != -1) return set_error(TV_ETOPO, "tv_validate_tree: parent[%d][0]=%d, the root must be -1", b, p[0]);
+        for (int i = 1; i < n; ++i)
+            if (p[i] < 0 || p[i] >= i)
+                return set_error(TV_ETOPO, "tv_validate_tree: parent[%d][%d]=%d is not an earlier node", b, i, p[i]);
+    }
+    return TV_OK;
+}
+
+int tv_validate_path(const int32_t* parent, const int32_t* n_nodes, const int32_t* path, const int32_t* path_len,
+                     int B, int N, int Lmax) {
+    const int st = tv_validate_tree(parent, n_nodes, B, N);
+    if (st != TV_OK) return st;
+    if (!path || !path_len) return set_error(TV_EINVAL, "tv_validate_path: null pointer");
+    if (Lmax < 1 || Lmax > N) return set_error(TV_ERANGE, "tv_validate_path: Lmax=%d not in [1, N=%d]", Lmax, N);
+    for (int b = 0; b < B; ++b) {
+        const int L = path_len[b], n = n_nodes[b];
+        if (L < 0 || L > Lmax || L > n)
+            return set_error(TV_EPATH, "tv_validate_path: path_len[%d]=%d not in [0, min(Lmax, n_nodes)]", b, L);
+        const int32_t* a = path + static_cast<size_t>(b) * Lmax;
+        const int32_t* p = parent + static_cast<size_t>(b) * N;
+        if (L > 0 && a[0] != 0) return set_error(TV_EPATH, "tv_validate_path: path[%d][0]=%d, must start at the root", b, a[0]);
+        for (int m = 1; m < L; ++m)
+            if (a[m] < 0 || a[m] >= n || p[a[m]] != a[m - 1])
+                return set_error(TV_EPATH, "tv_validate_path: path[%d][%d]=%d is not a child of path[%d][%d]=%d", b, m,
+                                 a[m], b, m - 1, a[m - 1]);
+    }
+    return TV_OK;
+}
+
+int lin_tree_verify(int B, int N, int Hk, int Hv, int dk, int dv, int dtype, int head_group, float scale,
+                    const int32_t* parent, const int32_t* n_nodes, const void* q, const void* k, const void* v,
+                    const void* g, const void* beta, const float* state, float* out, float* cap_delta,
+                    void* stream) {
+    clear_error();
+    const char* fn = "lin_tree_verify";
+    int st = check_common_lin(fn, B, N, Hk, Hv, dk, dv, dtype, head_group);
+    if (st != TV_OK) return st;
+    if (!std::isfinite(scale)) return set_error(TV_EINVAL, "%s: scale is not finite", fn);
+    if (!parent || !n_nodes || !q || !k || !v || !g || !beta || !state || !out || !cap_delta)
+        return set_error(TV_EINVAL, "%s: null pointer argument", fn);
+    const size_t al = dtype == TV_BF16 ? 8 : 16;
+    if (!aligned(q, al) || !aligned(k, al) || !aligned(state, 16))
+        return set_error(TV_EINVAL, "%s: q/k must be %zu-byte aligned and state 16-byte aligned", fn, al);
+    LinVerifyArgs a{B, N, Hk, Hv, dk, dv, Hv / Hk, head_group == TV_HEADS_TILED, scale, parent, n_nodes,
+                    q, k, v, g, beta, state, out, cap_delta};
+    return launch_lin_verify(a, dtype == TV_BF16, static_cast<hipStream_t>(stream));
+}
+
+int lin_tree_commit(int B, int N, int Hk, int Hv, int dk, int dv, int dtype, int head_group, const int32_t* path,
+                    const int32_t* path_len, int Lmax, const void* k, const void* g, const float* cap_delta,
+                    float* state, void* stream) {
+    clear_error();
+    const char* fn = "lin_tree_commit";
+    int st = check_common_lin(fn, B, N, Hk, Hv, dk, dv, dtype, head_group);
+    if (st != TV_OK) return st;
+    if (Lmax < 1 || Lmax > N) return set_error(TV_ERANGE, "%s: Lmax=%d not in [1, N=%d]", fn, Lmax, N);
+    if (!path || !path_len || !k || !g || !cap_delta || !state) return set_error(TV_EINVAL, "%s: null pointer argument", fn);
+    if (!aligned(state, 16)) return set_error(TV_EINVAL, "%s: state must be 16-byte aligned", fn);
+    LinCommitArgs a{B, N, Hk, Hv, dk, dv, Hv / Hk, head_group == TV_HEADS_TILED, Lmax, path, path_len, k, g,
+                    cap_delta, state};
+    return launch_lin_commit(a, dtype == TV_BF16, static_cast<hipStream_t>(stream));
+}
+
+size_t attn_tree_workspace_bytes(int B, int N, int Hq, int Hkv, int D, int Tcap, int window) {
+    clear_error();
+    if (B <= 0 || N <= 0 || N > TV_MAX_NODES || Hq <= 0 || Hkv <= 0 || Hq % Hkv || D <= 0 || Tcap <= 0 || window < 0)
+        return 0;
+    return attn_workspace_bytes(B, N, Hq, Hkv, D, Tcap, window);
+}
+
+int attn_tree_verify(int B, int N, int Hq, int Hkv, int D, int Tcap, int k_type, int v_type, int window, float scale,
+                     const int32_t* parent, const int32_t* n_nodes, const int32_t* n_past, const void* q,
+                     const void* k_cache, const void* v_cache, float* out, float* lse, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+    clear_error();
+    const char* fn = "attn_tree_verify";
+    if (B <= 0 || N <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || Tcap <= 0)
+        return set_error(TV_EINVAL, "%s: sizes must be positive (B=%d N=%d Hq=%d Hkv=%d D=%d Tcap=%d)", fn, B, N, Hq,
+                         Hkv, D, Tcap);
+    if (N > TV_MAX_NODES) return set_error(TV_ERANGE, "%s: N=%d exceeds %d tree nodes", fn, N, TV_MAX_NODES);
+    if (Hq % Hkv) return set_error(TV_EINVAL, "%s: Hq=%d is not a multiple of Hkv=%d", fn, Hq, Hkv);
+    if (Hq / Hkv > 8) return set_error(TV_EUNSUPPORTED, "%s: Hq/Hkv=%d query heads per KV head not built (<= 8)", fn, Hq / Hkv);
+    if (D != 256 && D != 128) return set_error(TV_EUNSUPPORTED, "%s: D=%d not built; supported head sizes: 128, 256", fn, D);
+    const bool kt_ok = k_type == TV_Q8_0 || k_type == TV_Q4_0, vt_ok = v_type == TV_Q8_0 || v_type == TV_Q4_0;
+    if (!kt_ok || !vt_ok)
+        return set_error(TV_EUNSUPPORTED,
+                         "%s: K/V type pair (%d, %d) not built; supported pairs: (Q8_0, Q8_0), (Q8_0, Q4_0), "
+                         "(Q4_0, Q8_0), (Q4_0, Q4_0)", fn, k_type, v_type);
+    if (window < 0) return set_error(TV_EINVAL, "%s: window=%d must be >= 0 (0 = full attention)", fn, window);
+    if (!std::isfinite(scale)) return set_error(TV_EINVAL, "%s: scale is not finite", fn);
+    if (!parent || !n_nodes || !n_past || !q || !k_cache || !v_cache || !out || !workspace)
+        return set_error(TV_EINVAL, "%s: null pointer argument", fn);
+    if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(workspace, 256))
+        return set_error(TV_EINVAL, "%s: q and the caches must be 16-byte aligned, workspace 256-byte aligned", fn);
+    const size_t need = attn_workspace_bytes(B, N, Hq, Hkv, D, Tcap, window);
+    if (need == 0) return set_error(TV_ERANGE, "%s: sizes overflow", fn);
+    if (workspace_bytes < need)
+        return set_error(TV_ERANGE, "%s: workspace of %zu bytes is smaller than the %zu needed", fn, workspace_bytes, need);
+    AttnArgs a{B, N, Hq, Hkv, D, Tcap, k_type, v_type, window, scale, parent, n_nodes, n_past, q,
+               static_cast<const uint8_t*>(k_cache), static_cast<const uint8_t*>(v_cache), out, lse, workspace};
+    return launch_attn(a, static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"

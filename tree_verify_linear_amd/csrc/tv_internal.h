@@ -1,0 +1,81 @@
+// Internal declarations shared by the library's translation units (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "tree_verify.h"
+
+namespace tv {
+
+// ---------------------------------------------------------------- host-side error state
+int set_error(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+void clear_error();
+int launch_status(const char* what);   // TV_OK or TV_EDEVICE from hipGetLastError
+
+// ---------------------------------------------------------------- launchers (host)
+struct LinVerifyArgs {
+    int B, N, Hk, Hv, dk, dv, group_div, tiled;
+    float scale;
+    const int32_t* parent;
+    const int32_t* n_nodes;
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* g;
+    const void* beta;
+    const float* state;
+    float* out;
+    float* cap_delta;
+};
+int launch_lin_verify(const LinVerifyArgs& a, bool bf16, hipStream_t stream);
+
+struct LinCommitArgs {
+    int B, N, Hk, Hv, dk, dv, group_div, tiled, Lmax;
+    const int32_t* path;
+    const int32_t* path_len;
+    const void* k;
+    const void* g;
+    const float* cap_delta;
+    float* state;
+};
+int launch_lin_commit(const LinCommitArgs& a, bool bf16, hipStream_t stream);
+
+struct AttnArgs {
+    int B, N, Hq, Hkv, D, Tcap, k_type, v_type, window;
+    float scale;
+    const int32_t* parent;
+    const int32_t* n_nodes;
+    const int32_t* n_past;
+    const void* q;
+    const uint8_t* k_cache;
+    const uint8_t* v_cache;
+    float* out;
+    float* lse;
+    void* workspace;
+};
+size_t attn_workspace_bytes(int B, int N, int Hq, int Hkv, int D, int Tcap, int window);
+int launch_attn(const AttnArgs& a, hipStream_t stream);
+
+// ---------------------------------------------------------------- device helpers
+#if defined(__HIP_DEVICE_COMPILE__) || defined(__HIPCC__)
+// Consecutive workgroup ids are dealt round-robin to the 8 XCDs (each with its own L2).
+// Remap so that every XCD works through one contiguous range of work units: units that
+// share inputs (neighbouring heads of one sequence) then share an L2.  Bijective for any
+// total.
+__device__ __forceinline__ int xcd_remap(int wg, int total) {
+    constexpr int kXcd = 8;
+    const int q = total / kXcd, r = total % kXcd;
+    const int x = wg % kXcd, idx = wg / kXcd;
+    return x * q + (x < r ? x : r) + idx;
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+    return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+__device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
+#endif
+
+}  // namespace tv
