@@ -50,11 +50,11 @@ def ancestor_matrix(parent, n: int) -> np.ndarray:
 def validate_path(parent, n: int, path, L: int) -> None:
     """An accepted path is a root path: it starts at the root and each entry is a child of
     the previous one ("Luce DFlash" README, "How it works": after accept, the state is the
-    committed prefix)."""
+    committed prefix).  An empty path (L = 0) accepts nothing and is valid."""
     path = np.asarray(path)
-    if L < 1 or L > n or L > len(path):
+    if L < 0 or L > n or L > len(path):
         raise ValueError(f"path length {L} out of range")
-    if int(path[0]) != 0:
+    if L > 0 and int(path[0]) != 0:
         raise ValueError("path must start at the root")
     for m in range(1, L):
         a = int(path[m])

@@ -251,3 +251,10 @@ def test_generated_workload_runs():
     assert np.isfinite(out).all() and np.isfinite(delta).all()
     new = lin_commit_replay(L.state, L.path, L.path_len, L.k, L.v, L.g, L.beta, L.parent, L.n_nodes, "bf16")
     assert np.isfinite(new).all()
+
+
+def test_empty_path_commits_nothing():
+    q, k, v, g, b, state, parent, n = _random_problem(12)
+    path = np.array([[0, 1]], np.int32)
+    new = lin_commit_replay(state, path, np.array([0], np.int32), k, v, g, b, parent, n)
+    assert np.array_equal(new, state.astype(np.float64))

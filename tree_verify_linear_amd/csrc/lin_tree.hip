@@ -93,7 +93,7 @@ __global__ __launch_bounds__(64) void lin_verify_kernel(LinVerifyArgs a) {
     constexpr int CST = 68;                   // padded row stride of Cs (floats)
     constexpr int GST = NT * 16 + 4;          // padded row stride of Gm
 
-    __shared__ float Cs[NT * 16][CST];        // Cs[c][j] = (S0^T x_c)[j0 + j]
+    __shared__ __align__(16) float Cs[NT * 16][CST];   // Cs[c][j] = (S0^T x_c)[j0 + j]
     __shared__ float Gm[GT * 16][GST];        // Gm[m][c] = k_m . x_c
     __shared__ float Dl[NMAX][64];            // delta_i per value channel
     __shared__ float Vl[NMAX][64];            // v_i per value channel
@@ -241,10 +241,10 @@ __global__ __launch_bounds__(64) void lin_verify_kernel(LinVerifyArgs a) {
 
 template <bool BF16IN>
 __global__ __launch_bounds__(256) void lin_commit_kernel(LinCommitArgs a, int rows, int rtiles) {
-    extern __shared__ float smem[];           // Kc[L][dk] then cd[L][rows]
+    extern __shared__ __align__(16) float smem[];   // Kc[L][dk] then cd[L][rows]
     __shared__ int ap[TV_MAX_NODES];
     __shared__ float ga[TV_MAX_NODES];
-    __shared__ float coef[TV_MAX_NODES + 1];
+    __shared__ float coef[TV_MAX_NODES + 4];
 
     const int t = threadIdx.x;
     int unit = xcd_remap(blockIdx.x, gridDim.x);
