@@ -117,6 +117,7 @@ typedef enum { TV_Q8_0 = 0, TV_Q4_0 = 1 } tv_kv_type;
  *              keys per value channel c).  Read only.
  *   out        device, fp32 [B][N][Hv][dv]
  *   cap_delta  device, fp32 [B][N][Hv][dv]: delta_i, consumed by lin_tree_commit
+ * q, k, v, state, out and cap_delta must be 16-byte aligned (TV_EINVAL otherwise).
  */
 int lin_tree_verify(int B, int N, int Hk, int Hv, int dk, int dv, int dtype, int head_group,
                     float scale, const int32_t* parent, const int32_t* n_nodes,

@@ -110,9 +110,9 @@ int lin_tree_verify(int B, int N, int Hk, int Hv, int dk, int dv, int dtype, int
     if (!std::isfinite(scale)) return set_error(TV_EINVAL, "%s: scale is not finite", fn);
     if (!parent || !n_nodes || !q || !k || !v || !g || !beta || !state || !out || !cap_delta)
         return set_error(TV_EINVAL, "%s: null pointer argument", fn);
-    const size_t al = dtype == TV_BF16 ? 8 : 16;
-    if (!aligned(q, al) || !aligned(k, al) || !aligned(state, 16))
-        return set_error(TV_EINVAL, "%s: q/k must be %zu-byte aligned and state 16-byte aligned", fn, al);
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(state, 16) || !aligned(out, 16) ||
+        !aligned(cap_delta, 16))
+        return set_error(TV_EINVAL, "%s: q, k, v, state, out and cap_delta must be 16-byte aligned", fn);
     LinVerifyArgs a{B, N, Hk, Hv, dk, dv, Hv / Hk, head_group == TV_HEADS_TILED, scale, parent, n_nodes,
                     q, k, v, g, beta, state, out, cap_delta};
     return launch_lin_verify(a, dtype == TV_BF16, static_cast<hipStream_t>(stream));

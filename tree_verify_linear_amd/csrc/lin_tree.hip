@@ -5,20 +5,27 @@
 //     u_i = S_p^T k_i,  delta_i = beta_i (v_i - g_i u_i),  S_i = g_i S_p + k_i delta_i^T,
 //     o_i = scale S_i^T q_i.
 // Unrolling the recurrence along the root path gives, for any vector x,
-//     S_p^T x = G_p S0^T x + sum_{m on path(p)} gamma(p, m) (k_m . x) delta_m
-// with G_p the product of g over path(p) and gamma(p, m) the product of g over the path
-// nodes strictly below m.  So only S0^T k_i and S0^T q_i (2N products per value channel)
-// touch the state; everything else is O(N * depth) per channel plus the key Gram matrix.
+//     S_p^T x = G_p S0^T x + sum_{m strict ancestor of i} gamma(i, m) (k_m . x) delta_m
+// with G_p the product of g over the root path of p and gamma(i, m) the product of g over
+// the strict ancestors of i below m.  So only S0^T k_i and S0^T q_i (2n products per value
+// channel) touch the state; the rest is O(n * depth) per channel plus the key Gram matrix:
+//     delta_i = beta_i v_i - beta_i g_i G_p a_i + sum_m Pu[i][m] delta_m
+//     o_i     = scale g_i G_p b_i + scale (k_i . q_i) delta_i + sum_m Pw[i][m] delta_m
+// with a_i = (S0^T k_i)[j], b_i = (S0^T q_i)[j] for value channel j and, for each strict
+// ancestor m of i, Pu[i][m] = -beta_i g_i gamma(i, m) (k_m . k_i) and
+// Pw[i][m] = scale g_i gamma(i, m) (k_m . q_i).
 //
-// Verify: one wave per (sequence, value head, tile of <= 64 value channels).
-//   * The tile of S0 (64 channels x dk fp32, one row per channel) is loaded once, split into
-//     bf16 hi + lo parts (|x - hi - lo| <= 2^-16 |x|) and contracted with [k_0..k_{n-1},
-//     q_0..q_{n-1}] on the matrix cores (v_mfma_f32_16x16x32_bf16, fp32 accumulate); bf16
-//     keys and queries are exact operands.  fp32 inputs are split too (hi*hi+hi*lo+lo*hi).
-//   * The same MFMA gives the key Gram matrix k_m . k_i and k_m . q_i.
-//   * The tree is then walked in index order with one lane per value channel: delta_i and
-//     o_i need only on-chip data (the projections, the Gram matrix and the ancestors'
-//     deltas in LDS).  Per-node states are never formed; S0 is never written.
+// Verify: a work unit is (sequence, value head, tile of <= 64 value channels).
+//   * The unit's S0 tile (one row of dk fp32 per channel) is split into bf16 hi + lo parts
+//     (|x - hi - lo| <= 2^-16 |x|) and contracted with [k_0..k_{n-1}, q_0..q_{n-1}] on the
+//     matrix cores (v_mfma_f32_16x16x32_bf16, fp32 accumulate); bf16 keys and queries are
+//     exact operands, fp32 ones are split too (hi*hi + hi*lo + lo*hi).  The same MFMA gives
+//     the key Gram matrix.
+//   * The tree walk runs one lane per value channel in straight-line code: node i's
+//     coefficients sit in lane i's registers and are broadcast with readlane, deltas stay in
+//     registers.  Per-node states are never formed; S0 is never written.
+//   * Waves are persistent (one per SIMD) and double-buffer whole units: the next unit's
+//     loads are issued before the current unit is computed, so HBM never waits on compute.
 // Commit: the accepted path's captured deltas are flushed into the state in place,
 //     S <- (prod_m g_{a_m}) S0 + sum_m c_m k_{a_m} delta_{a_m}^T,  c_m = prod_{m'>m} g_{a_m'},
 //   a streaming rank-L update (HBM bound).
@@ -35,6 +42,10 @@ __device__ __forceinline__ f32x4 mfma16x16x32(const bf16x8& a, const bf16x8& b, 
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+__device__ __forceinline__ float readlane_f(float x, int lane) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), lane));
+}
+
 // 8 fp32 values -> bf16 hi and lo with x = hi + lo + O(2^-16 |x|).
 __device__ __forceinline__ void split_bf16(const float4& x0, const float4& x1, bf16x8& hi, bf16x8& lo) {
     const float v[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
@@ -46,11 +57,10 @@ __device__ __forceinline__ void split_bf16(const float4& x0, const float4& x1, b
     }
 }
 
-// Contraction-index order used for both MFMA operands: lane group g (lane / 16) of K-step
-// ks holds rows ks*32 + {4g..4g+3} and ks*32 + 16 + {4g..4g+3}, so one 16-byte load per
-// half covers a contiguous 64-byte run per row across the four groups.
+// Contraction order shared by both MFMA operands: lane group g (lane / 16) of K-step ks
+// holds elements ks*32 + 8g .. ks*32 + 8g + 7 of its row (zero past dk).
 template <int DK>
-__device__ __forceinline__ bool second_half_valid(int ks) { return ks * 32 + 16 < DK; }
+__device__ __forceinline__ bool kvalid(int ks, int g4) { return ks * 32 + 8 * g4 < DK; }
 
 template <bool BF16IN>
 __device__ __forceinline__ float load_scalar(const void* base, size_t idx) {
@@ -58,80 +68,378 @@ __device__ __forceinline__ float load_scalar(const void* base, size_t idx) {
     else return static_cast<const float*>(base)[idx];
 }
 
-// Loads the 8 contraction elements of one key/query row for K-step ks as bf16 hi (and lo
-// for fp32 inputs).  `row` points at element 0 of the row.
+// One key/query row's 8 contraction elements for K-step ks, as bf16 hi (and lo for fp32).
 template <int DK, bool BF16IN>
-__device__ __forceinline__ void load_row_operand(const void* row, int ks, int g4, bool valid,
-                                                 bf16x8& hi, bf16x8& lo) {
-    const int r0 = ks * 32 + 4 * g4;
+__device__ __forceinline__ void load_row_operand(const void* row, int ks, int g4, bool valid, bf16x8& hi,
+                                                 bf16x8& lo) {
+    const int r0 = ks * 32 + 8 * g4;
+    const bool ok = valid && kvalid<DK>(ks, g4);
     if constexpr (BF16IN) {
-        const uint16_t* p = static_cast<const uint16_t*>(row) + r0;
-        uint2 a = make_uint2(0, 0), c = make_uint2(0, 0);
-        if (valid) {
-            a = *reinterpret_cast<const uint2*>(p);
-            if (second_half_valid<DK>(ks)) c = *reinterpret_cast<const uint2*>(p + 16);
-        }
-        u32x4 w = {a.x, a.y, c.x, c.y};
-        hi = __builtin_bit_cast(bf16x8, w);
+        uint4 w = make_uint4(0, 0, 0, 0);
+        if (ok) w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(row) + r0);
+        u32x4 u = {w.x, w.y, w.z, w.w};
+        hi = __builtin_bit_cast(bf16x8, u);
         lo = bf16x8{};
     } else {
-        const float* p = static_cast<const float*>(row) + r0;
         float4 x0 = make_float4(0.f, 0.f, 0.f, 0.f), x1 = x0;
-        if (valid) {
+        if (ok) {
+            const float* p = static_cast<const float*>(row) + r0;
             x0 = *reinterpret_cast<const float4*>(p);
-            if (second_half_valid<DK>(ks)) x1 = *reinterpret_cast<const float4*>(p + 16);
+            x1 = *reinterpret_cast<const float4*>(p + 4);
         }
         split_bf16(x0, x1, hi, lo);
     }
 }
 
-template <int DK, int NT, bool BF16IN>
-__global__ __launch_bounds__(64) void lin_verify_kernel(LinVerifyArgs a) {
-    constexpr int KS = (DK + 31) / 32;        // MFMA K-steps over dk
-    constexpr int NMAX = NT * 8;              // 2n columns fit in NT tiles of 16
-    constexpr int GT = (NMAX + 15) / 16;      // Gram row tiles
-    constexpr int CST = 68;                   // padded row stride of Cs (floats)
-    constexpr int GST = NT * 16 + 4;          // padded row stride of Gm
+// A unit's S0 tile (MT x 16 value channels x dk) in MFMA A-operand order.
+template <int DK>
+__device__ __forceinline__ void load_state_tile(float4 (&sa)[4][(DK + 31) / 32][2], const float* tile, int MT,
+                                                int l16, int g4) {
+    constexpr int KS = (DK + 31) / 32;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            sa[mt][ks][0] = sa[mt][ks][1] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (mt < MT && kvalid<DK>(ks, g4)) {
+                const float* p = tile + (mt * 16 + l16) * DK + ks * 32 + 8 * g4;
+                sa[mt][ks][0] = *reinterpret_cast<const float4*>(p);
+                sa[mt][ks][1] = *reinterpret_cast<const float4*>(p + 4);
+            }
+        }
+}
 
-    __shared__ __align__(16) float Cs[NT * 16][CST];   // Cs[c][j] = (S0^T x_c)[j0 + j]
-    __shared__ float Gm[GT * 16][GST];        // Gm[m][c] = k_m . x_c
-    __shared__ float Dl[NMAX][64];            // delta_i per value channel
-    __shared__ float Vl[NMAX][64];            // v_i per value channel
+struct UnitIds {
+    int b, h, kh, ct, j0;
+};
+
+__device__ __forceinline__ UnitIds unit_ids(const LinVerifyArgs& a, int unit, int ctiles, int CW) {
+    UnitIds u;
+    u.ct = unit % ctiles;
+    u.h = (unit / ctiles) % a.Hv;
+    u.b = unit / ctiles / a.Hv;
+    u.kh = a.tiled ? u.h % a.Hk : u.h / a.group_div;
+    u.j0 = u.ct * CW;
+    return u;
+}
+
+// Everything one unit reads from global memory, held in registers while in flight.
+template <int DK, int NT, bool BF16IN>
+struct UnitIn {
+    static constexpr int KS = (DK + 31) / 32;
+    static constexpr int NMAX = NT * 8;
+    static constexpr int ESZ = BF16IN ? 2 : 4;
+    static constexpr int VL = (NMAX * 64 * ESZ + 1023) / 1024;   // 16-byte v loads per lane
+    float4 sa[4][KS][2];
+    bf16x8 bh[NT][KS], bo[NT][KS];
+    uint4 vraw[VL];
+    uint32_t graw, braw;                             // lane i: node i's g and beta, raw input bits
+    int praw, nraw;                                  // lane i: parent[i]; n_nodes[b] (unclamped)
+};
+
+// Issues every load of a unit.  No address depends on loaded data (the tree size n is
+// only applied at compute time; rows up to N are loaded), so a wave can issue the next
+// unit's loads without waiting for anything.
+template <int DK, int NT, bool BF16IN>
+__device__ __forceinline__ void load_unit(UnitIn<DK, NT, BF16IN>& in, const LinVerifyArgs& a, int unit, int ctiles,
+                                          int CW, int lane) {
+    using U = UnitIn<DK, NT, BF16IN>;
+    const int g4 = lane >> 4, l16 = lane & 15;
+    const UnitIds id = unit_ids(a, unit, ctiles, CW);
+    const int N = a.N;                              // <= NMAX by dispatch
+    in.nraw = a.n_nodes[id.b];
+    in.praw = -1;
+    in.graw = in.braw = 0u;
+    if (lane < N) {
+        in.praw = a.parent[static_cast<size_t>(id.b) * N + lane];
+        const size_t gi = (static_cast<size_t>(id.b) * N + lane) * a.Hv + id.h;
+        if constexpr (BF16IN) {
+            in.graw = static_cast<const uint16_t*>(a.g)[gi];
+            in.braw = static_cast<const uint16_t*>(a.beta)[gi];
+        } else {
+            in.graw = static_cast<const uint32_t*>(a.g)[gi];
+            in.braw = static_cast<const uint32_t*>(a.beta)[gi];
+        }
+    }
+    // B operand columns: c < N -> k_c, N <= c < 2N -> q_{c-N}, beyond -> zero.
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        const int c = nt * 16 + l16;
+        const bool isk = c < N;
+        const bool valid = c < 2 * N;
+        const int node = valid ? (isk ? c : c - N) : 0;
+        const size_t rowoff = ((static_cast<size_t>(id.b) * N + node) * a.Hk + id.kh) * DK;
+        const void* row = static_cast<const char*>(isk ? a.k : a.q) + rowoff * U::ESZ;
+#pragma unroll
+        for (int ks = 0; ks < U::KS; ++ks) load_row_operand<DK, BF16IN>(row, ks, g4, valid, in.bh[nt][ks], in.bo[nt][ks]);
+    }
+    // v rows of this unit's channels: 16 bytes per lane, several nodes per instruction.
+    const int epl = 16 / U::ESZ;                    // elements per lane
+    const int lpr = CW / epl;                       // lanes per node row
+    const int rpi = 64 / lpr;                       // node rows per instruction
+#pragma unroll
+    for (int t = 0; t < U::VL; ++t) {
+        const int row = t * rpi + lane / lpr, col = (lane % lpr) * epl;
+        in.vraw[t] = make_uint4(0, 0, 0, 0);
+        if (row < N)
+            in.vraw[t] = *reinterpret_cast<const uint4*>(
+                static_cast<const char*>(a.v) +
+                (((static_cast<size_t>(id.b) * N + row) * a.Hv + id.h) * a.dv + id.j0 + col) * U::ESZ);
+    }
+    const float* tile = a.state + (static_cast<size_t>(id.b) * a.Hv + id.h) * a.dv * DK + static_cast<size_t>(id.j0) * DK;
+    load_state_tile<DK>(in.sa, tile, CW >> 4, l16, g4);
+}
+
+// Shared memory of one verify wave.
+template <int NT, bool BF16IN>
+struct VerifySmem {
+    static constexpr int NMAX = NT * 8;
+    static constexpr int GT = (NMAX + 15) / 16;
+    static constexpr int CST = 68;                  // padded row stride of Cs (floats)
+    static constexpr int GST = NT * 16 + 4;         // padded row stride of Gm
+    __align__(16) float Cs[NT * 16][CST];          // Cs[c][j] = (S0^T x_c)[j0 + j]; rows n.. become outputs
+    union {
+        float Gm[GT * 16][GST];                     // Gm[m][c] = k_m . x_c (until the coefficients are built)
+        __align__(16) float Ds[NMAX][64];           // then delta_i per value channel
+    };
+    __align__(16) uint8_t Vs[NMAX * 64 * (BF16IN ? 2 : 4)];   // v rows of the unit, [node][channel]
+    __align__(16) float Pu[NMAX][NMAX];            // Pu[i][m], zero unless m is a strict ancestor of i
+    __align__(16) float Pw[NMAX][NMAX];
+    float cv[NMAX], ca[NMAX], cb[NMAX], cd[NMAX];   // per-node scalars of the walk
+    float gl[NMAX];
+    int par[NMAX];
+};
+
+template <int DK, int NT, bool BF16IN>
+__device__ __forceinline__ void compute_unit(const UnitIn<DK, NT, BF16IN>& in, VerifySmem<NT, BF16IN>& sm,
+                                             const LinVerifyArgs& a, int unit, int ctiles, int CW, int lane) {
+    using U = UnitIn<DK, NT, BF16IN>;
+    constexpr int KS = U::KS, NMAX = U::NMAX, GT = (NMAX + 15) / 16;
+    const int g4 = lane >> 4, l16 = lane & 15;
+    const int N = a.N;
+    const int n = clampi(in.nraw, 0, N);
+    if (n <= 0) return;
+    const UnitIds id = unit_ids(a, unit, ctiles, CW);
+    const int MT = CW >> 4;
+    // this lane's node (lane < n): parent, decay and write strength; zero beyond the tree
+    const bool real = lane < n;
+    const int pme = real && lane > 0 ? clampi(in.praw, 0, lane - 1) : -1;
+    float gme = 0.f, bme = 0.f;
+    if constexpr (BF16IN) {
+        gme = real ? bf16_bits_to_f32(static_cast<uint16_t>(in.graw)) : 0.f;
+        bme = real ? bf16_bits_to_f32(static_cast<uint16_t>(in.braw)) : 0.f;
+    } else {
+        gme = real ? __uint_as_float(in.graw) : 0.f;
+        bme = real ? __uint_as_float(in.braw) : 0.f;
+    }
+
+    // 1. tree metadata and v rows into LDS; the key Gram matrix.
+    if (lane < NMAX) {
+        sm.par[lane] = pme;
+        sm.gl[lane] = gme;
+    }
+    {
+        const int epl = 16 / U::ESZ, lpr = CW / epl, rpi = 64 / lpr;
+#pragma unroll
+        for (int t = 0; t < U::VL; ++t) {
+            const int row = t * rpi + lane / lpr, col = (lane % lpr) * epl;
+            if (row < NMAX) *reinterpret_cast<uint4*>(&sm.Vs[(row * 64 + col) * U::ESZ]) = in.vraw[t];
+        }
+    }
+#pragma unroll
+    for (int gt = 0; gt < GT; ++gt) {
+        if (gt * 16 >= n) continue;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                acc = mfma16x16x32(in.bh[gt][ks], in.bh[nt][ks], acc);
+                if constexpr (!BF16IN) {
+                    acc = mfma16x16x32(in.bh[gt][ks], in.bo[nt][ks], acc);
+                    acc = mfma16x16x32(in.bo[gt][ks], in.bh[nt][ks], acc);
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sm.Gm[gt * 16 + 4 * g4 + e][nt * 16 + l16] = acc[e];
+        }
+    }
+
+    // 2. S0^T x_c for the unit's channels.
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+        if (mt >= MT) continue;
+        bf16x8 ah[KS], al[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) split_bf16(in.sa[mt][ks][0], in.sa[mt][ks][1], ah[ks], al[ks]);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                acc = mfma16x16x32(ah[ks], in.bh[nt][ks], acc);
+                acc = mfma16x16x32(al[ks], in.bh[nt][ks], acc);
+                if constexpr (!BF16IN) acc = mfma16x16x32(ah[ks], in.bo[nt][ks], acc);
+            }
+            *reinterpret_cast<float4*>(&sm.Cs[nt * 16 + l16][mt * 16 + 4 * g4]) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+        }
+    }
+    __syncthreads();
+
+    // 3. lane = node: ancestor set and the walk coefficients of node `lane`, written as rows
+    //    of LDS so the walk reads four of them per broadcast load.
+    if (lane < NMAX) {
+        uint64_t am = 0;
+        for (int m = pme; m >= 0; m = sm.par[m]) am |= 1ull << m;
+        const int li = real ? lane : 0;
+        float run = 1.f;                            // product of g over ancestors below m
+        float pu[NMAX], pw[NMAX];
+#pragma unroll
+        for (int m = NMAX - 1; m >= 0; --m) {
+            const bool an = (am >> m) & 1ull;
+            pu[m] = an ? -bme * gme * run * sm.Gm[m][li] : 0.f;
+            pw[m] = an ? a.scale * gme * run * sm.Gm[m][N + li] : 0.f;
+            run = an ? run * sm.gl[m < n ? m : 0] : run;
+        }
+#pragma unroll
+        for (int m = 0; m < NMAX; m += 4) {
+            *reinterpret_cast<float4*>(&sm.Pu[lane][m]) = make_float4(pu[m], pu[m + 1], pu[m + 2], pu[m + 3]);
+            *reinterpret_cast<float4*>(&sm.Pw[lane][m]) = make_float4(pw[m], pw[m + 1], pw[m + 2], pw[m + 3]);
+        }
+        sm.cv[lane] = bme;                          // run is now G_parent
+        sm.ca[lane] = bme * gme * run;
+        sm.cb[lane] = a.scale * gme * run;
+        sm.cd[lane] = a.scale * sm.Gm[li][N + li];
+    }
+    __syncthreads();
+    auto v_of = [&](int i) {
+        if constexpr (BF16IN) return bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(sm.Vs)[i * 64 + lane]);
+        else return reinterpret_cast<const float*>(sm.Vs)[i * 64 + lane];
+    };
+
+    // 4. the delta walk: lane = value channel, nodes in index order.  Branch-free, with
+    //    every LDS address a compile-time offset, so loads of later nodes overlap earlier
+    //    arithmetic: nodes at or beyond n have zero coefficients and values (delta 0).
+    float dr[NMAX];
+#pragma unroll
+    for (int i = 0; i < NMAX; ++i) {
+        float d0 = sm.cv[i] * v_of(i) - sm.ca[i] * sm.Cs[i][lane], d1 = 0.f;
+#pragma unroll
+        for (int m = 0; m + 1 < i; m += 2) {
+            d0 = fmaf(sm.Pu[i][m], dr[m], d0);
+            d1 = fmaf(sm.Pu[i][m + 1], dr[m + 1], d1);
+        }
+        if (i & 1) d0 = fmaf(sm.Pu[i][i - 1], dr[i - 1], d0);
+        dr[i] = i < n ? d0 + d1 : 0.f;              // padding rows may hold anything
+    }
+
+    // 5. outputs, now that every delta is known (independent per node).
+    float orow[NMAX];
+#pragma unroll
+    for (int i = 0; i < NMAX; ++i) {
+        float o0 = fmaf(sm.cb[i], sm.Cs[N + i][lane], sm.cd[i] * dr[i]), o1 = 0.f;
+#pragma unroll
+        for (int m = 0; m + 1 < i; m += 2) {
+            o0 = fmaf(sm.Pw[i][m], dr[m], o0);
+            o1 = fmaf(sm.Pw[i][m + 1], dr[m + 1], o1);
+        }
+        if (i & 1) o0 = fmaf(sm.Pw[i][i - 1], dr[i - 1], o0);
+        orow[i] = o0 + o1;
+    }
+    // no LDS writes inside the walks (they would order every later read after them)
+#pragma unroll
+    for (int i = 0; i < NMAX; ++i) {
+        sm.Ds[i][lane] = dr[i];
+        sm.Cs[N + i][lane] = orow[i];               // b_i is consumed: row N + i now holds o_i
+    }
+    __syncthreads();
+
+    // 6. deltas (Ds rows 0..n-1) and outputs (Cs rows N..N+n-1): 16-byte stores, four rows
+    //    per instruction.
+    {
+        const size_t rowbase = (static_cast<size_t>(id.b) * a.N * a.Hv + id.h) * a.dv + id.j0;
+        const size_t ostep = static_cast<size_t>(a.Hv) * a.dv;
+        const int c4 = (lane & 15) * 4;
+        for (int r = lane >> 4; r < 2 * n; r += 4) {
+            const bool isd = r < n;
+            const int i = isd ? r : r - n;
+            if (c4 < CW) {
+                float* dst = (isd ? a.cap_delta : a.out) + rowbase + i * ostep + c4;
+                *reinterpret_cast<float4*>(dst) = *reinterpret_cast<const float4*>(isd ? &sm.Ds[i][c4] : &sm.Cs[N + i][c4]);
+            }
+        }
+    }
+    __syncthreads();                                // LDS is reused by the next unit
+}
+
+// Units of this persistent wave: the XCD it runs on owns one contiguous range of units
+// (workgroup ids are dealt round-robin to the 8 XCDs), taken in turn by its waves.
+struct UnitRange {
+    int first, end, stride;
+};
+__device__ __forceinline__ UnitRange wave_units(int total) {
+    constexpr int kXcd = 8;
+    const int w = blockIdx.x, G = gridDim.x;
+    const int x = w % kXcd, lw = w / kXcd;
+    const int waves_x = G / kXcd + (x < G % kXcd ? 1 : 0);
+    const int q = total / kXcd, r = total % kXcd;
+    const int start = x * q + (x < r ? x : r), cnt = q + (x < r ? 1 : 0);
+    return {start + lw, start + cnt, waves_x};
+}
+
+// Verify for trees of up to 32 nodes: persistent waves, two units in flight per wave.
+template <int DK, int NT, bool BF16IN>
+__global__ __launch_bounds__(64, 1) void lin_verify_kernel(LinVerifyArgs a, int total_units) {
+    static_assert(NT <= 4, "register walk is for trees of up to 32 nodes");
+    __shared__ VerifySmem<NT, BF16IN> sm;
+    const int lane = threadIdx.x;
+    const int CW = a.dv < 64 ? a.dv : 64;
+    const int ctiles = a.dv / CW;
+    const UnitRange ur = wave_units(total_units);
+    // One copy of the unit code (it is large; two copies would crowd the instruction cache):
+    // the prefetched unit is moved into place at the end of each step.
+    UnitIn<DK, NT, BF16IN> cur;
+    if (ur.first < ur.end) load_unit(cur, a, ur.first, ctiles, CW, lane);
+    for (int u = ur.first; u < ur.end; u += ur.stride) {
+        UnitIn<DK, NT, BF16IN> nxt;
+        const bool more = u + ur.stride < ur.end;
+        if (more) load_unit(nxt, a, u + ur.stride, ctiles, CW, lane);
+        compute_unit(cur, sm, a, u, ctiles, CW, lane);
+        if (more) cur = nxt;
+    }
+}
+
+// Verify for trees of 33..64 nodes: the same math, one unit per wave, with the walk driven
+// by per-node ancestor lists and the deltas kept in LDS.
+template <int DK, int NT, bool BF16IN>
+__global__ __launch_bounds__(64) void lin_verify_big_kernel(LinVerifyArgs a) {
+    constexpr int KS = (DK + 31) / 32;
+    constexpr int NMAX = NT * 8;
+    constexpr int GT = (NMAX + 15) / 16;
+    constexpr int CST = 68;
+    constexpr int GST = NT * 16 + 4;
+
+    __shared__ __align__(16) float Cs[NT * 16][CST];
+    __shared__ float Gm[GT * 16][GST];
+    __shared__ float Dl[NMAX][64];
+    __shared__ float Vl[NMAX][64];
     __shared__ float gl[NMAX], bl[NMAX];
     __shared__ int par[NMAX], dep[NMAX];
-    __shared__ int anc[NMAX][NMAX];           // anc[i][t]: t-th strict ancestor (nearest first)
+    __shared__ int anc[NMAX][NMAX];               // anc[i][t]: t-th strict ancestor (nearest first)
 
     const int lane = threadIdx.x;
     const int g4 = lane >> 4, l16 = lane & 15;
     const int CW = a.dv < 64 ? a.dv : 64;
     const int MT = CW >> 4;
     const int ctiles = a.dv / CW;
-    int unit = xcd_remap(blockIdx.x, gridDim.x);
-    const int ct = unit % ctiles;
-    unit /= ctiles;
-    const int h = unit % a.Hv;
-    const int b = unit / a.Hv;
-    const int kh = a.tiled ? h % a.Hk : h / a.group_div;
+    const UnitIds id = unit_ids(a, xcd_remap(blockIdx.x, gridDim.x), ctiles, CW);
+    const int b = id.b, h = id.h, kh = id.kh, j0 = id.j0;
     const int n = clampi(a.n_nodes[b], 0, a.N < NMAX ? a.N : NMAX);
     if (n <= 0) return;
-    const int j0 = ct * CW;
 
-    // 1. committed-state tile as MFMA A operand (rows = value channels); issued first.
     float4 sa[4][KS][2];
-    const float* srow = a.state + (static_cast<size_t>(b) * a.Hv + h) * a.dv * DK + static_cast<size_t>(j0) * DK;
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            sa[mt][ks][0] = sa[mt][ks][1] = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (mt < MT) {
-                const float* p = srow + (mt * 16 + l16) * DK + ks * 32 + 4 * g4;
-                sa[mt][ks][0] = *reinterpret_cast<const float4*>(p);
-                if (second_half_valid<DK>(ks)) sa[mt][ks][1] = *reinterpret_cast<const float4*>(p + 16);
-            }
-        }
-
-    // 2. B operand columns: c < n -> k_c, n <= c < 2n -> q_{c-n}, beyond -> zero.
+    load_state_tile<DK>(sa, a.state + (static_cast<size_t>(b) * a.Hv + h) * a.dv * DK + static_cast<size_t>(j0) * DK,
+                        MT, l16, g4);
     bf16x8 bh[NT][KS], bo[NT][KS];
     {
         const size_t esz = BF16IN ? 2 : 4;
@@ -139,20 +447,16 @@ __global__ __launch_bounds__(64) void lin_verify_kernel(LinVerifyArgs a) {
         for (int nt = 0; nt < NT; ++nt) {
             const int c = nt * 16 + l16;
             const bool isk = c < n;
-            const int node = isk ? c : c - n;
             const bool valid = c < 2 * n;
-            const void* base = isk ? a.k : a.q;
-            const size_t rowoff = ((static_cast<size_t>(b) * a.N + (valid ? node : 0)) * a.Hk + kh) * DK;
-            const void* row = static_cast<const char*>(base) + rowoff * esz;
+            const int node = valid ? (isk ? c : c - n) : 0;
+            const size_t rowoff = ((static_cast<size_t>(b) * a.N + node) * a.Hk + kh) * DK;
+            const void* row = static_cast<const char*>(isk ? a.k : a.q) + rowoff * esz;
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) load_row_operand<DK, BF16IN>(row, ks, g4, valid, bh[nt][ks], bo[nt][ks]);
         }
     }
-
-    // 3. tree metadata, gates and values.
     if (lane < n) {
-        const int p = lane == 0 ? -1 : clampi(a.parent[static_cast<size_t>(b) * a.N + lane], 0, lane - 1);
-        par[lane] = p;
+        par[lane] = lane == 0 ? -1 : clampi(a.parent[static_cast<size_t>(b) * a.N + lane], 0, lane - 1);
         const size_t gi = (static_cast<size_t>(b) * a.N + lane) * a.Hv + h;
         gl[lane] = load_scalar<BF16IN>(a.g, gi);
         bl[lane] = load_scalar<BF16IN>(a.beta, gi);
@@ -161,8 +465,6 @@ __global__ __launch_bounds__(64) void lin_verify_kernel(LinVerifyArgs a) {
         const size_t vi = ((static_cast<size_t>(b) * a.N + i) * a.Hv + h) * a.dv + j0 + lane;
         Vl[i][lane] = lane < CW ? load_scalar<BF16IN>(a.v, vi) : 0.f;
     }
-
-    // 4. Gram matrix: rows are the key columns (tiles 0..GT-1 of the B operand).
 #pragma unroll
     for (int gt = 0; gt < GT; ++gt) {
         if (gt * 16 >= n) continue;
@@ -181,8 +483,6 @@ __global__ __launch_bounds__(64) void lin_verify_kernel(LinVerifyArgs a) {
             for (int e = 0; e < 4; ++e) Gm[gt * 16 + 4 * g4 + e][nt * 16 + l16] = acc[e];
         }
     }
-
-    // 5. S0^T x_c for this tile's channels.
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
         if (mt >= MT) continue;
@@ -198,13 +498,10 @@ __global__ __launch_bounds__(64) void lin_verify_kernel(LinVerifyArgs a) {
                 acc = mfma16x16x32(al[ks], bh[nt][ks], acc);
                 if constexpr (!BF16IN) acc = mfma16x16x32(ah[ks], bo[nt][ks], acc);
             }
-            *reinterpret_cast<float4*>(&Cs[nt * 16 + l16][mt * 16 + 4 * g4]) =
-                make_float4(acc[0], acc[1], acc[2], acc[3]);
+            *reinterpret_cast<float4*>(&Cs[nt * 16 + l16][mt * 16 + 4 * g4]) = make_float4(acc[0], acc[1], acc[2], acc[3]);
         }
     }
     __syncthreads();
-
-    // 6. ancestor lists: lane i follows its own parent chain once.
     if (lane < n) {
         int t = 0;
         for (int m = par[lane]; m >= 0; m = par[m]) anc[lane][t++] = m;
@@ -212,7 +509,6 @@ __global__ __launch_bounds__(64) void lin_verify_kernel(LinVerifyArgs a) {
     }
     __syncthreads();
 
-    // 7. the tree walk, nodes in index order, one lane per value channel.
     const int j = lane;
     for (int i = 0; i < n; ++i) {
         float u = 0.f, w = 0.f, gam = 1.f;
@@ -225,7 +521,7 @@ __global__ __launch_bounds__(64) void lin_verify_kernel(LinVerifyArgs a) {
             w = fmaf(gam * Gm[m][n + i], dm, w);
             gam *= gl[m];
         }
-        u = fmaf(gam, Cs[i][j], u);        // gam = G_parent
+        u = fmaf(gam, Cs[i][j], u);                 // gam = G_parent
         w = fmaf(gam, Cs[n + i][j], w);
         const float gi = gl[i], bi = bl[i];
         const float dl = bi * (Vl[i][j] - gi * u);
@@ -241,7 +537,7 @@ __global__ __launch_bounds__(64) void lin_verify_kernel(LinVerifyArgs a) {
 
 template <bool BF16IN>
 __global__ __launch_bounds__(256) void lin_commit_kernel(LinCommitArgs a, int rows, int rtiles) {
-    extern __shared__ __align__(16) float smem[];   // Kc[L][dk] then cd[L][rows]
+    extern __shared__ __align__(16) float smem[];  // Kc[L][dk] then cd[L][rows]
     __shared__ int ap[TV_MAX_NODES];
     __shared__ float ga[TV_MAX_NODES];
     __shared__ float coef[TV_MAX_NODES + 4];
@@ -276,7 +572,7 @@ __global__ __launch_bounds__(256) void lin_commit_kernel(LinCommitArgs a, int ro
             coef[m] = c;
             c *= ga[m];
         }
-        coef[L] = c;                            // product over the whole path
+        coef[L] = c;                                // product over the whole path
     }
     float* Kc = smem;
     float* cd = smem + L * dk;
@@ -309,14 +605,36 @@ __global__ __launch_bounds__(256) void lin_commit_kernel(LinCommitArgs a, int ro
     if (t + 256 < nvec) update(s1, t + 256);
 }
 
+// Waves the persistent verify kernel keeps resident: one per SIMD on every CU.
+int resident_waves() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 1024;
+    if (!cached[dev]) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+        cached[dev] = cus * 4;
+    }
+    return cached[dev];
+}
+
 template <int DK, int NT>
 int launch_verify_dk_nt(const LinVerifyArgs& a, bool bf16, hipStream_t stream) {
     const int CW = a.dv < 64 ? a.dv : 64;
     const long long units = static_cast<long long>(a.B) * a.Hv * (a.dv / CW);
     if (units > 0x7fffffffLL) return set_error(TV_ERANGE, "lin_tree_verify: too many work units (%lld)", units);
-    dim3 grid(static_cast<unsigned>(units)), block(64);
-    if (bf16) hipLaunchKernelGGL((lin_verify_kernel<DK, NT, true>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((lin_verify_kernel<DK, NT, false>), grid, block, 0, stream, a);
+    dim3 block(64);
+    if constexpr (NT <= 4) {
+        const long long waves = resident_waves();
+        dim3 grid(static_cast<unsigned>(units < waves ? units : waves));
+        const int total = static_cast<int>(units);
+        if (bf16) hipLaunchKernelGGL((lin_verify_kernel<DK, NT, true>), grid, block, 0, stream, a, total);
+        else hipLaunchKernelGGL((lin_verify_kernel<DK, NT, false>), grid, block, 0, stream, a, total);
+    } else {
+        dim3 grid(static_cast<unsigned>(units));
+        if (bf16) hipLaunchKernelGGL((lin_verify_big_kernel<DK, NT, true>), grid, block, 0, stream, a);
+        else hipLaunchKernelGGL((lin_verify_big_kernel<DK, NT, false>), grid, block, 0, stream, a);
+    }
     return launch_status("lin_tree_verify");
 }
 
