@@ -171,7 +171,7 @@ size_t attn_tree_workspace_bytes(int B, int N, int Hq, int Hkv, int D, int Tcap,
  *
  *   B, N       sequences; tree rows per sequence (1 <= N <= 64)
  *   Hq, Hkv    query heads, KV heads (Hq % Hkv == 0, Hq / Hkv <= 8)
- *   D          head size: 256 (also 128)
+ *   D          head size: 256
  *   Tcap       slots per (sequence, KV head) row of the cache; n_past[b] + n_nodes[b] <= Tcap
  *   k_type, v_type   tv_kv_type of each cache ({Q8_0, Q4_0} x {Q8_0, Q4_0})
  *   window     0 = full attention, else the window W > 0

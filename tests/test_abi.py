@@ -85,6 +85,7 @@ def test_attention_argument_errors():
     assert call(Hq=25) == tvl.TV_EINVAL
     assert call(Hq=40, Hkv=4) == tvl.TV_EUNSUPPORTED              # 10 query heads per KV head
     assert call(D=192) == tvl.TV_EUNSUPPORTED
+    assert call(D=128) == tvl.TV_EUNSUPPORTED
     assert call(kt=2) == tvl.TV_EUNSUPPORTED
     assert b"supported pairs" in L.tv_last_error()
     assert call(W=-1) == tvl.TV_EINVAL

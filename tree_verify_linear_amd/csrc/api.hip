@@ -152,7 +152,7 @@ int attn_tree_verify(int B, int N, int Hq, int Hkv, int D, int Tcap, int k_type,
     if (N > TV_MAX_NODES) return set_error(TV_ERANGE, "%s: N=%d exceeds %d tree nodes", fn, N, TV_MAX_NODES);
     if (Hq % Hkv) return set_error(TV_EINVAL, "%s: Hq=%d is not a multiple of Hkv=%d", fn, Hq, Hkv);
     if (Hq / Hkv > 8) return set_error(TV_EUNSUPPORTED, "%s: Hq/Hkv=%d query heads per KV head not built (<= 8)", fn, Hq / Hkv);
-    if (D != 256 && D != 128) return set_error(TV_EUNSUPPORTED, "%s: D=%d not built; supported head sizes: 128, 256", fn, D);
+    if (D != 256) return set_error(TV_EUNSUPPORTED, "%s: D=%d not built; supported head size: 256", fn, D);
     const bool kt_ok = k_type == TV_Q8_0 || k_type == TV_Q4_0, vt_ok = v_type == TV_Q8_0 || v_type == TV_Q4_0;
     if (!kt_ok || !vt_ok)
         return set_error(TV_EUNSUPPORTED,
