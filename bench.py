@@ -1,0 +1,343 @@
+#!/usr/bin/env python3
+"""Tree-verify step benchmark on one GPU.
+
+One step takes every node of a batch of 64 draft trees (22 nodes each) through one
+gated delta-rule layer -- ``lin_tree_verify`` then ``lin_tree_commit`` of each
+sequence's accepted path -- and one tree-masked attention layer (``attn_tree_verify``,
+Q8_0 cache of 4096 committed slots, window 2048).  Widths: linear 16 key / 48 value heads
+of 128, fp32 state; attention 24 query / 4 KV heads of 256.
+
+value = node-layers per second = 2 * (tree nodes in the batch) / step time, i.e. the
+harmonic mean of the linear layer's and the attention layer's nodes/s.
+
+Inputs are seeded synthetic tensors (workloads.workload_batched); a pool of two distinct
+input sets (about 1.5 GB) rotates between steps so the 256 MB last-level cache cannot
+hold a step's working set.  Per-kernel durations come from HIP events recorded on the
+stream the kernels are launched on (torch's current stream) around every call in the
+timed region.
+
+Output: one JSON line.  ``roofline`` is for the kernel with the largest mean duration;
+its ``traffic`` is read from the committed hardware-counter summary under ``profiles/``
+when that summary was taken on the current kernel source (else null).  ``cpu_baseline``
+times the fp64 CPU oracle over whole sequences of the same workload for about ten
+seconds.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+COUNTER_FILE = os.path.join(ROOT, "profiles", "hbm_counters_batched64.txt")
+KERNEL_SOURCES = {
+    "lin_tree_verify": "tree_verify_linear_amd/csrc/lin_tree.hip",
+    "lin_tree_commit": "tree_verify_linear_amd/csrc/lin_tree.hip",
+    "attn_tree_verify": "tree_verify_linear_amd/csrc/attn_tree.hip",
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--batch", type=int, default=64)
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle timing")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU oracle sample budget")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="also run one device-to-device copy of this many MiB (counter calibration)")
+    return ap.parse_args()
+
+
+# ----------------------------------------------------------------------------- bytes
+
+def lin_verify_bytes(L) -> int:
+    """Algorithmic HBM bytes of one lin_tree_verify call: the committed state once, the
+    per-node inputs, the outputs and captured deltas (valid nodes only)."""
+    B, Hv, dv, dk = L.state.shape
+    Hk = L.q.shape[2]
+    eb = 2 if L.dtype == "bf16" else 4
+    nodes = int(L.n_nodes.sum())
+    per_node = 2 * Hk * dk * eb + Hv * dv * eb + 2 * Hv * eb + 2 * Hv * dv * 4
+    return B * Hv * dv * dk * 4 + nodes * per_node + L.parent.nbytes + L.n_nodes.nbytes
+
+
+def lin_commit_bytes(L) -> int:
+    """State read + written once, plus k, captured delta and g of every accepted node."""
+    B, Hv, dv, dk = L.state.shape
+    Hk = L.k.shape[2]
+    eb = 2 if L.dtype == "bf16" else 4
+    acc = int(L.path_len.sum())
+    return 2 * B * Hv * dv * dk * 4 + acc * (Hk * dk * eb + Hv * dv * 4 + Hv * eb) + L.path.nbytes
+
+
+def attn_bytes(A) -> int:
+    """Quantised K and V rows of the union of visible slots per (sequence, KV head), the
+    bf16 queries and the fp32 outputs and log-sum-exps."""
+    from workloads import row_bytes
+    B, N, Hq, D = A.q.shape
+    rb = row_bytes(A.k_type, D) + row_bytes(A.v_type, D)
+    total = 0
+    for b in range(B):
+        n, T = int(A.n_nodes[b]), int(A.n_past[b])
+        committed = T if A.window == 0 else min(T, A.window - 1)
+        total += A.Hkv * (committed + n) * rb + n * Hq * (D * 2 + D * 4 + 4)
+    return total
+
+
+def attn_flops(A) -> float:
+    """2 * D flops for each of QK and PV, over each row's visible slots."""
+    from workloads import row_bytes  # noqa: F401  (same module as the byte model)
+    B, N, Hq, D = A.q.shape
+    total = 0
+    for b in range(B):
+        n, T, W = int(A.n_nodes[b]), int(A.n_past[b]), A.window
+        parent = A.parent[b]
+        dep = [0] * n
+        for i in range(1, n):
+            dep[i] = dep[parent[i]] + 1
+        for i in range(n):
+            vis_c = T if W == 0 else max(0, min(T, W - 1 - dep[i]))
+            vis_t = dep[i] + 1 if W == 0 else min(dep[i] + 1, W)
+            total += Hq * (vis_c + vis_t)
+    return 4.0 * D * total
+
+
+# ----------------------------------------------------------------------------- helpers
+
+def sha256_of(rel: str) -> str:
+    """SHA-256 of a kernel source with // comments and blank lines removed, so that a
+    comment edit does not disown counters taken on unchanged code."""
+    with open(os.path.join(ROOT, rel)) as f:
+        lines = [ln.split("//", 1)[0].rstrip() for ln in f]
+    return hashlib.sha256("\n".join(ln for ln in lines if ln).encode()).hexdigest()
+
+
+def counter_traffic(kernel: str):
+    """HBM bytes per launch from the committed counter summary, if it matches the source."""
+    if not os.path.exists(COUNTER_FILE):
+        return None
+    fields = {}
+    with open(COUNTER_FILE) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                key, val = line.split(":", 1)
+                fields[key.strip()] = val.strip()
+    src = KERNEL_SOURCES[kernel]
+    if fields.get(f"{kernel}.source_sha256") != sha256_of(src):
+        return None
+    try:
+        return float(fields[f"{kernel}.hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def to_device(L, A, dev):
+    import numpy as np
+    import torch
+
+    def bits(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    def i32(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+
+    d = dict(q=bits(L.q), k=bits(L.k), v=bits(L.v), g=bits(L.g), beta=bits(L.beta),
+             state=torch.from_numpy(L.state).to(dev), parent=i32(L.parent), n_nodes=i32(L.n_nodes),
+             path=i32(L.path), path_len=i32(L.path_len),
+             aq=bits(A.q), kc=torch.from_numpy(A.k_cache).to(dev), vc=torch.from_numpy(A.v_cache).to(dev),
+             n_past=i32(A.n_past), aparent=i32(A.parent), an_nodes=i32(A.n_nodes))
+    B, N, Hv, dv = L.v.shape
+    d["out"] = torch.empty((B, N, Hv, dv), dtype=torch.float32, device=dev)
+    d["cap"] = torch.empty_like(d["out"])
+    Bq, Nq, Hq, D = A.q.shape
+    d["aout"] = torch.empty((Bq, Nq, Hq, D), dtype=torch.float32, device=dev)
+    d["lse"] = torch.empty((Bq, Nq, Hq), dtype=torch.float32, device=dev)
+    return d
+
+
+def cpu_baseline(L, A, budget_s: float):
+    """fp64 oracle over whole sequences (verify, attention, commit) for about budget_s."""
+    import numpy as np
+    import oracle
+
+    def sl(x, b):
+        return x[b:b + 1]
+
+    B = L.q.shape[0]
+    nodes = 0
+    seqs = 0
+    w0, c0 = time.perf_counter(), time.process_time()
+    for b in range(B):
+        oracle.lin_tree_verify(sl(L.q, b), sl(L.k, b), sl(L.v, b), sl(L.g, b), sl(L.beta, b), sl(L.state, b),
+                               sl(L.parent, b), sl(L.n_nodes, b), L.scale, L.dtype)
+        oracle.lin_commit_replay(sl(L.state, b), sl(L.path, b), sl(L.path_len, b), sl(L.k, b), sl(L.v, b),
+                                 sl(L.g, b), sl(L.beta, b), sl(L.parent, b), sl(L.n_nodes, b), L.dtype)
+        oracle.attn_tree_verify(sl(A.q, b), sl(A.k_cache, b), sl(A.v_cache, b), A.k_type, A.v_type,
+                                sl(A.n_past, b), sl(A.parent, b), sl(A.n_nodes, b), A.window, A.scale, A.Hkv)
+        nodes += int(L.n_nodes[b])
+        seqs += 1
+        if time.perf_counter() - w0 >= budget_s:
+            break
+    wall = time.perf_counter() - w0
+    cpu = time.process_time() - c0
+    blas = None
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max((p.get("num_threads", 1) for p in threadpool_info()), default=None)
+    except Exception:
+        pass
+    return {
+        "value": 2.0 * nodes / wall,
+        "unit": "node-layers/s",
+        "cores": max(1, round(cpu / wall)),
+        "kind": "oracle",
+        "sample": f"{seqs} of {B} sequences of the batched step (linear verify + commit + attention, "
+                  f"{nodes} nodes), fp64 NumPy, {wall:.1f} s wall, {cpu:.1f} s CPU",
+        "host_cpus": os.cpu_count(),
+        "blas_threads": blas,
+    }
+
+
+# ----------------------------------------------------------------------------- main
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "the tree-verify kernels need no exchange between GPUs and no multi-GPU path is built.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import tree_verify_linear_amd as tvl
+    from workloads import workload_batched
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    tvl.lib()
+
+    B = args.batch
+    t_gen = time.perf_counter()
+    sets = [workload_batched(B), workload_batched(B, seq_ids=list(range(B, 2 * B)))]
+    print(f"# generated {len(sets)} input sets in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr, flush=True)
+    pool = [to_device(W.lin[0], W.attn[0], dev) for W in sets]
+    L0, A0 = sets[0].lin[0], sets[0].attn[0]
+    Hkv, Tcap = A0.k_cache.shape[1], A0.k_cache.shape[2]
+    ws_bytes = max(tvl.attn_tree_workspace_bytes(B, A0.q.shape[1], A0.Hq, Hkv, A0.D, Tcap, A0.window), 256)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    names = ["lin_tree_verify", "attn_tree_verify", "lin_tree_commit"]
+
+    def step(i, ev=None):
+        d = pool[i % len(pool)]
+        W = sets[i % len(sets)]
+        L, A = W.lin[0], W.attn[0]
+        if ev:
+            ev[0].record()
+        tvl.lin_tree_verify(d["q"], d["k"], d["v"], d["g"], d["beta"], d["state"], d["parent"], d["n_nodes"],
+                            L.scale, out=d["out"], cap_delta=d["cap"])
+        if ev:
+            ev[1].record()
+        tvl.attn_tree_verify(d["aq"], d["kc"], d["vc"], A.k_type, A.v_type, d["n_past"], d["aparent"],
+                             d["an_nodes"], A.window, A.scale, out=d["aout"], lse=d["lse"], workspace=ws)
+        if ev:
+            ev[2].record()
+        tvl.lin_tree_commit(d["state"], d["path"], d["path_len"], d["k"], d["g"], d["cap"])
+        if ev:
+            ev[3].record()
+
+    if args.copy_probe_mib > 0:
+        n = args.copy_probe_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    print("# warmup done", file=sys.stderr, flush=True)
+
+    K = args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    torch.cuda.synchronize()
+    h0 = time.perf_counter()
+    for i in range(K):
+        step(args.warmup + i, evs[i])
+    torch.cuda.synchronize()
+    host_ms = (time.perf_counter() - h0) * 1e3 / K
+    per = {n: [] for n in names}
+    for e in evs:
+        for j, n in enumerate(names):
+            per[n].append(e[j].elapsed_time(e[j + 1]))
+    ms_step = evs[0][0].elapsed_time(evs[-1][3]) / K
+    print(f"# timed {K} steps", file=sys.stderr, flush=True)
+
+    nodes = sum(int(W.lin[0].n_nodes.sum()) for W in sets) / len(sets)
+    value = 2.0 * nodes / (ms_step * 1e-3)
+    byts = {
+        "lin_tree_verify": sum(lin_verify_bytes(W.lin[0]) for W in sets) / len(sets),
+        "attn_tree_verify": sum(attn_bytes(W.attn[0]) for W in sets) / len(sets),
+        "lin_tree_commit": sum(lin_commit_bytes(W.lin[0]) for W in sets) / len(sets),
+    }
+    kernels = {}
+    for n in names:
+        ms = sum(per[n]) / len(per[n])
+        med = sorted(per[n])[len(per[n]) // 2]
+        gbs = byts[n] / (ms * 1e-3) / 1e9
+        kernels[n] = {"mean_us": round(ms * 1e3, 2), "median_us": round(med * 1e3, 2),
+                      "algorithmic_MB": round(byts[n] / 1e6, 2), "GB_per_s": round(gbs, 1),
+                      "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+                      "nodes_per_s": round(nodes / (ms * 1e-3), 1)}
+    fl = sum(attn_flops(W.attn[0]) for W in sets) / len(sets)
+    kernels["attn_tree_verify"]["TFLOP_per_s"] = round(fl / (kernels["attn_tree_verify"]["mean_us"] * 1e-6) / 1e12, 2)
+    dom = max(names, key=lambda n: kernels[n]["mean_us"])
+    achieved = kernels[dom]["GB_per_s"]
+    roofline = {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": counter_traffic(dom),
+                "algorithmic_bytes_per_launch": int(byts[dom])}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(L0, A0, args.cpu_seconds)
+
+    line = {
+        "metric": "tree-verify nodes/s per layer (22-node tree) + achieved HBM GB/s vs peak",
+        "value": round(value, 1),
+        "unit": "node-layers/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "host_ms_per_step": round(host_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"batched tree verify: {B} sequences x 22-node DDTree, linear layer Hk16/Hv48 "
+                               f"dk=dv=128 fp32 state + commit, attention Hq24/Hkv4 D256 Q8_0 T=4096 window 2048",
+                   "global_batch": B, "tree_nodes": 22, "kv_type": "q8_0", "window": 2048, "n_past": 4096},
+        "kernels": kernels,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

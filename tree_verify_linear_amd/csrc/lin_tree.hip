@@ -21,9 +21,11 @@
 //     matrix cores (v_mfma_f32_16x16x32_bf16, fp32 accumulate); bf16 keys and queries are
 //     exact operands, fp32 ones are split too (hi*hi + hi*lo + lo*hi).  The same MFMA gives
 //     the key Gram matrix.
-//   * The tree walk runs one lane per value channel in straight-line code: node i's
-//     coefficients sit in lane i's registers and are broadcast with readlane, deltas stay in
-//     registers.  Per-node states are never formed; S0 is never written.
+//   * Lane i computes node i's ancestor set and walk coefficients and writes them as LDS
+//     row i.  The walk then runs one lane per value channel, nodes in index order, in
+//     branch-free straight-line code whose LDS addresses are compile-time offsets (nodes
+//     beyond the tree have zero coefficients); deltas stay in registers.  Per-node states
+//     are never formed; S0 is never written.
 //   * Waves are persistent (one per SIMD) and double-buffer whole units: the next unit's
 //     loads are issued before the current unit is computed, so HBM never waits on compute.
 // Commit: the accepted path's captured deltas are flushed into the state in place,
