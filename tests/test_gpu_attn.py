@@ -114,5 +114,8 @@ def test_deterministic_and_batch_invariant():
     one = workload_batched(1, seq_ids=[1]).attn[0]
     ob, lb = run_gpu(one)
     n = int(one.n_nodes[0])
-    # the KV split plan depends on the batch size, so only rounding may differ
-    assert rel_err(ob[0, :n], o1[1, :n]) < 1e-5
+    # The KV split plan depends on the batch size, and P is rounded to fp16 against each
+    # split's own reference max, so the two runs round differently: each is within TOL of the
+    # exact result, hence within 2 TOL of each other.
+    assert rel_err(ob[0, :n], o1[1, :n]) <= 2 * TOL
+    assert np.max(np.abs(lb[0, :n] - l1[1, :n])) <= 2 * TOL_LSE

@@ -7,19 +7,29 @@
 // T + depth(i); it sees committed slot t iff window == 0 or T + depth(i) - t < window, and
 // tree slot T + j iff j is on its root path and (window == 0 or depth(i) - depth(j) < window).
 //
-// Work unit: (sequence, KV head, row block, KV split).  The rows are the (node, query head)
-// pairs that share the KV head -- 22 nodes x 6 heads = 132 rows for the 27B layer -- so every
-// K/V byte is read from HBM once per split and reused by all of them.
-//   * K/V slot tiles (32 slots) are copied raw into LDS with 16-byte loads, then dequantised
-//     cooperatively.  Every value d*q is split exactly into fp16 hi + lo (d is fp16 and q has
-//     at most 8 bits, so d*q has <= 19 significant bits and the fp16 residual is exact); K
-//     is kept row-major, V transposed (slots contiguous) for the PV operand.
-//   * S^T = K Q^T on the matrix cores (v_mfma_f32_16x16x32_f16, fp32 accumulate): Q (bf16,
-//     exactly representable in fp16 within range) stays in registers as the B operand, K hi
-//     and lo come from LDS as the A operand.  The scores of one row then sit in one lane
-//     group in exactly the layout the PV product wants for P, so no transpose is needed.
-//   * Mask, scale and an online softmax in the exp2 domain; P is rounded once to fp16 (the
-//     only rounding of the whole contraction) and O += P V_hi + P V_lo.
+// Work unit: (sequence, KV head, block of <= 144 rows, KV split).  The rows are the (node,
+// query head) pairs that share the KV head -- 22 nodes x 6 heads = 132 rows, 9 row tiles of
+// 16 -- so every K/V byte is read from HBM once per split and reused by all of them.
+//
+// Layout of the work inside a workgroup (8 waves, two per SIMD, in two roles):
+//   * K/V slot tiles (32 slots) are copied raw into LDS with 16-byte loads issued one tile
+//     ahead.  Dequantisation is exact: d*q has at most 19 significant bits (fp16 d, <= 8-bit
+//     q), so it splits exactly into fp16 hi = RN(d*q) and lo = d*q - hi.
+//   * Scoring waves (4): the head dimension (256 = 8 quantisation blocks) is split in four
+//     quarters; scoring wave w owns blocks 2w, 2w+1 and computes S^T = K Q^T over those 64
+//     dimensions for all 9 row tiles on v_mfma_f32_16x16x32_f16 (K hi and lo as the A
+//     operand, Q in registers as the B operand, fp32 accumulate).  The partial scores of a row
+//     tile meet in LDS at the scoring wave that owns the tile's softmax.  The owner
+//     masks, runs an online softmax in the exp2 domain (the reference max moves only when a
+//     row max grows by more than 2^8; O is then rescaled) and writes P -- rounded once to
+//     fp16, the only rounding of the whole contraction -- to LDS in the PV A-operand layout
+//     (the score layout of S^T already is that layout, so no transpose).
+//   * PV waves (4): PV wave w owns output columns 64w .. 64w+63 of all rows.  It dequantises
+//     its columns of V into fp16 hi/lo (slot-major, the PV B operand) and accumulates
+//     O += P V_hi + P V_lo, one tile behind the scores.
+//   * Each SIMD carries one wave of each role, and the phases pair them up: while the scoring
+//     wave issues the QK^T matrix instructions the PV wave dequantises V, and while the
+//     scoring wave runs the softmax the PV wave issues the PV matrix instructions.
 //   * Each split writes unnormalised O, its running max and sum; a combine pass rescales and
 //     sums the splits.  With a single split the kernel normalises and writes the output.
 #include <cmath>
@@ -31,13 +41,18 @@ namespace {
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int TS = 32;                 // slots per tile
-constexpr int WAVES = 4;
-constexpr int THREADS = WAVES * 64;
-constexpr int MAXRT = 3;               // row tiles (of 16 rows) per wave
-constexpr int ROWS_PER_BLOCK = WAVES * MAXRT * 16;   // 192
+constexpr int D = 256;
+constexpr int TS = 32;                       // slots per tile
+constexpr int WAVES = 8;                     // 4 scoring + 4 PV waves
+constexpr int THREADS = 64 * WAVES;
+constexpr int RTMAX = 9;                     // row tiles per row block
+constexpr int OWNMAX = (RTMAX + 3) / 4;      // softmax tiles owned per scoring wave
+constexpr int ROWS_PER_BLOCK = RTMAX * 16;   // 144
+constexpr int MAXROW = 8 * 34;               // bytes of one slot's row (Q8_0, the larger)
+constexpr int VST = TS + 4;                  // fp16 stride of a transposed V column
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -45,16 +60,79 @@ __device__ __forceinline__ f32x4 mfma_f16(const f16x8& a, const f16x8& b, const 
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ int blk_bytes(int type) { return type == TV_Q8_0 ? 34 : 18; }
+template <int TYPE>
+struct Fmt {
+    static constexpr int BLK = TYPE == TV_Q8_0 ? 34 : 18;   // bytes per 32-element block
+    static constexpr int ROW = 8 * BLK;                      // bytes per slot (256 elements)
+};
 
-__device__ __forceinline__ float f16_bits_to_f32(uint16_t h) {
-    return static_cast<float>(__builtin_bit_cast(_Float16, h));
+__device__ __forceinline__ _Float16 block_scale(const uint8_t* blk) {
+    return __builtin_bit_cast(_Float16, *reinterpret_cast<const uint16_t*>(blk));
 }
 
-// Exact split of x = d*q (d fp16, |q| <= 127) into two fp16 values.
-__device__ __forceinline__ void split_f16(float x, _Float16& hi, _Float16& lo) {
-    hi = static_cast<_Float16>(x);
-    lo = static_cast<_Float16>(x - static_cast<float>(hi));
+__device__ __forceinline__ uint32_t lds_u32(const uint8_t* p) { return *reinterpret_cast<const uint32_t*>(p); }
+
+// Four bytes at the even byte offset `o` of an LDS row, read as aligned dwords.  The integer
+// part of a block starts two bytes after its scale, so it is dword aligned in odd blocks and
+// two bytes off in even ones (34- and 18-byte blocks alike).
+template <bool ALIGNED>
+__device__ __forceinline__ uint32_t bytes4(const uint8_t* row, int o) {
+    if constexpr (ALIGNED) {
+        return lds_u32(row + o);
+    } else {
+        return __builtin_amdgcn_alignbyte(lds_u32(row + o + 2), lds_u32(row + o - 2), 2u);
+    }
+}
+// The same with the alignment known only at run time (o % 4 is 0 or 2).
+__device__ __forceinline__ uint32_t bytes4_rt(const uint8_t* row, int o) {
+    const uint8_t* p = row + (o & ~3);
+    return __builtin_amdgcn_alignbyte(lds_u32(p + 4), lds_u32(p), static_cast<uint32_t>(o & 3));
+}
+
+// Bytes 0, 1 (resp. 2, 3) of x placed under the fp16 exponent of 1024: the pair of fp16
+// values 1024 + byte.
+__device__ __forceinline__ f16x2 biased_lo(uint32_t x) {
+    return __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(0x64646464u, x, 0x04010400u));
+}
+__device__ __forceinline__ f16x2 biased_hi(uint32_t x) {
+    return __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(0x64646464u, x, 0x04030402u));
+}
+
+// Four quantised integers per dword -> biased byte form: Q8_0 flips the sign bit (q + 128),
+// Q4_0 selects the low or high nibbles (q + 8).  `ints_bias` undoes the bias exactly.
+template <int TYPE>
+__device__ __forceinline__ uint32_t to_biased(uint32_t w, int nib_shift) {
+    if constexpr (TYPE == TV_Q8_0) return w ^ 0x80808080u;
+    else return (w >> nib_shift) & 0x0f0f0f0fu;
+}
+template <int TYPE>
+constexpr float ints_bias() { return TYPE == TV_Q8_0 ? 1152.f : 1032.f; }
+
+// Elements 8g .. 8g+7 of block kb of a slot row, as exact fp16 integers (the MFMA operand of
+// lane group g).  Block kb is even iff !ODD.
+template <int TYPE, bool ODD>
+__device__ __forceinline__ f16x8 block_ints8(const uint8_t* row, int kb, int g) {
+    int o, sh = 0;
+    if constexpr (TYPE == TV_Q8_0) {
+        o = 34 * kb + 2 + 8 * g;
+    } else {
+        o = 18 * kb + 2 + 8 * (g & 1);      // elements 16.. are the high nibbles of bytes 0..
+        sh = g >= 2 ? 4 : 0;
+    }
+    const uint32_t w0 = to_biased<TYPE>(bytes4<ODD>(row, o), sh);
+    const uint32_t w1 = to_biased<TYPE>(bytes4<ODD>(row, o + 4), sh);
+    const f16x2 bias = static_cast<_Float16>(ints_bias<TYPE>());
+    const f16x2 p0 = biased_lo(w0) - bias, p1 = biased_hi(w0) - bias;
+    const f16x2 p2 = biased_lo(w1) - bias, p3 = biased_hi(w1) - bias;
+    return f16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
+// d*q = hi + lo exactly (see the file comment): hi rounds the exact product once, the fused
+// multiply-add returns the residual, which needs at most 8 significant bits.
+template <typename V>
+__device__ __forceinline__ void split_exact(const V& q, const V& d, V& hi, V& lo) {
+    hi = d * q;
+    lo = __builtin_elementwise_fma(d, q, -hi);
 }
 
 struct AttnLaunch {
@@ -70,54 +148,42 @@ struct AttnLaunch {
     float* lpart;       // [B][Hkv][nsplit][rows_pad]  running sum
 };
 
-template <int D>
 struct AttnSmem {
-    static constexpr int NB = D / 32;
-    static constexpr int KST = D + 8;              // fp16 row stride of the K tile (padded)
-    static constexpr int VST = TS + 4;             // fp16 row stride of the transposed V tile
-    __align__(16) uint8_t kraw[TS * NB * 34];
-    __align__(16) uint8_t vraw[TS * NB * 34];
-    __align__(16) _Float16 khi[TS][KST];
-    __align__(16) _Float16 klo[TS][KST];
-    __align__(16) _Float16 vhi[D][VST];
-    __align__(16) _Float16 vlo[D][VST];
+    __align__(16) uint8_t rawk[TS * MAXROW + 16];           // K rows of the tile being scored
+    __align__(16) uint8_t rawv[2][TS * MAXROW + 16];        // V rows, two tiles in flight
+    __align__(16) f32x4 spart[RTMAX][3][2][64];             // partial scores from non-owners
+    __align__(16) f32x4 sdump[4][2][64];                    // the owner's copy (not read)
+    __align__(16) f16x8 pbuf[2][RTMAX][64];                 // P in the PV operand layout
+    __align__(16) _Float16 vdq[4][2][64][VST];              // [PV wave][hi, lo][column][slot]
+    __align__(16) float alpha[2][RTMAX][64];                // O rescale factor, row = index % 16
+    int grow[2][RTMAX];                                     // row tile needs a rescale
+    float mfin[ROWS_PER_BLOCK], lfin[ROWS_PER_BLOCK];
     uint64_t anc[TV_MAX_NODES];
     int dep[TV_MAX_NODES];
     int par[TV_MAX_NODES];
 };
 
-// Decodes 8 consecutive elements (e0 .. e0+7, e0 % 8 == 0) of one quantised block at `blk`.
-__device__ __forceinline__ void decode8(const uint8_t* blk, int type, int e0, float (&x)[8]) {
-    const float d = f16_bits_to_f32(*reinterpret_cast<const uint16_t*>(blk));
-    if (type == TV_Q8_0) {
-        const uint16_t* p = reinterpret_cast<const uint16_t*>(blk + 2 + e0);
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const uint16_t w = p[k];
-            x[2 * k] = d * static_cast<float>(static_cast<int8_t>(w & 0xff));
-            x[2 * k + 1] = d * static_cast<float>(static_cast<int8_t>(w >> 8));
-        }
-    } else {
-        const bool high = e0 >= 16;
-        const uint16_t* p = reinterpret_cast<const uint16_t*>(blk + 2 + (e0 & 15));
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const uint16_t w = p[k];
-            const int b0 = w & 0xff, b1 = w >> 8;
-            const int n0 = high ? (b0 >> 4) : (b0 & 15), n1 = high ? (b1 >> 4) : (b1 & 15);
-            x[2 * k] = d * static_cast<float>(n0 - 8);
-            x[2 * k + 1] = d * static_cast<float>(n1 - 8);
-        }
-    }
-}
+// Softmax state of one owned row tile (this lane's row l16).
+struct RowState {
+    int node, dep, rlo;         // rlo: first committed slot the row sees
+    uint64_t anc;
+    float m, l;                 // running max (log2 domain, lane-group uniform), lane's sum
+    bool on;                    // the row exists
+};
 
-template <int D>
+template <int KT, int VT>
 __global__ __launch_bounds__(THREADS, 1) void attn_kernel(AttnLaunch L) {
-    constexpr int NB = D / 32, KS = D / 32, NTD = D / 16;
-    using SM = AttnSmem<D>;
-    __shared__ SM sm;
+    using KF = Fmt<KT>;
+    using VF = Fmt<VT>;
+    constexpr int KCH = TS * KF::ROW / 16, VCH = TS * VF::ROW / 16;    // 16-byte pieces per tile
+    constexpr int STG = THREADS;                                        // staging threads (all)
+    constexpr int KPT = (KCH + STG - 1) / STG, VPT = (VCH + STG - 1) / STG;
+    __shared__ AttnSmem sm;
     const AttnArgs& a = L.a;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6) & (WAVES - 1);   // wave-uniform
+    const bool scorer = wave < 4;
+    const int wl = wave & 3;
     const int g4 = lane >> 4, l16 = lane & 15;
 
     int wg = xcd_remap(blockIdx.x, gridDim.x);
@@ -128,16 +194,21 @@ __global__ __launch_bounds__(THREADS, 1) void attn_kernel(AttnLaunch L) {
     const int kvh = wg % a.Hkv;
     const int b = wg / a.Hkv;
 
-    const int n = clampi(a.n_nodes[b], 0, a.N);
+    const int N = a.N;
+    const int n = clampi(a.n_nodes[b], 0, N);
     const int T = clampi(a.n_past[b], 0, a.Tcap - n);
     const int W = a.window;
     const int lo_b = W ? (T - W + 1 > 0 ? T - W + 1 : 0) : 0;   // first committed slot any node sees
     const int hi_b = T + n;
     const int s0 = lo_b + split * L.chunk;
     const int s1 = s0 + L.chunk < hi_b ? s0 + L.chunk : hi_b;
+    const int ntiles = s1 > s0 ? (s1 - s0 + TS - 1) / TS : 0;
+    const int rowbase = rb * ROWS_PER_BLOCK;
+    const int RT = (L.rows - rowbase + 15) / 16 < RTMAX ? (L.rows - rowbase + 15) / 16 : RTMAX;
+    const size_t part = (static_cast<size_t>(b) * a.Hkv + kvh) * L.nsplit + split;
 
     // tree metadata (depth, ancestor sets) for this sequence
-    if (tid < n) sm.par[tid] = tid == 0 ? -1 : clampi(a.parent[static_cast<size_t>(b) * a.N + tid], 0, tid - 1);
+    if (tid < n) sm.par[tid] = tid == 0 ? -1 : clampi(a.parent[static_cast<size_t>(b) * N + tid], 0, tid - 1);
     __syncthreads();
     if (tid == 0) {
         for (int i = 0; i < n; ++i) {
@@ -147,247 +218,365 @@ __global__ __launch_bounds__(THREADS, 1) void attn_kernel(AttnLaunch L) {
         }
     }
 
-    // this lane's rows: Q as the MFMA B operand, and the row's mask parameters
-    const int kt = a.k_type, vt = a.v_type;
-    f16x8 qop[MAXRT][KS];
-    int rnode[MAXRT], rlo[MAXRT], rdep[MAXRT];
-    uint64_t ranc[MAXRT];
+    const uint8_t* kbase = a.k_cache + (static_cast<size_t>(b) * a.Hkv + kvh) * a.Tcap * KF::ROW;
+    const uint8_t* vbase = a.v_cache + (static_cast<size_t>(b) * a.Hkv + kvh) * a.Tcap * VF::ROW;
+    // raw tile staging (all threads): 16-byte pieces, rows past the cache end read as zero
+    uint4 rk[KPT], rv[VPT];
+    auto gload = [&](int tile) {
+        const int t0 = s0 + tile * TS;
+        const int slots_ok = a.Tcap - t0 < TS ? a.Tcap - t0 : TS;
+#pragma unroll
+        for (int x = 0; x < KPT; ++x) {
+            const int c = tid + x * STG;
+            rk[x] = make_uint4(0, 0, 0, 0);
+            if (c < KCH && c * 16 < slots_ok * KF::ROW)
+                rk[x] = *reinterpret_cast<const uint4*>(kbase + static_cast<size_t>(t0) * KF::ROW + c * 16);
+        }
+#pragma unroll
+        for (int x = 0; x < VPT; ++x) {
+            const int c = tid + x * STG;
+            rv[x] = make_uint4(0, 0, 0, 0);
+            if (c < VCH && c * 16 < slots_ok * VF::ROW)
+                rv[x] = *reinterpret_cast<const uint4*>(vbase + static_cast<size_t>(t0) * VF::ROW + c * 16);
+        }
+    };
+    auto lstore = [&](int tile) {
+#pragma unroll
+        for (int x = 0; x < KPT; ++x) {
+            const int c = tid + x * STG;
+            if (c < KCH) *reinterpret_cast<uint4*>(&sm.rawk[c * 16]) = rk[x];
+        }
+#pragma unroll
+        for (int x = 0; x < VPT; ++x) {
+            const int c = tid + x * STG;
+            if (c < VCH) *reinterpret_cast<uint4*>(&sm.rawv[tile & 1][c * 16]) = rv[x];
+        }
+    };
+    // Raw tile k+1 into LDS (rawk was last read by the scores of tile k, rawv[(k+1)&1] by the
+    // dequantisation of tile k-1, both before the phase barrier), then loads of tile k+2.
+    auto stage = [&](int k) {
+        if (k + 1 < ntiles) {
+            lstore(k + 1);
+            if (k + 2 < ntiles) gload(k + 2);
+        }
+    };
+
+    if (ntiles > 0) {
+        gload(0);
+        lstore(0);
+        if (ntiles > 1) gload(1);
+    }
     __syncthreads();
+
+    // Barrier sequence, identical in both roles: one above, two per tile step k = 0..ntiles
+    // (after phase 1 and after phase 2), one before the epilogue's output writes.
+    if (scorer) {
+        // ------------------------------------------------------------ scoring waves
+        // Q of all row tiles, this wave's two blocks, as the QK B operand
+        f16x8 qop[RTMAX][2];
 #pragma unroll
-    for (int t = 0; t < MAXRT; ++t) {
-        const int r = rb * ROWS_PER_BLOCK + (wave + WAVES * t) * 16 + l16;
-        const int node = r / L.G, hh = r - node * L.G;
-        const bool ok = r < L.rows && node < n;
-        rnode[t] = ok ? node : -1;
-        rdep[t] = ok ? sm.dep[node] : 0;
-        ranc[t] = ok ? sm.anc[node] : 0ull;
-        rlo[t] = W ? T + rdep[t] - W + 1 : 0;
-        const uint16_t* qrow = static_cast<const uint16_t*>(a.q) +
-                               ((static_cast<size_t>(b) * a.N + (ok ? node : 0)) * a.Hq + kvh * L.G + hh) * D;
+        for (int r = 0; r < RTMAX; ++r) {
+            const int row = rowbase + r * 16 + l16;
+            const int node = row / L.G, hh = row - node * L.G;
+            const bool ok = r < RT && row < L.rows && node < n;
+            const uint16_t* qrow = static_cast<const uint16_t*>(a.q) +
+                                   ((static_cast<size_t>(b) * N + (ok ? node : 0)) * a.Hq + kvh * L.G + hh) * D;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            uint4 w = make_uint4(0, 0, 0, 0);
-            if (ok) w = *reinterpret_cast<const uint4*>(qrow + ks * 32 + 8 * g4);
-            const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+            for (int kb = 0; kb < 2; ++kb) {
+                uint4 w = make_uint4(0, 0, 0, 0);
+                if (ok) w = *reinterpret_cast<const uint4*>(qrow + (2 * wl + kb) * 32 + 8 * g4);
+                const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    qop[r][kb][2 * e] = static_cast<_Float16>(__uint_as_float(u[e] << 16));
+                    qop[r][kb][2 * e + 1] = static_cast<_Float16>(__uint_as_float(u[e] & 0xffff0000u));
+                }
+            }
+        }
+        // softmax rows this wave owns: row tiles wl, wl + 4, wl + 8
+        RowState rs[OWNMAX];
+        int rlo_max[OWNMAX];
+        f32x4 own[OWNMAX][2];
+#pragma unroll
+        for (int j = 0; j < OWNMAX; ++j) {
+            const int r = wl + 4 * j;
+            const int row = rowbase + r * 16 + l16;
+            const int node = row / L.G;
+            rs[j].on = r < RT && row < L.rows && node < n;
+            rs[j].node = rs[j].on ? node : 0;
+            rs[j].dep = rs[j].on ? sm.dep[node] : 0;
+            rs[j].anc = rs[j].on ? sm.anc[node] : 0ull;
+            rs[j].rlo = W ? T + rs[j].dep - W + 1 : 0;
+            rs[j].m = -INFINITY;
+            rs[j].l = 0.f;
+            // a committed tile is unmasked for this row tile when every row sees all its
+            // slots (rows that do not exist are cleared separately)
+            int rm = rs[j].on ? rs[j].rlo : -0x7fffffff;
+#pragma unroll
+            for (int o = 1; o < 16; o <<= 1) {
+                const int t = __shfl_xor(rm, o);
+                rm = t > rm ? t : rm;
+            }
+            rlo_max[j] = __builtin_amdgcn_readfirstlane(rm);
+            own[j][0] = own[j][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        const float sl2 = a.scale * kLog2e;
+
+        for (int k = 0; k <= ntiles; ++k) {
+            // phase 1: partial scores of tile k
+            if (k < ntiles) {
+#pragma unroll
+                for (int st = 0; st < 2; ++st) {
+                    f16x8 ah[2], al[2];
+                    const uint8_t* krow = &sm.rawk[(16 * st + l16) * KF::ROW];
+                    {
+                        const f16x8 d0 = block_scale(krow + 2 * wl * KF::BLK);
+                        const f16x8 d1 = block_scale(krow + (2 * wl + 1) * KF::BLK);
+                        split_exact(block_ints8<KT, false>(krow, 2 * wl, g4), d0, ah[0], al[0]);
+                        split_exact(block_ints8<KT, true>(krow, 2 * wl + 1, g4), d1, ah[1], al[1]);
+                    }
+#pragma unroll
+                    for (int r = 0; r < RTMAX; ++r) {
+                        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int kb = 0; kb < 2; ++kb) {
+                            acc = mfma_f16(ah[kb], qop[r][kb], acc);
+                            acc = mfma_f16(al[kb], qop[r][kb], acc);
+                        }
+                        // the owner keeps its partial; its store goes to a dump slot, so the
+                        // row-tile loop stays free of branches
+                        const int owner = r & 3;
+                        if (wl == owner) own[r >> 2][st] = acc;
+                        f32x4* dst = wl == owner ? &sm.sdump[wl][st][lane]
+                                                 : &sm.spart[r][(wl - owner - 1) & 3][st][lane];
+                        *dst = acc;
+                    }
+                }
+            }
+            __syncthreads();
+            // phase 2: stage the next tile; softmax of tile k for the owned row tiles
+            stage(k);
+            if (k < ntiles) {
+                const int t0 = s0 + k * TS;
+                const int bufk = k & 1;
+                auto softmax = [&](int j) {
+                    const int r = wl + 4 * j;
+                    f32x4 pa_[3], pb_[3];
+#pragma unroll
+                    for (int src = 0; src < 3; ++src) {
+                        pa_[src] = sm.spart[r][src][0][lane];
+                        pb_[src] = sm.spart[r][src][1][lane];
+                    }
+                    const f32x4 sa = (own[j][0] + pa_[0]) + (pa_[1] + pa_[2]);
+                    const f32x4 sb = (own[j][1] + pb_[0]) + (pb_[1] + pb_[2]);
+                    float x[8];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        x[e] = sa[e] * sl2;
+                        x[4 + e] = sb[e] * sl2;
+                    }
+                    const bool fast = t0 + TS <= (T < s1 ? T : s1) && t0 >= rlo_max[j];
+                    if (!fast) {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            const int slot = t0 + (e < 4 ? 4 * g4 + e : 16 + 4 * g4 + (e - 4));
+                            bool vis = rs[j].on && slot < s1;
+                            if (slot < T) {
+                                vis = vis && slot >= rs[j].rlo;
+                            } else {
+                                const int jn = slot - T;     // < n <= 64 whenever slot < s1
+                                vis = vis && jn < TV_MAX_NODES && ((rs[j].anc >> (jn & 63)) & 1ull) &&
+                                      (W == 0 || rs[j].dep - sm.dep[jn & 63] < W);
+                            }
+                            x[e] = vis ? x[e] : -INFINITY;
+                        }
+                    } else if (!rs[j].on) {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) x[e] = -INFINITY;
+                    }
+                    float mt = x[0];
+#pragma unroll
+                    for (int e = 1; e < 8; ++e) mt = fmaxf(mt, x[e]);
+                    // the row's 32 slots sit in the four lane groups: max over l, l^16, l^32
+                    const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(mt), __float_as_uint(mt), false, false);
+                    mt = fmaxf(__uint_as_float(s16[0]), __uint_as_float(s16[1]));
+                    const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt), false, false);
+                    mt = fmaxf(__uint_as_float(s32[0]), __uint_as_float(s32[1]));
+                    // Lazy rescaling: P is taken against a reference max that moves only when
+                    // the row max grows by more than 2^8 (so P <= 256); alpha is 1 otherwise.
+                    const bool grow = mt > rs[j].m + 8.f;
+                    const bool anyg = __builtin_amdgcn_ballot_w64(grow) != 0;
+                    const float mnew = grow ? mt : rs[j].m;
+                    const float al = rs[j].m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(rs[j].m - mnew);
+                    rs[j].m = mnew;
+                    const float m = mnew == -INFINITY ? 0.f : mnew;      // then every x is -inf
+                    f16x8 p;
+                    float ps = 0.f;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const float pe = __builtin_amdgcn_exp2f(x[e] - m);
+                        ps += pe;
+                        p[e] = static_cast<_Float16>(pe);
+                    }
+                    rs[j].l = rs[j].l * al + ps;
+                    sm.pbuf[bufk][r][lane] = p;
+                    sm.alpha[bufk][r][lane] = al;                      // row l16's factor
+                    if (lane == 0) sm.grow[bufk][r] = anyg;
+                };
+                softmax(0);
+                softmax(1);
+                if (wl + 8 < RTMAX) softmax(2);                       // row tile 8: wave 0
+            }
+            __syncthreads();
+        }
+        // epilogue: row maxima and sums for the PV waves (and the split partials)
+#pragma unroll
+        for (int j = 0; j < OWNMAX; ++j) {
+            const int r = wl + 4 * j;
+            float l = rs[j].l;
+            l += __shfl_xor(l, 16);
+            l += __shfl_xor(l, 32);
+            if (r < RT && g4 == 0) {
+                sm.mfin[r * 16 + l16] = rs[j].m;
+                sm.lfin[r * 16 + l16] = l;
+                const int row = rowbase + r * 16 + l16;
+                if (L.nsplit > 1 && row < L.rows) {
+                    L.mpart[part * L.rows_pad + row] = rs[j].m;
+                    L.lpart[part * L.rows_pad + row] = l;
+                }
+            }
+        }
+        __syncthreads();
+    } else {
+        // ------------------------------------------------------------ PV waves
+        f32x4 oacc[RTMAX][4];
+#pragma unroll
+        for (int r = 0; r < RTMAX; ++r)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) oacc[r][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+        for (int k = 0; k <= ntiles; ++k) {
+            // phase 1: this wave's 64 columns of V for tile k-1 into fp16 hi/lo, slot-major.
+            // Lane: 4 slots x 4 columns of one block per pass; the bytes are transposed first
+            // (slot pairs per column), so the fp16 pairs come out slot-major.
+            if (k >= 1) {
+                const uint8_t* raw = sm.rawv[(k - 1) & 1];
+                const int hb = lane >> 5, sq = (lane >> 3) & 3, cq = lane & 7;
+                const int kb = 2 * wl + hb, e0 = 4 * cq;
+                const int o = VT == TV_Q8_0 ? 34 * kb + 2 + e0 : 18 * kb + 2 + (e0 & 15);
+                const int sh = e0 >= 16 ? 4 : 0;
+                const f16x2 bias = static_cast<_Float16>(ints_bias<VT>());
+#pragma unroll
+                for (int pass = 0; pass < 2; ++pass) {
+                    const int sbase = 16 * pass + 4 * sq;
+                    uint32_t w[4];
+                    _Float16 dd[4];
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) {
+                        const uint8_t* row = raw + (sbase + s) * VF::ROW;
+                        w[s] = to_biased<VT>(bytes4_rt(row, o), sh);
+                        dd[s] = block_scale(row + kb * VF::BLK);
+                    }
+                    f16x4 hc[4], lc[4];
+#pragma unroll
+                    for (int pp = 0; pp < 2; ++pp) {
+                        // u0 = [w_a.b0, w_b.b0, w_a.b1, w_b.b1], u1 = the same for bytes 2, 3
+                        const uint32_t u0 = __builtin_amdgcn_perm(w[2 * pp + 1], w[2 * pp], 0x05010400u);
+                        const uint32_t u1 = __builtin_amdgcn_perm(w[2 * pp + 1], w[2 * pp], 0x07030602u);
+                        const f16x2 q[4] = {biased_lo(u0) - bias, biased_hi(u0) - bias, biased_lo(u1) - bias,
+                                            biased_hi(u1) - bias};
+                        const f16x2 d2 = {dd[2 * pp], dd[2 * pp + 1]};
+#pragma unroll
+                        for (int c = 0; c < 4; ++c) {
+                            f16x2 h, l;
+                            split_exact(q[c], d2, h, l);
+                            hc[c][2 * pp] = h[0];
+                            hc[c][2 * pp + 1] = h[1];
+                            lc[c][2 * pp] = l[0];
+                            lc[c][2 * pp + 1] = l[1];
+                        }
+                    }
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        *reinterpret_cast<f16x4*>(&sm.vdq[wl][0][32 * hb + e0 + c][sbase]) = hc[c];
+                        *reinterpret_cast<f16x4*>(&sm.vdq[wl][1][32 * hb + e0 + c][sbase]) = lc[c];
+                    }
+                }
+            }
+            __syncthreads();
+            // phase 2: stage the next tile; O += P V for tile k-1
+            stage(k);
+            if (k >= 1) {
+                const int bufp = (k - 1) & 1;
+                int anyg = 0;
+#pragma unroll
+                for (int r = 0; r < RTMAX; ++r) anyg |= sm.grow[bufp][r];
+                if (anyg) {
+#pragma unroll
+                    for (int r = 0; r < RTMAX; ++r) {
+                        if (!sm.grow[bufp][r]) continue;
+                        const f32x4 al = *reinterpret_cast<const f32x4*>(&sm.alpha[bufp][r][4 * g4]);
+#pragma unroll
+                        for (int jj = 0; jj < 4; ++jj) oacc[r][jj] *= al;
+                    }
+                }
+#pragma unroll
+                for (int half = 0; half < 2; ++half) {
+                    f16x8 bh[2], bl[2];
+#pragma unroll
+                    for (int jj = 0; jj < 2; ++jj) {
+                        const int col = 16 * (2 * half + jj) + l16;
+                        const f16x4 h0 = *reinterpret_cast<const f16x4*>(&sm.vdq[wl][0][col][4 * g4]);
+                        const f16x4 h1 = *reinterpret_cast<const f16x4*>(&sm.vdq[wl][0][col][16 + 4 * g4]);
+                        const f16x4 l0 = *reinterpret_cast<const f16x4*>(&sm.vdq[wl][1][col][4 * g4]);
+                        const f16x4 l1 = *reinterpret_cast<const f16x4*>(&sm.vdq[wl][1][col][16 + 4 * g4]);
+                        bh[jj] = f16x8{h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
+                        bl[jj] = f16x8{l0[0], l0[1], l0[2], l0[3], l1[0], l1[1], l1[2], l1[3]};
+                    }
+#pragma unroll
+                    for (int r = 0; r < RTMAX; ++r) {
+                        const f16x8 pa = sm.pbuf[bufp][r][lane];
+#pragma unroll
+                        for (int jj = 0; jj < 2; ++jj) {
+                            oacc[r][2 * half + jj] = mfma_f16(pa, bh[jj], oacc[r][2 * half + jj]);
+                            oacc[r][2 * half + jj] = mfma_f16(pa, bl[jj], oacc[r][2 * half + jj]);
+                        }
+                    }
+                }
+            }
+            __syncthreads();
+        }
+        __syncthreads();
+        // epilogue: this wave's 64 columns of every row
+#pragma unroll
+        for (int r = 0; r < RTMAX; ++r) {
+            if (r >= RT) continue;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                qop[t][ks][2 * e] = static_cast<_Float16>(__uint_as_float(u[e] << 16));
-                qop[t][ks][2 * e + 1] = static_cast<_Float16>(__uint_as_float(u[e] & 0xffff0000u));
-            }
-        }
-    }
-
-    f32x4 oacc[MAXRT][NTD];
+                const int rl = r * 16 + 4 * g4 + e;
+                const int row = rowbase + rl;
+                const int node = row / L.G, hh = row - node * L.G;
+                if (row >= L.rows || node >= n) continue;
+                if (L.nsplit == 1) {
+                    const float lsum = sm.lfin[rl];
+                    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+                    float* orow = a.out + ((static_cast<size_t>(b) * N + node) * a.Hq + kvh * L.G + hh) * D + 64 * wl;
 #pragma unroll
-    for (int t = 0; t < MAXRT; ++t)
-#pragma unroll
-        for (int nt = 0; nt < NTD; ++nt) oacc[t][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float mrow[MAXRT], lrow[MAXRT];
-#pragma unroll
-    for (int t = 0; t < MAXRT; ++t) {
-        mrow[t] = -INFINITY;
-        lrow[t] = 0.f;
-    }
-    const float sl2 = a.scale * kLog2e;
-    const int kbb = blk_bytes(kt), vbb = blk_bytes(vt);
-    const int krow = NB * kbb, vrow = NB * vbb;
-    const uint8_t* kbase = a.k_cache + (static_cast<size_t>(b) * a.Hkv + kvh) * a.Tcap * krow;
-    const uint8_t* vbase = a.v_cache + (static_cast<size_t>(b) * a.Hkv + kvh) * a.Tcap * vrow;
-
-    for (int t0 = s0; t0 < s1; t0 += TS) {
-        // 1. raw K and V rows of slots t0 .. t0+TS-1 into LDS (16-byte pieces; rows past the
-        //    cache end are zero, rows past s1 are masked below)
-        {
-            const int kch = TS * krow / 16, vch = TS * vrow / 16;
-            const int slots_ok = a.Tcap - t0 < TS ? a.Tcap - t0 : TS;
-            for (int c = tid; c < kch; c += THREADS) {
-                uint4 w = make_uint4(0, 0, 0, 0);
-                if (c * 16 < slots_ok * krow) w = *reinterpret_cast<const uint4*>(kbase + static_cast<size_t>(t0) * krow + c * 16);
-                *reinterpret_cast<uint4*>(&sm.kraw[c * 16]) = w;
-            }
-            for (int c = tid; c < vch; c += THREADS) {
-                uint4 w = make_uint4(0, 0, 0, 0);
-                if (c * 16 < slots_ok * vrow) w = *reinterpret_cast<const uint4*>(vbase + static_cast<size_t>(t0) * vrow + c * 16);
-                *reinterpret_cast<uint4*>(&sm.vraw[c * 16]) = w;
-            }
-        }
-        __syncthreads();
-        // 2. dequantise: K row-major (one (slot, 8 elements) piece per item), V transposed
-        //    (4 slots x 8 elements per item)
-        for (int item = tid; item < TS * (D / 8); item += THREADS) {
-            const int slot = item / (D / 8), e0 = (item % (D / 8)) * 8;
-            float x[8];
-            decode8(&sm.kraw[slot * krow + (e0 / 32) * kbb], kt, e0 % 32, x);
-            f16x8 h, l;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                _Float16 hh_, ll_;
-                split_f16(x[e], hh_, ll_);
-                h[e] = hh_;
-                l[e] = ll_;
-            }
-            *reinterpret_cast<f16x8*>(&sm.khi[slot][e0]) = h;
-            *reinterpret_cast<f16x8*>(&sm.klo[slot][e0]) = l;
-        }
-        for (int item = tid; item < (TS / 4) * (D / 8); item += THREADS) {
-            const int sq = item / (D / 8), e0 = (item % (D / 8)) * 8;
-            float x[4][8];
-#pragma unroll
-            for (int s = 0; s < 4; ++s) decode8(&sm.vraw[(4 * sq + s) * vrow + (e0 / 32) * vbb], vt, e0 % 32, x[s]);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                f16x4 h, l;
-#pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    _Float16 hh_, ll_;
-                    split_f16(x[s][e], hh_, ll_);
-                    h[s] = hh_;
-                    l[s] = ll_;
-                }
-                *reinterpret_cast<f16x4*>(&sm.vhi[e0 + e][4 * sq]) = h;
-                *reinterpret_cast<f16x4*>(&sm.vlo[e0 + e][4 * sq]) = l;
-            }
-        }
-        __syncthreads();
-
-        // 3. S^T = K Q^T for the wave's row tiles: sacc[st][t][e] = score of slot
-        //    t0 + 16 st + 4 g4 + e against row l16 of row tile t
-        f32x4 sacc[2][MAXRT];
-#pragma unroll
-        for (int st = 0; st < 2; ++st) {
-#pragma unroll
-            for (int t = 0; t < MAXRT; ++t) sacc[st][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const f16x8 ah = *reinterpret_cast<const f16x8*>(&sm.khi[st * 16 + l16][ks * 32 + 8 * g4]);
-                const f16x8 al = *reinterpret_cast<const f16x8*>(&sm.klo[st * 16 + l16][ks * 32 + 8 * g4]);
-#pragma unroll
-                for (int t = 0; t < MAXRT; ++t) {
-                    sacc[st][t] = mfma_f16(ah, qop[t][ks], sacc[st][t]);
-                    sacc[st][t] = mfma_f16(al, qop[t][ks], sacc[st][t]);
-                }
-                __builtin_amdgcn_sched_barrier(0);     // bound the operands kept live
-            }
-        }
-
-        // 4. mask, online softmax (exp2 domain), P in fp16 as the PV A operand
-        f16x8 pa[MAXRT];
-#pragma unroll
-        for (int t = 0; t < MAXRT; ++t) {
-            float sv[8];
-            float mt = -INFINITY;
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                const int slot = t0 + (k < 4 ? 4 * g4 + k : 16 + 4 * g4 + (k - 4));
-                bool vis = rnode[t] >= 0 && slot < s1;
-                if (slot < T) {
-                    vis = vis && slot >= rlo[t];
+                    for (int jj = 0; jj < 4; ++jj) orow[16 * jj + l16] = oacc[r][jj][e] * inv;
+                    if (a.lse && wl == 0 && l16 == 0)
+                        a.lse[(static_cast<size_t>(b) * N + node) * a.Hq + kvh * L.G + hh] =
+                            (sm.mfin[rl] + log2f(lsum)) * kLn2;
                 } else {
-                    const int j = slot - T;
-                    vis = vis && j < 64 && ((ranc[t] >> j) & 1ull) && (W == 0 || rdep[t] - sm.dep[j < 64 ? j : 0] < W);
+                    float* op = L.opart + (part * L.rows_pad + row) * D + 64 * wl;
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) op[16 * jj + l16] = oacc[r][jj][e];
                 }
-                const float s = (k < 4 ? sacc[0][t][k] : sacc[1][t][k - 4]) * sl2;
-                sv[k] = vis ? s : -INFINITY;
-                mt = fmaxf(mt, sv[k]);
-            }
-            mt = fmaxf(mt, __shfl_xor(mt, 16));
-            mt = fmaxf(mt, __shfl_xor(mt, 32));
-            // Lazy rescaling: P is taken against a reference max that moves only when a row's
-            // max grows by more than 2^8 (so P <= 256, still exact to fp16's relative
-            // precision); O and the sum are rescaled only then, for the whole wave at once.
-            const bool grow = mt > mrow[t] + 8.f;
-            if (__builtin_amdgcn_ballot_w64(grow)) {
-                const float mnew = grow ? mt : mrow[t];
-                const float alpha = (mnew == -INFINITY || mrow[t] == -INFINITY) ? 0.f : exp2f(mrow[t] - mnew);
-                lrow[t] *= alpha;
-                mrow[t] = mnew;
-                float af[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) af[e] = __shfl(alpha, 4 * g4 + e);
-#pragma unroll
-                for (int nt = 0; nt < NTD; ++nt)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) oacc[t][nt][e] *= af[e];
-            }
-            float psum = 0.f;
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                const float p = mrow[t] == -INFINITY ? 0.f : exp2f(sv[k] - mrow[t]);
-                pa[t][k] = static_cast<_Float16>(p);
-                psum += static_cast<float>(pa[t][k]);       // the weights actually applied
-            }
-            lrow[t] += psum;
-        }
-
-        // 5. O += P V (hi and lo parts of V)
-#pragma unroll
-        for (int nt = 0; nt < NTD; ++nt) {
-            const int e = nt * 16 + l16;
-            const f16x4 h0 = *reinterpret_cast<const f16x4*>(&sm.vhi[e][4 * g4]);
-            const f16x4 h1 = *reinterpret_cast<const f16x4*>(&sm.vhi[e][16 + 4 * g4]);
-            const f16x4 l0 = *reinterpret_cast<const f16x4*>(&sm.vlo[e][4 * g4]);
-            const f16x4 l1 = *reinterpret_cast<const f16x4*>(&sm.vlo[e][16 + 4 * g4]);
-            const f16x8 bh = {h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
-            const f16x8 bl = {l0[0], l0[1], l0[2], l0[3], l1[0], l1[1], l1[2], l1[3]};
-#pragma unroll
-            for (int t = 0; t < MAXRT; ++t) {
-                oacc[t][nt] = mfma_f16(pa[t], bh, oacc[t][nt]);
-                oacc[t][nt] = mfma_f16(pa[t], bl, oacc[t][nt]);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        __syncthreads();                               // LDS tiles are rewritten next
-    }
-
-    // 6. per-row sums across the four lane groups, then write
-#pragma unroll
-    for (int t = 0; t < MAXRT; ++t) {
-        lrow[t] += __shfl_xor(lrow[t], 16);
-        lrow[t] += __shfl_xor(lrow[t], 32);
-    }
-    const size_t part = (static_cast<size_t>(b) * a.Hkv + kvh) * L.nsplit + split;
-#pragma unroll
-    for (int t = 0; t < MAXRT; ++t) {
-        const int rt = wave + WAVES * t;
-        const int rbase = rb * ROWS_PER_BLOCK + rt * 16;
-        if (rbase >= L.rows) continue;
-        if (L.nsplit == 1) {
-            // normalise here: O rows 4 g4 + e need their row's sum and max
-            float inv[4], mx[4], sm_[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                sm_[e] = __shfl(lrow[t], 4 * g4 + e);
-                mx[e] = __shfl(mrow[t], 4 * g4 + e);
-                inv[e] = sm_[e] > 0.f ? 1.f / sm_[e] : 0.f;
-            }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = rbase + 4 * g4 + e;
-                const int node = r / L.G, hh = r - node * L.G;
-                if (r >= L.rows || node >= n) continue;
-                float* orow = a.out + ((static_cast<size_t>(b) * a.N + node) * a.Hq + kvh * L.G + hh) * D;
-#pragma unroll
-                for (int nt = 0; nt < NTD; ++nt) orow[nt * 16 + l16] = oacc[t][nt][e] * inv[e];
-                if (a.lse && l16 == 0)
-                    a.lse[(static_cast<size_t>(b) * a.N + node) * a.Hq + kvh * L.G + hh] =
-                        (mx[e] + log2f(sm_[e])) * kLn2;
-            }
-        } else {
-            float* op = L.opart + (part * L.rows_pad + rbase) * D;
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-#pragma unroll
-                for (int nt = 0; nt < NTD; ++nt) op[(4 * g4 + e) * D + nt * 16 + l16] = oacc[t][nt][e];
-            if (g4 == 0) {
-                L.mpart[part * L.rows_pad + rbase + l16] = mrow[t];
-                L.lpart[part * L.rows_pad + rbase + l16] = lrow[t];
             }
         }
     }
 }
 
 // Merges the splits of one row: O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
-template <int D>
 __global__ __launch_bounds__(64) void attn_combine_kernel(AttnLaunch L) {
     const AttnArgs& a = L.a;
     int wg = blockIdx.x;
@@ -436,8 +625,9 @@ int cu_count() {
     return cached[dev];
 }
 
-// Split policy: about one workgroup per CU, splits of at least 256 slots.  Depends only on
-// host-known sizes (n_past lives on the device), using the widest visible span.
+// Split policy: about one workgroup per CU (the LDS footprint allows one), splits of at least
+// two tiles.  Depends only on host-known sizes (n_past lives on the device), using the
+// widest visible span.
 struct SplitPlan {
     int G, rows, rows_pad, rblocks, nsplit, chunk;
 };
@@ -452,7 +642,7 @@ SplitPlan plan_splits(int B, int N, int Hq, int Hkv, int Tcap, int window, int c
     if (span < 1) span = 1;
     const long long units = static_cast<long long>(B) * Hkv * p.rblocks;
     long long ns = (cus + units - 1) / units;
-    const long long maxns = (span + 255) / 256;
+    const long long maxns = (span + 2 * TS - 1) / (2 * TS);
     if (ns > maxns) ns = maxns;
     if (ns < 1) ns = 1;
     long long chunk = (span + ns - 1) / ns;
@@ -462,21 +652,27 @@ SplitPlan plan_splits(int B, int N, int Hq, int Hkv, int Tcap, int window, int c
     return p;
 }
 
-size_t workspace_for(const SplitPlan& p, int B, int Hkv, int D) {
+size_t workspace_for(const SplitPlan& p, int B, int Hkv, int D_) {
     if (p.nsplit <= 1) return 256;
     const size_t parts = static_cast<size_t>(B) * Hkv * p.nsplit * p.rows_pad;
-    const size_t bytes = parts * (static_cast<size_t>(D) + 2) * sizeof(float);
+    const size_t bytes = parts * (static_cast<size_t>(D_) + 2) * sizeof(float);
     return (bytes + 255) / 256 * 256;
+}
+
+template <int KT, int VT>
+void launch_pair(const AttnLaunch& L, unsigned wgs, hipStream_t stream) {
+    hipLaunchKernelGGL((attn_kernel<KT, VT>), dim3(wgs), dim3(THREADS), 0, stream, L);
 }
 
 }  // namespace
 
-size_t attn_workspace_bytes(int B, int N, int Hq, int Hkv, int D, int Tcap, int window) {
+size_t attn_workspace_bytes(int B, int N, int Hq, int Hkv, int D_, int Tcap, int window) {
     const SplitPlan p = plan_splits(B, N, Hq, Hkv, Tcap, window, cu_count());
-    return workspace_for(p, B, Hkv, D);
+    return workspace_for(p, B, Hkv, D_);
 }
 
 int launch_attn(const AttnArgs& a, hipStream_t stream) {
+    if (a.D != D) return set_error(TV_EUNSUPPORTED, "attn_tree_verify: D=%d not built", a.D);
     const SplitPlan p = plan_splits(a.B, a.N, a.Hq, a.Hkv, a.Tcap, a.window, cu_count());
     AttnLaunch L;
     L.a = a;
@@ -495,10 +691,14 @@ int launch_attn(const AttnArgs& a, hipStream_t stream) {
     const long long rowsall = static_cast<long long>(a.B) * a.Hkv * p.rows;
     if (wgs > 0x7fffffffLL || rowsall > 0x7fffffffLL)
         return set_error(TV_ERANGE, "attn_tree_verify: too many work units");
-    if (a.D != 256) return set_error(TV_EUNSUPPORTED, "attn_tree_verify: D=%d not built", a.D);
-    hipLaunchKernelGGL(attn_kernel<256>, dim3(static_cast<unsigned>(wgs)), dim3(THREADS), 0, stream, L);
+    const unsigned w = static_cast<unsigned>(wgs);
+    if (a.k_type == TV_Q8_0 && a.v_type == TV_Q8_0) launch_pair<TV_Q8_0, TV_Q8_0>(L, w, stream);
+    else if (a.k_type == TV_Q8_0 && a.v_type == TV_Q4_0) launch_pair<TV_Q8_0, TV_Q4_0>(L, w, stream);
+    else if (a.k_type == TV_Q4_0 && a.v_type == TV_Q8_0) launch_pair<TV_Q4_0, TV_Q8_0>(L, w, stream);
+    else if (a.k_type == TV_Q4_0 && a.v_type == TV_Q4_0) launch_pair<TV_Q4_0, TV_Q4_0>(L, w, stream);
+    else return set_error(TV_EUNSUPPORTED, "attn_tree_verify: K/V type pair not built");
     if (p.nsplit > 1)
-        hipLaunchKernelGGL(attn_combine_kernel<256>, dim3(static_cast<unsigned>(rowsall)), dim3(64), 0, stream, L);
+        hipLaunchKernelGGL(attn_combine_kernel, dim3(static_cast<unsigned>(rowsall)), dim3(64), 0, stream, L);
     return launch_status("attn_tree_verify");
 }
 
