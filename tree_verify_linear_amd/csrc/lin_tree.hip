@@ -26,8 +26,8 @@
 //     branch-free straight-line code whose LDS addresses are compile-time offsets (nodes
 //     beyond the tree have zero coefficients); deltas stay in registers.  Per-node states
 //     are never formed; S0 is never written.
-//   * Waves are persistent (one per SIMD) and double-buffer whole units: the next unit's
-//     loads are issued before the current unit is computed, so HBM never waits on compute.
+//   * One wave per unit; several units stay resident per CU, so one unit's loads overlap
+//     another's arithmetic.  No load address depends on loaded data.
 // Commit: the accepted path's captured deltas are flushed into the state in place,
 //     S <- (prod_m g_{a_m}) S0 + sum_m c_m k_{a_m} delta_{a_m}^T,  c_m = prod_{m'>m} g_{a_m'},
 //   a streaming rank-L update (HBM bound).
@@ -149,7 +149,9 @@ __device__ __forceinline__ void load_unit(UnitIn<DK, NT, BF16IN>& in, const LinV
     const int g4 = lane >> 4, l16 = lane & 15;
     const UnitIds id = unit_ids(a, unit, ctiles, CW);
     const int N = a.N;                              // <= NMAX by dispatch
-    in.nraw = a.n_nodes[id.b];
+    // wave-uniform: read through the constant address space (a scalar load, counted apart
+    // from the vector loads and stores, so nothing waits on them for it)
+    in.nraw = ((const __attribute__((address_space(4))) int32_t*)(a.n_nodes))[id.b];
     in.praw = -1;
     in.graw = in.braw = 0u;
     if (lane < N) {
@@ -200,28 +202,30 @@ struct VerifySmem {
     static constexpr int CST = 68;                  // padded row stride of Cs (floats)
     static constexpr int GST = NT * 16 + 4;         // padded row stride of Gm
     __align__(16) float Cs[NT * 16][CST];          // Cs[c][j] = (S0^T x_c)[j0 + j]; rows n.. become outputs
+    // Three lifetimes in one place (one wave reads each before the next is written):
     union {
-        float Gm[GT * 16][GST];                     // Gm[m][c] = k_m . x_c (until the coefficients are built)
+        float Gm[GT * 16][GST];                     // Gm[m][c] = k_m . x_c, until the coefficients are built
+        struct {
+            __align__(16) float Pu[NMAX][NMAX];    // Pu[i][m], zero unless m is a strict ancestor of i
+            __align__(16) float Pw[NMAX][NMAX];    //   (both read by the walks)
+        };
         __align__(16) float Ds[NMAX][64];           // then delta_i per value channel
     };
     __align__(16) uint8_t Vs[NMAX * 64 * (BF16IN ? 2 : 4)];   // v rows of the unit, [node][channel]
-    __align__(16) float Pu[NMAX][NMAX];            // Pu[i][m], zero unless m is a strict ancestor of i
-    __align__(16) float Pw[NMAX][NMAX];
     float cv[NMAX], ca[NMAX], cb[NMAX], cd[NMAX];   // per-node scalars of the walk
     float gl[NMAX];
     int par[NMAX];
 };
 
 template <int DK, int NT, bool BF16IN>
-__device__ __forceinline__ void compute_unit(const UnitIn<DK, NT, BF16IN>& in, VerifySmem<NT, BF16IN>& sm,
-                                             const LinVerifyArgs& a, int unit, int ctiles, int CW, int lane) {
+__device__ __forceinline__ int compute_unit(const UnitIn<DK, NT, BF16IN>& in, VerifySmem<NT, BF16IN>& sm,
+                                            const LinVerifyArgs& a, int unit, int ctiles, int CW, int lane) {
     using U = UnitIn<DK, NT, BF16IN>;
     constexpr int KS = U::KS, NMAX = U::NMAX, GT = (NMAX + 15) / 16;
     const int g4 = lane >> 4, l16 = lane & 15;
     const int N = a.N;
     const int n = clampi(in.nraw, 0, N);
-    if (n <= 0) return;
-    const UnitIds id = unit_ids(a, unit, ctiles, CW);
+    if (n <= 0) return 0;
     const int MT = CW >> 4;
     // this lane's node (lane < n): parent, decay and write strength; zero beyond the tree
     const bool real = lane < n;
@@ -294,6 +298,7 @@ __device__ __forceinline__ void compute_unit(const UnitIn<DK, NT, BF16IN>& in, V
         uint64_t am = 0;
         for (int m = pme; m >= 0; m = sm.par[m]) am |= 1ull << m;
         const int li = real ? lane : 0;
+        const float cdv = a.scale * sm.Gm[li][N + li];   // before the rows below replace Gm
         float run = 1.f;                            // product of g over ancestors below m
         float pu[NMAX], pw[NMAX];
 #pragma unroll
@@ -311,7 +316,7 @@ __device__ __forceinline__ void compute_unit(const UnitIn<DK, NT, BF16IN>& in, V
         sm.cv[lane] = bme;                          // run is now G_parent
         sm.ca[lane] = bme * gme * run;
         sm.cb[lane] = a.scale * gme * run;
-        sm.cd[lane] = a.scale * sm.Gm[li][N + li];
+        sm.cd[lane] = cdv;
     }
     __syncthreads();
     auto v_of = [&](int i) {
@@ -356,59 +361,47 @@ __device__ __forceinline__ void compute_unit(const UnitIn<DK, NT, BF16IN>& in, V
     }
     __syncthreads();
 
-    // 6. deltas (Ds rows 0..n-1) and outputs (Cs rows N..N+n-1): 16-byte stores, four rows
-    //    per instruction.
-    {
-        const size_t rowbase = (static_cast<size_t>(id.b) * a.N * a.Hv + id.h) * a.dv + id.j0;
-        const size_t ostep = static_cast<size_t>(a.Hv) * a.dv;
-        const int c4 = (lane & 15) * 4;
-        for (int r = lane >> 4; r < 2 * n; r += 4) {
-            const bool isd = r < n;
-            const int i = isd ? r : r - n;
-            if (c4 < CW) {
-                float* dst = (isd ? a.cap_delta : a.out) + rowbase + i * ostep + c4;
-                *reinterpret_cast<float4*>(dst) = *reinterpret_cast<const float4*>(isd ? &sm.Ds[i][c4] : &sm.Cs[N + i][c4]);
-            }
+    return n;
+}
+
+// The unit's deltas (Ds rows 0..n-1) and outputs (Cs rows N..N+n-1): 16-byte stores, four
+// rows per instruction.  Issued after the next unit's inputs have landed, so the wait for
+// those inputs never includes these stores.
+template <int NT, bool BF16IN>
+__device__ __forceinline__ void store_unit(VerifySmem<NT, BF16IN>& sm, const LinVerifyArgs& a, int unit, int n,
+                                           int ctiles, int CW, int lane) {
+    const int N = a.N;
+    const UnitIds id = unit_ids(a, unit, ctiles, CW);
+    const size_t rowbase = (static_cast<size_t>(id.b) * a.N * a.Hv + id.h) * a.dv + id.j0;
+    const size_t ostep = static_cast<size_t>(a.Hv) * a.dv;
+    const int c4 = (lane & 15) * 4;
+    for (int r = lane >> 4; r < 2 * n; r += 4) {
+        const bool isd = r < n;
+        const int i = isd ? r : r - n;
+        if (c4 < CW) {
+            float* dst = (isd ? a.cap_delta : a.out) + rowbase + i * ostep + c4;
+            *reinterpret_cast<float4*>(dst) = *reinterpret_cast<const float4*>(isd ? &sm.Ds[i][c4] : &sm.Cs[N + i][c4]);
         }
     }
     __syncthreads();                                // LDS is reused by the next unit
 }
 
-// Units of this persistent wave: the XCD it runs on owns one contiguous range of units
-// (workgroup ids are dealt round-robin to the 8 XCDs), taken in turn by its waves.
-struct UnitRange {
-    int first, end, stride;
-};
-__device__ __forceinline__ UnitRange wave_units(int total) {
-    constexpr int kXcd = 8;
-    const int w = blockIdx.x, G = gridDim.x;
-    const int x = w % kXcd, lw = w / kXcd;
-    const int waves_x = G / kXcd + (x < G % kXcd ? 1 : 0);
-    const int q = total / kXcd, r = total % kXcd;
-    const int start = x * q + (x < r ? x : r), cnt = q + (x < r ? 1 : 0);
-    return {start + lw, start + cnt, waves_x};
-}
-
-// Verify for trees of up to 32 nodes: persistent waves, two units in flight per wave.
+// Verify for trees of up to 32 nodes: one unit per workgroup of one wave.  The hardware
+// dispatcher keeps several units resident per CU (registers allow two waves per SIMD, the
+// LDS footprint seven workgroups per CU), so one unit's memory latency hides behind
+// another's arithmetic.
 template <int DK, int NT, bool BF16IN>
-__global__ __launch_bounds__(64, 1) void lin_verify_kernel(LinVerifyArgs a, int total_units) {
+__global__ __launch_bounds__(64, 2) void lin_verify_kernel(LinVerifyArgs a) {
     static_assert(NT <= 4, "register walk is for trees of up to 32 nodes");
     __shared__ VerifySmem<NT, BF16IN> sm;
     const int lane = threadIdx.x;
     const int CW = a.dv < 64 ? a.dv : 64;
     const int ctiles = a.dv / CW;
-    const UnitRange ur = wave_units(total_units);
-    // One copy of the unit code (it is large; two copies would crowd the instruction cache):
-    // the prefetched unit is moved into place at the end of each step.
-    UnitIn<DK, NT, BF16IN> cur;
-    if (ur.first < ur.end) load_unit(cur, a, ur.first, ctiles, CW, lane);
-    for (int u = ur.first; u < ur.end; u += ur.stride) {
-        UnitIn<DK, NT, BF16IN> nxt;
-        const bool more = u + ur.stride < ur.end;
-        if (more) load_unit(nxt, a, u + ur.stride, ctiles, CW, lane);
-        compute_unit(cur, sm, a, u, ctiles, CW, lane);
-        if (more) cur = nxt;
-    }
+    const int u = xcd_remap(blockIdx.x, gridDim.x);
+    UnitIn<DK, NT, BF16IN> in;
+    load_unit(in, a, u, ctiles, CW, lane);
+    const int n = compute_unit(in, sm, a, u, ctiles, CW, lane);
+    store_unit(sm, a, u, n, ctiles, CW, lane);
 }
 
 // Verify for trees of 33..64 nodes: the same math, one unit per wave, with the walk driven
@@ -607,19 +600,6 @@ __global__ __launch_bounds__(256) void lin_commit_kernel(LinCommitArgs a, int ro
     if (t + 256 < nvec) update(s1, t + 256);
 }
 
-// Waves the persistent verify kernel keeps resident: one per SIMD on every CU.
-int resident_waves() {
-    static int cached[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 1024;
-    if (!cached[dev]) {
-        int cus = 0;
-        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-        cached[dev] = cus * 4;
-    }
-    return cached[dev];
-}
-
 template <int DK, int NT>
 int launch_verify_dk_nt(const LinVerifyArgs& a, bool bf16, hipStream_t stream) {
     const int CW = a.dv < 64 ? a.dv : 64;
@@ -627,11 +607,9 @@ int launch_verify_dk_nt(const LinVerifyArgs& a, bool bf16, hipStream_t stream) {
     if (units > 0x7fffffffLL) return set_error(TV_ERANGE, "lin_tree_verify: too many work units (%lld)", units);
     dim3 block(64);
     if constexpr (NT <= 4) {
-        const long long waves = resident_waves();
-        dim3 grid(static_cast<unsigned>(units < waves ? units : waves));
-        const int total = static_cast<int>(units);
-        if (bf16) hipLaunchKernelGGL((lin_verify_kernel<DK, NT, true>), grid, block, 0, stream, a, total);
-        else hipLaunchKernelGGL((lin_verify_kernel<DK, NT, false>), grid, block, 0, stream, a, total);
+        dim3 grid(static_cast<unsigned>(units));
+        if (bf16) hipLaunchKernelGGL((lin_verify_kernel<DK, NT, true>), grid, block, 0, stream, a);
+        else hipLaunchKernelGGL((lin_verify_kernel<DK, NT, false>), grid, block, 0, stream, a);
     } else {
         dim3 grid(static_cast<unsigned>(units));
         if (bf16) hipLaunchKernelGGL((lin_verify_big_kernel<DK, NT, true>), grid, block, 0, stream, a);
