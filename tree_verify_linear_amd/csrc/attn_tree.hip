@@ -176,7 +176,9 @@ __global__ __launch_bounds__(THREADS, 1) void attn_kernel(AttnLaunch L) {
     using KF = Fmt<KT>;
     using VF = Fmt<VT>;
     constexpr int KCH = TS * KF::ROW / 16, VCH = TS * VF::ROW / 16;    // 16-byte pieces per tile
-    constexpr int STG = THREADS;                                        // staging threads (all)
+    // Staging threads: every wave but scoring wave 0, which owns a third softmax row tile
+    // (9 row tiles over 4 scoring waves) and would otherwise set the pace of phase 2.
+    constexpr int STG = THREADS - 64;
     constexpr int KPT = (KCH + STG - 1) / STG, VPT = (VCH + STG - 1) / STG;
     __shared__ AttnSmem sm;
     const AttnArgs& a = L.a;
@@ -220,21 +222,21 @@ __global__ __launch_bounds__(THREADS, 1) void attn_kernel(AttnLaunch L) {
 
     const uint8_t* kbase = a.k_cache + (static_cast<size_t>(b) * a.Hkv + kvh) * a.Tcap * KF::ROW;
     const uint8_t* vbase = a.v_cache + (static_cast<size_t>(b) * a.Hkv + kvh) * a.Tcap * VF::ROW;
-    // raw tile staging (all threads): 16-byte pieces, rows past the cache end read as zero
+    // raw tile staging: 16-byte pieces, rows past the cache end read as zero
     uint4 rk[KPT], rv[VPT];
     auto gload = [&](int tile) {
         const int t0 = s0 + tile * TS;
         const int slots_ok = a.Tcap - t0 < TS ? a.Tcap - t0 : TS;
 #pragma unroll
         for (int x = 0; x < KPT; ++x) {
-            const int c = tid + x * STG;
+            const int c = (tid - 64) + x * STG;
             rk[x] = make_uint4(0, 0, 0, 0);
             if (c < KCH && c * 16 < slots_ok * KF::ROW)
                 rk[x] = *reinterpret_cast<const uint4*>(kbase + static_cast<size_t>(t0) * KF::ROW + c * 16);
         }
 #pragma unroll
         for (int x = 0; x < VPT; ++x) {
-            const int c = tid + x * STG;
+            const int c = (tid - 64) + x * STG;
             rv[x] = make_uint4(0, 0, 0, 0);
             if (c < VCH && c * 16 < slots_ok * VF::ROW)
                 rv[x] = *reinterpret_cast<const uint4*>(vbase + static_cast<size_t>(t0) * VF::ROW + c * 16);
@@ -243,25 +245,26 @@ __global__ __launch_bounds__(THREADS, 1) void attn_kernel(AttnLaunch L) {
     auto lstore = [&](int tile) {
 #pragma unroll
         for (int x = 0; x < KPT; ++x) {
-            const int c = tid + x * STG;
+            const int c = (tid - 64) + x * STG;
             if (c < KCH) *reinterpret_cast<uint4*>(&sm.rawk[c * 16]) = rk[x];
         }
 #pragma unroll
         for (int x = 0; x < VPT; ++x) {
-            const int c = tid + x * STG;
+            const int c = (tid - 64) + x * STG;
             if (c < VCH) *reinterpret_cast<uint4*>(&sm.rawv[tile & 1][c * 16]) = rv[x];
         }
     };
     // Raw tile k+1 into LDS (rawk was last read by the scores of tile k, rawv[(k+1)&1] by the
     // dequantisation of tile k-1, both before the phase barrier), then loads of tile k+2.
+    const bool stager = tid >= 64;
     auto stage = [&](int k) {
-        if (k + 1 < ntiles) {
+        if (stager && k + 1 < ntiles) {
             lstore(k + 1);
             if (k + 2 < ntiles) gload(k + 2);
         }
     };
 
-    if (ntiles > 0) {
+    if (stager && ntiles > 0) {
         gload(0);
         lstore(0);
         if (ntiles > 1) gload(1);
