@@ -552,8 +552,14 @@ __global__ __launch_bounds__(256) void lin_commit_kernel(LinCommitArgs a, int ro
     float4* S = reinterpret_cast<float4*>(a.state + ((static_cast<size_t>(b) * a.Hv + h) * a.dv + j0) * dk);
     const int nvec = rows * dk / 4;
     float4 s0 = make_float4(0.f, 0.f, 0.f, 0.f), s1 = s0;
-    if (t < nvec) s0 = S[t];
-    if (t + 256 < nvec) s1 = S[t + 256];
+    // the state is streamed once: non-temporal loads and stores keep it out of the caches
+    f32x4* Sv = reinterpret_cast<f32x4*>(S);
+    auto ld = [&](int v) {
+        const f32x4 x = __builtin_nontemporal_load(&Sv[v]);
+        return make_float4(x[0], x[1], x[2], x[3]);
+    };
+    if (t < nvec) s0 = ld(t);
+    if (t + 256 < nvec) s1 = ld(t + 256);
 
     if (t < L) {
         const int node = clampi(a.path[static_cast<size_t>(b) * a.Lmax + t], 0, a.N - 1);
@@ -571,9 +577,25 @@ __global__ __launch_bounds__(256) void lin_commit_kernel(LinCommitArgs a, int ro
     }
     float* Kc = smem;
     float* cd = smem + L * dk;
-    for (int idx = t; idx < L * dk; idx += 256) {
-        const int m = idx / dk, r = idx - m * dk;
-        Kc[idx] = load_scalar<BF16IN>(a.k, ((static_cast<size_t>(b) * a.N + ap[m]) * a.Hk + kh) * dk + r);
+    if constexpr (BF16IN) {
+        // eight bf16 keys per 16-byte load (dk is a multiple of 16)
+        for (int idx = t; idx < L * dk / 8; idx += 256) {
+            const int m = idx / (dk / 8), r = (idx - m * (dk / 8)) * 8;
+            const uint4 w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.k) +
+                                                          ((static_cast<size_t>(b) * a.N + ap[m]) * a.Hk + kh) * dk + r);
+            const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+            float* dst = &Kc[m * dk + r];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                dst[2 * e] = __uint_as_float(u[e] << 16);
+                dst[2 * e + 1] = __uint_as_float(u[e] & 0xffff0000u);
+            }
+        }
+    } else {
+        for (int idx = t; idx < L * dk; idx += 256) {
+            const int m = idx / dk, r = idx - m * dk;
+            Kc[idx] = load_scalar<BF16IN>(a.k, ((static_cast<size_t>(b) * a.N + ap[m]) * a.Hk + kh) * dk + r);
+        }
     }
     __syncthreads();
     for (int idx = t; idx < L * rows; idx += 256) {
@@ -594,7 +616,7 @@ __global__ __launch_bounds__(256) void lin_commit_kernel(LinCommitArgs a, int ro
             s.z = fmaf(c, kk.z, s.z);
             s.w = fmaf(c, kk.w, s.w);
         }
-        S[v] = s;
+        __builtin_nontemporal_store(f32x4{s.x, s.y, s.z, s.w}, &Sv[v]);
     };
     if (t < nvec) update(s0, t);
     if (t + 256 < nvec) update(s1, t + 256);
