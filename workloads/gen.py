@@ -13,6 +13,8 @@ Shapes follow the library's layouts (row-major, innermost last):
 * tree: ``parent[B][Nmax]`` int32 (``-1`` for the root and for padding rows beyond
   ``n_nodes[b]``); ``n_nodes[B]`` int32.
 * accepted path: ``path[B][Lmax]`` int32 (``-1`` padding), ``path_len[B]`` int32.
+* acceptance: draft ``tokens[B][N]`` int32 (distinct among siblings; node 0 holds the last
+  committed token) and target ``logits[B][N][V]`` (bf16 bits or fp32).
 
 bf16 tensors are returned as ``uint16`` bit patterns (round-to-nearest-even from fp32).
 """
@@ -24,7 +26,7 @@ from dataclasses import dataclass, field
 import numpy as np
 
 # Tensor ids used in the seed tuple.
-T_TREE, T_PATH, T_Q, T_K, T_V, T_G, T_BETA, T_STATE, T_AQ, T_KC, T_VC, T_LOGITS = range(12)
+T_TREE, T_PATH, T_Q, T_K, T_V, T_G, T_BETA, T_STATE, T_AQ, T_KC, T_VC, T_LOGITS, T_DTOK, T_TLOGIT = range(14)
 
 QK8_0_BYTES = 34   # fp16 scale + 32 int8
 QK4_0_BYTES = 18   # fp16 scale + 16 bytes of packed nibbles
@@ -390,3 +392,59 @@ def workload_long_context(window: int = 0, T: int = 131072, n_lin: int = 16, n_a
     while li < n_lin:
         order.append(("lin", li)); li += 1
     return Workload(f"long-context-t{T}-w{window}", lin=lins, attn=attns, order=order)
+
+
+# ----------------------------------------------------------------------------- acceptance
+
+@dataclass
+class AcceptInputs:
+    dtype: str
+    logits: np.ndarray      # [B][N][V] bf16 bits (uint16) or float32
+    tokens: np.ndarray      # [B][N] int32 draft tokens
+    parent: np.ndarray
+    n_nodes: np.ndarray
+    V: int
+
+
+def gen_accept(cfg: int, parents, V: int, dtype: str = "bf16", match_p: float = 0.75, tie_p: float = 0.0,
+               layer: int = 0, seq_ids=None) -> AcceptInputs:
+    """Draft tokens (distinct among the children of each node) and target logits ~ N(0, 1)
+    with one planted maximum (8 + |N(0, 0.5)|) per node.  With probability ``match_p`` the
+    planted token is a random child's draft token, so the greedy walk descends; with
+    probability ``tie_p`` a second random index receives exactly the same value."""
+    seq_ids = list(range(len(parents))) if seq_ids is None else list(seq_ids)
+    parent, n_nodes = pad_trees(parents)
+    B, N = parent.shape
+    tokens = np.zeros((B, N), dtype=np.int32)
+    logits = np.zeros((B, N, V), dtype=np.uint16 if dtype == "bf16" else np.float32)
+    for b, sid in enumerate(seq_ids):
+        n = int(n_nodes[b])
+        rt = rng_for(cfg, sid, layer, T_DTOK)
+        tok = rt.integers(0, V, size=N).astype(np.int64)
+        kids = [[c for c in range(1, n) if int(parent[b, c]) == p] for p in range(n)]
+        for ch in kids:
+            seen = set()
+            for c in ch:
+                while int(tok[c]) in seen:
+                    tok[c] = int(rt.integers(0, V))
+                seen.add(int(tok[c]))
+        tokens[b] = tok
+        rl = rng_for(cfg, sid, layer, T_TLOGIT)
+        x = rl.standard_normal((N, V), dtype=np.float32)
+        for i in range(n):
+            if kids[i] and rl.random() < match_p:
+                t = int(tok[kids[i][int(rl.integers(0, len(kids[i])))]])
+            else:
+                t = int(rl.integers(0, V))
+            x[i, t] = np.float32(8.0 + abs(rl.normal(0.0, 0.5)))
+            if tie_p > 0 and rl.random() < tie_p:
+                x[i, int(rl.integers(0, V))] = x[i, t]
+        logits[b] = f32_to_bf16_bits(x) if dtype == "bf16" else x
+    return AcceptInputs(dtype, logits, tokens, parent, n_nodes, V)
+
+
+def workload_accept(B: int = 64, V: int = 151936, dtype: str = "bf16", cfg: int = 3, seq_ids=None,
+                    tie_p: float = 0.0) -> AcceptInputs:
+    """Greedy acceptance over the batched step's trees (same seeds as ``workload_batched``)."""
+    parents, _ = trees_for(cfg, B, "ddtree", seq_ids=seq_ids)
+    return gen_accept(cfg, parents, V, dtype, tie_p=tie_p, layer=50, seq_ids=seq_ids)
