@@ -18,7 +18,10 @@ timed region.
 
 Output: one JSON line.  ``roofline`` is for the kernel with the largest mean duration;
 its ``traffic`` is read from the committed hardware-counter summary under ``profiles/``
-when that summary was taken on the current kernel source (else null).  ``cpu_baseline``
+when that summary was taken on the current kernel source (else null).  ``next_kernels``
+times, after the step and outside ``value``, the greedy acceptance of the step's trees
+(vocabulary 151936, bf16 logits) and the compaction of the attention cache to the
+accepted paths.  ``cpu_baseline``
 times the fp64 CPU oracle over whole sequences of the same workload for about ten
 seconds.
 
@@ -93,6 +96,22 @@ def attn_bytes(A) -> int:
         committed = T if A.window == 0 else min(T, A.window - 1)
         total += A.Hkv * (committed + n) * rb + n * Hq * (D * 2 + D * 4 + 4)
     return total
+
+
+def accept_bytes(X) -> int:
+    """Logits of every valid node read once, the tree and draft tokens, and the outputs
+    (argmax per node, path, its length, the next token)."""
+    B, N, V = X.logits.shape
+    eb = X.logits.itemsize
+    return int(X.n_nodes.sum()) * V * eb + X.parent.nbytes + X.tokens.nbytes + X.n_nodes.nbytes + 4 * (2 * B * N + 2 * B)
+
+
+def compact_bytes(path, path_len, Hkv, rk, rv) -> int:
+    """Each moved row (accepted node not already in place) read once and written once in
+    both caches, plus the path."""
+    import numpy as np
+    moved = sum(int(np.count_nonzero(path[b][:path_len[b]] != np.arange(path_len[b]))) for b in range(len(path_len)))
+    return moved * Hkv * (rk + rv) * 2 + path.nbytes + path_len.nbytes
 
 
 def attn_flops(A) -> float:
@@ -209,6 +228,74 @@ def cpu_baseline(L, A, budget_s: float):
     }
 
 
+def time_next_rows(args, tvl, torch, dev, d, A, B):
+    """Greedy acceptance over the step's trees (vocabulary 151936, bf16 logits) and the
+    compaction of the attention layer's cache to the accepted paths.  Timed on their own,
+    after the step; they are not part of ``value``."""
+    import numpy as np
+    from workloads import workload_accept, row_bytes
+
+    sets = [workload_accept(B), workload_accept(B, seq_ids=list(range(B, 2 * B)))]
+    devs = []
+    for X in sets:
+        lg = torch.from_numpy(np.ascontiguousarray(X.logits).view(np.int16)).view(torch.bfloat16).to(dev)
+        i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)  # noqa: E731
+        devs.append(dict(logits=lg, parent=i32(X.parent), n_nodes=i32(X.n_nodes), tokens=i32(X.tokens)))
+    N, V = sets[0].logits.shape[1], sets[0].logits.shape[2]
+    ws = torch.empty(max(tvl.tree_accept_workspace_bytes(B, N, V), 256), dtype=torch.uint8, device=dev)
+    outs = [torch.empty((B, N), dtype=torch.int32, device=dev), torch.empty((B, N), dtype=torch.int32, device=dev),
+            torch.empty((B,), dtype=torch.int32, device=dev), torch.empty((B,), dtype=torch.int32, device=dev)]
+
+    def accept(i):
+        x = devs[i % 2]
+        return tvl.tree_accept_greedy(x["logits"], x["parent"], x["n_nodes"], x["tokens"], *outs, workspace=ws)
+
+    reps = max(args.steps, 5)
+    for i in range(2):
+        accept(i)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record()
+    for i in range(reps):
+        accept(i)
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    acc_ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(reps)]
+
+    # Compaction of the attention cache along the paths accepted by the last call above.
+    path, plen = outs[1].clone(), outs[2].clone()
+    torch.cuda.synchronize()
+    ph, lh = path.cpu().numpy(), plen.cpu().numpy()
+    rk, rv = row_bytes(A.k_type, A.D), row_bytes(A.v_type, A.D)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    tvl.kv_tree_compact(d["kc"], d["vc"], A.k_type, A.v_type, d["n_past"], path, plen)
+    torch.cuda.synchronize()
+    ev[0].record()
+    for i in range(reps):
+        tvl.kv_tree_compact(d["kc"], d["vc"], A.k_type, A.v_type, d["n_past"], path, plen)
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    cmp_ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(reps)]
+
+    def entry(ms_list, nbytes, extra):
+        ms = sum(ms_list) / len(ms_list)
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        return dict(mean_us=round(ms * 1e3, 2), median_us=round(sorted(ms_list)[len(ms_list) // 2] * 1e3, 2),
+                    algorithmic_MB=round(nbytes / 1e6, 3), GB_per_s=round(gbs, 1),
+                    frac_hbm_peak=round(gbs / HBM_PEAK_GBS, 4), **extra)
+
+    ab = sum(accept_bytes(X) for X in sets) / len(sets)
+    cb = compact_bytes(ph, lh, A.Hkv, rk, rv)
+    print(f"# timed acceptance and compaction ({reps} calls each)", file=sys.stderr, flush=True)
+    return {
+        "tree_accept_greedy": entry(acc_ms, ab, {"workload": f"{B} sequences x 22-node trees, vocabulary {V}, "
+                                                             "bf16 logits (argmax + walk, two launches)"}),
+        "kv_tree_compact": entry(cmp_ms, cb, {"workload": f"{B} sequences, Hkv {A.Hkv}, D {A.D}, {A.k_type}/"
+                                                          f"{A.v_type}, accepted paths (mean length "
+                                                          f"{float(lh.mean()):.2f})"}),
+    }
+
+
 # ----------------------------------------------------------------------------- main
 
 def main():
@@ -311,6 +398,8 @@ def main():
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": counter_traffic(dom),
                 "algorithmic_bytes_per_launch": int(byts[dom])}
 
+    next_kernels = time_next_rows(args, tvl, torch, dev, pool[0], A0, B)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(L0, A0, args.cpu_seconds)
@@ -333,6 +422,7 @@ def main():
                                f"dk=dv=128 fp32 state + commit, attention Hq24/Hkv4 D256 Q8_0 T=4096 window 2048",
                    "global_batch": B, "tree_nodes": 22, "kv_type": "q8_0", "window": 2048, "n_past": 4096},
         "kernels": kernels,
+        "next_kernels": next_kernels,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

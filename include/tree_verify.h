@@ -13,6 +13,12 @@
  *   attn_tree_verify  full-attention layer: tree-masked softmax attention over a Q8_0 /
  *                     Q4_0 quantised KV cache with an optional sliding window.
  *
+ * Two more close the loop from scores to the next step:
+ *
+ *   tree_accept_greedy  argmax of every node's logits and the greedy walk that picks the
+ *                       accepted root path (the path the commit calls take);
+ *   kv_tree_compact     moves the accepted nodes' K/V rows to the committed prefix.
+ *
  * Sources (page title, section):
  *   "Luce DFlash" server README -- "How it works" (DDTree tree verify: one forward scores
  *     the whole tree through a mask derived from parent pointers; per-step rollback of the
@@ -191,6 +197,68 @@ int attn_tree_verify(int B, int N, int Hq, int Hkv, int D, int Tcap, int k_type,
                      const int32_t* n_past, const void* q, const void* k_cache,
                      const void* v_cache, float* out, float* lse, void* workspace,
                      size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace tree_accept_greedy needs (0 for invalid sizes or dtype). */
+size_t tree_accept_workspace_bytes(int B, int N, int V, int dtype);
+
+/*
+ * tree_accept_greedy -- greedy acceptance of the draft tree from the target's logits.
+ * ("Luce DFlash" README, "How it works": one forward scores the whole tree, then the
+ * committed prefix is advanced to the accepted path; "Scope and limits": verification is
+ * argmax, and temperature 0 keeps the committed tokens exactly the greedy ones.)
+ *
+ *   target[b][i] = argmax_v logits[b][i][v] for i < n_nodes[b]: the lowest index holding
+ *                  the largest value, NaN entries never selected, 0 for a row that is all
+ *                  NaN; -1 for n_nodes[b] <= i < N.  +0 and -0 compare equal.
+ *   The walk starts at the root (node 0, always accepted).  From accepted node p the next
+ *   accepted node is the lowest-index child c of p (parent[c] == p, c < n_nodes[b]) whose
+ *   draft token tokens[b][c] equals target[b][p]; it stops when no child matches.
+ *   path[b][m]     the m-th accepted node, root first, -1 for m >= path_len[b] (m < N)
+ *   path_len[b]    accepted nodes, root included (1 <= path_len[b] <= n_nodes[b])
+ *   next_token[b]  target[b][last accepted node]: the token committed after the accepted
+ *                  draft tokens.
+ *
+ *   B, N       sequences; tree rows per sequence (1 <= N <= 64)
+ *   V          vocabulary size (logits per row)
+ *   dtype      TV_BF16 or TV_F32: the logits' element type
+ *   logits     device, [B][N][V] of dtype, 16-byte aligned; rows beyond n_nodes are not read
+ *   parent, n_nodes  device, see "Tree representation" (n_nodes is clamped into [1, N])
+ *   tokens     device, int32 [B][N]: draft token of each node (the root's is ignored)
+ *   target     device, int32 [B][N]          path  device, int32 [B][N]
+ *   path_len, next_token   device, int32 [B]
+ *   workspace  device, >= tree_accept_workspace_bytes(B, N, V, dtype) bytes, 256-byte
+ *              aligned; needs no initialisation, garbage afterwards
+ * The outputs feed lin_tree_commit (path, path_len, Lmax = N) and kv_tree_compact.
+ */
+int tree_accept_greedy(int B, int N, int V, int dtype, const void* logits,
+                       const int32_t* parent, const int32_t* n_nodes, const int32_t* tokens,
+                       int32_t* target, int32_t* path, int32_t* path_len,
+                       int32_t* next_token, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
+/*
+ * kv_tree_compact -- moves the accepted tree nodes' K/V rows to the committed prefix.
+ * ("Luce DFlash" README, "How it works": after acceptance the KV cache is restored to the
+ * committed prefix, which then ends with the accepted path.)
+ *
+ * For each sequence b with T = n_past[b] and m < path_len[b]: the row of every KV head at
+ * slot T + path[b][m] (where verify stored node path[b][m]) is copied byte for byte to slot
+ * T + m, in both caches.  All sources are read before any destination is written, so the
+ * result does not depend on the order of the moves.  Every other slot keeps its bytes.
+ * Moves whose source or destination slot falls outside [0, Tcap), or whose node index is
+ * negative, are skipped; path_len is clamped into [0, Lmax].  The caller advances n_past
+ * by path_len afterwards.
+ *
+ *   B, Hkv, D, Tcap, k_type, v_type   as for attn_tree_verify; D a multiple of 32, <= 512
+ *   n_past     device, int32 [B]
+ *   path       device, int32 [B][Lmax] (as written by tree_accept_greedy with Lmax = N)
+ *   path_len   device, int32 [B]
+ *   Lmax       row stride of path, 1 <= Lmax <= 64
+ *   k_cache, v_cache   device, in/out, 16-byte aligned, layouts as for attn_tree_verify
+ */
+int kv_tree_compact(int B, int Hkv, int D, int Tcap, int k_type, int v_type,
+                    const int32_t* n_past, const int32_t* path, const int32_t* path_len,
+                    int Lmax, void* k_cache, void* v_cache, void* stream);
 
 /* Host-side checks of tree metadata (host pointers).  TV_OK or TV_ETOPO / TV_EPATH /
  * TV_EINVAL / TV_ERANGE with a message naming the first offending entry. */

@@ -132,3 +132,50 @@ def test_validate_tree_and_path():
         tvl.validate_path(parent, n, path, L + 30)
     ok0 = np.zeros_like(L)
     tvl.validate_path(parent, n, path, ok0)                # empty paths are allowed
+
+
+def test_accept_argument_errors():
+    L = tvl.lib()
+    f = _fake()
+    V = 151936
+
+    def call(B=2, N=22, V=V, dtype=1, ptr=f, logits=None, ws=1 << 30):
+        lg = f if logits is None else logits
+        return L.tree_accept_greedy(B, N, V, dtype, lg, *([ptr] * 7), f, ws, None)
+
+    assert call(B=0) == tvl.TV_EINVAL
+    assert call(V=0) == tvl.TV_EINVAL
+    assert call(N=65) == tvl.TV_ERANGE
+    assert call(dtype=3) == tvl.TV_EUNSUPPORTED
+    assert b"TV_BF16" in L.tv_last_error()
+    assert call(ptr=None) == tvl.TV_EINVAL
+    assert call(logits=ctypes.c_void_p(4098)) == tvl.TV_EINVAL      # misaligned logits
+    assert b"aligned" in L.tv_last_error()
+    need = tvl.tree_accept_workspace_bytes(2, 22, V)
+    # one 64-bit partial per (sequence, node, chunk of 16384 bf16 logits), rounded to 256 bytes
+    assert need == -(-2 * 22 * 10 * 8 // 256) * 256
+    assert tvl.tree_accept_workspace_bytes(2, 22, V, __import__("torch").float32) == -(-2 * 22 * 19 * 8 // 256) * 256
+    assert call(ws=need - 1) == tvl.TV_ERANGE
+    assert b"workspace" in L.tv_last_error()
+    assert L.tree_accept_workspace_bytes(2, 65, V, 1) == 0
+    assert L.tree_accept_workspace_bytes(2, 22, V, 5) == 0
+
+
+def test_compact_argument_errors():
+    L = tvl.lib()
+    f = _fake()
+
+    def call(B=2, Hkv=4, D=256, Tcap=4200, kt=0, vt=0, Lmax=22, ptr=f, cache=None):
+        c = f if cache is None else cache
+        return L.kv_tree_compact(B, Hkv, D, Tcap, kt, vt, ptr, ptr, ptr, Lmax, c, c, None)
+
+    assert call(Hkv=0) == tvl.TV_EINVAL
+    assert call(D=48) == tvl.TV_EUNSUPPORTED
+    assert call(D=544) == tvl.TV_EUNSUPPORTED
+    assert call(vt=4) == tvl.TV_EUNSUPPORTED
+    assert b"supported pairs" in L.tv_last_error()
+    assert call(Lmax=0) == tvl.TV_ERANGE
+    assert call(Lmax=65) == tvl.TV_ERANGE
+    assert call(ptr=None) == tvl.TV_EINVAL
+    assert call(cache=ctypes.c_void_p(4104)) == tvl.TV_EINVAL
+    assert b"aligned" in L.tv_last_error()

@@ -15,7 +15,8 @@ import os
 import torch
 
 __all__ = ["TreeVerifyError", "lib", "lib_path", "lin_tree_verify", "lin_tree_commit",
-           "attn_tree_verify", "attn_tree_workspace_bytes", "validate_tree", "validate_path",
+           "attn_tree_verify", "attn_tree_workspace_bytes", "tree_accept_greedy",
+           "tree_accept_workspace_bytes", "kv_tree_compact", "validate_tree", "validate_path",
            "abi_version", "KV_TYPES", "EXPORTS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -33,6 +34,9 @@ EXPORTS = {
     "lin_tree_commit": (_i, [_i, _i, _i, _i, _i, _i, _i, _i, _p, _p, _i, _p, _p, _p, _p, _p]),
     "attn_tree_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
     "attn_tree_verify": (_i, [_i, _i, _i, _i, _i, _i, _i, _i, _i, _f, _p, _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
+    "tree_accept_workspace_bytes": (_sz, [_i, _i, _i, _i]),
+    "tree_accept_greedy": (_i, [_i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
+    "kv_tree_compact": (_i, [_i, _i, _i, _i, _i, _i, _p, _p, _p, _i, _p, _p, _p]),
     "tv_validate_tree": (_i, [_p, _p, _i, _i]),
     "tv_validate_path": (_i, [_p, _p, _p, _p, _i, _i, _i]),
     "tv_last_error": (ctypes.c_char_p, []),
@@ -172,6 +176,51 @@ def attn_tree_verify(q, k_cache, v_cache, k_type: str, v_type: str, n_past, pare
                                   _ptr(v_cache), _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
                                   _stream(q.device)))
     return out, lse
+
+
+def tree_accept_workspace_bytes(B: int, N: int, V: int, dtype=torch.bfloat16) -> int:
+    return int(lib().tree_accept_workspace_bytes(B, N, V, _in_dtype(torch.empty(0, dtype=dtype))))
+
+
+def tree_accept_greedy(logits, parent, n_nodes, tokens, target=None, path=None, path_len=None,
+                       next_token=None, workspace=None):
+    """Greedy acceptance from the target's logits (bf16 or fp32 ``[B][N][V]``).  Returns
+    ``(target, path, path_len, next_token)``: int32 ``[B][N]``, ``[B][N]``, ``[B]``, ``[B]``."""
+    B, N, V = logits.shape
+    _dev(logits, "logits", (torch.bfloat16, torch.float32))
+    _dev(parent, "parent", torch.int32, (B, N)); _dev(n_nodes, "n_nodes", torch.int32, (B,))
+    _dev(tokens, "tokens", torch.int32, (B, N))
+    dev = logits.device
+    target = torch.empty((B, N), dtype=torch.int32, device=dev) if target is None else target
+    path = torch.empty((B, N), dtype=torch.int32, device=dev) if path is None else path
+    path_len = torch.empty((B,), dtype=torch.int32, device=dev) if path_len is None else path_len
+    next_token = torch.empty((B,), dtype=torch.int32, device=dev) if next_token is None else next_token
+    _dev(target, "target", torch.int32, (B, N)); _dev(path, "path", torch.int32, (B, N))
+    _dev(path_len, "path_len", torch.int32, (B,)); _dev(next_token, "next_token", torch.int32, (B,))
+    if workspace is None:
+        workspace = torch.empty(max(tree_accept_workspace_bytes(B, N, V, logits.dtype), 256), dtype=torch.uint8,
+                                device=dev)
+    _dev(workspace, "workspace", torch.uint8)
+    _check(lib().tree_accept_greedy(B, N, V, _in_dtype(logits), _ptr(logits), _ptr(parent), _ptr(n_nodes),
+                                    _ptr(tokens), _ptr(target), _ptr(path), _ptr(path_len), _ptr(next_token),
+                                    _ptr(workspace), workspace.numel(), _stream(dev)))
+    return target, path, path_len, next_token
+
+
+def kv_tree_compact(k_cache, v_cache, k_type: str, v_type: str, n_past, path, path_len):
+    """Move each sequence's accepted tree rows (slot n_past + path[m]) to slot n_past + m,
+    in place, in both caches ``[B][Hkv][Tcap][row bytes]`` (uint8)."""
+    B, Hkv, Tcap, rk = k_cache.shape
+    D = rk // KV_BLOCK_BYTES[k_type] * 32
+    _dev(k_cache, "k_cache", torch.uint8, (B, Hkv, Tcap, D // 32 * KV_BLOCK_BYTES[k_type]))
+    _dev(v_cache, "v_cache", torch.uint8, (B, Hkv, Tcap, D // 32 * KV_BLOCK_BYTES[v_type]))
+    _dev(n_past, "n_past", torch.int32, (B,))
+    _dev(path, "path", torch.int32); _dev(path_len, "path_len", torch.int32, (B,))
+    if path.dim() != 2 or path.shape[0] != B:
+        raise ValueError(f"path has shape {tuple(path.shape)}, expected ({B}, Lmax)")
+    _check(lib().kv_tree_compact(B, Hkv, D, Tcap, KV_TYPES[k_type], KV_TYPES[v_type], _ptr(n_past), _ptr(path),
+                                 _ptr(path_len), path.shape[1], _ptr(k_cache), _ptr(v_cache), _stream(k_cache.device)))
+    return k_cache, v_cache
 
 
 def _host_i32(a, name):

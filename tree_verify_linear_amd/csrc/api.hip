@@ -173,4 +173,60 @@ int attn_tree_verify(int B, int N, int Hq, int Hkv, int D, int Tcap, int k_type,
     return launch_attn(a, static_cast<hipStream_t>(stream));
 }
 
+size_t tree_accept_workspace_bytes(int B, int N, int V, int dtype) {
+    clear_error();
+    if (B <= 0 || N <= 0 || N > TV_MAX_NODES || V <= 0 || (dtype != TV_F32 && dtype != TV_BF16)) return 0;
+    return accept_workspace_bytes(B, N, V, dtype == TV_BF16);
+}
+
+int tree_accept_greedy(int B, int N, int V, int dtype, const void* logits, const int32_t* parent,
+                       const int32_t* n_nodes, const int32_t* tokens, int32_t* target, int32_t* path,
+                       int32_t* path_len, int32_t* next_token, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+    clear_error();
+    const char* fn = "tree_accept_greedy";
+    if (B <= 0 || N <= 0 || V <= 0)
+        return set_error(TV_EINVAL, "%s: sizes must be positive (B=%d N=%d V=%d)", fn, B, N, V);
+    if (N > TV_MAX_NODES) return set_error(TV_ERANGE, "%s: N=%d exceeds %d tree nodes", fn, N, TV_MAX_NODES);
+    if (dtype != TV_F32 && dtype != TV_BF16)
+        return set_error(TV_EUNSUPPORTED, "%s: dtype %d not built; supported: TV_F32, TV_BF16", fn, dtype);
+    if (!logits || !parent || !n_nodes || !tokens || !target || !path || !path_len || !next_token || !workspace)
+        return set_error(TV_EINVAL, "%s: null pointer argument", fn);
+    if (!aligned(logits, 16) || !aligned(workspace, 256))
+        return set_error(TV_EINVAL, "%s: logits must be 16-byte aligned, workspace 256-byte aligned", fn);
+    if (static_cast<double>(B) * N * V > 9.0e15) return set_error(TV_ERANGE, "%s: tensor sizes overflow", fn);
+    const size_t need = accept_workspace_bytes(B, N, V, dtype == TV_BF16);
+    if (workspace_bytes < need)
+        return set_error(TV_ERANGE, "%s: workspace of %zu bytes is smaller than the %zu needed", fn, workspace_bytes, need);
+    AcceptArgs a{B, N, V, dtype == TV_BF16, logits, parent, n_nodes, tokens, target, path, path_len, next_token,
+                 workspace};
+    return launch_accept(a, static_cast<hipStream_t>(stream));
+}
+
+int kv_tree_compact(int B, int Hkv, int D, int Tcap, int k_type, int v_type, const int32_t* n_past,
+                    const int32_t* path, const int32_t* path_len, int Lmax, void* k_cache, void* v_cache,
+                    void* stream) {
+    clear_error();
+    const char* fn = "kv_tree_compact";
+    if (B <= 0 || Hkv <= 0 || D <= 0 || Tcap <= 0)
+        return set_error(TV_EINVAL, "%s: sizes must be positive (B=%d Hkv=%d D=%d Tcap=%d)", fn, B, Hkv, D, Tcap);
+    if (D % 32 != 0 || D > 512)
+        return set_error(TV_EUNSUPPORTED, "%s: D=%d not built; supported: multiples of 32 up to 512", fn, D);
+    const bool kt_ok = k_type == TV_Q8_0 || k_type == TV_Q4_0, vt_ok = v_type == TV_Q8_0 || v_type == TV_Q4_0;
+    if (!kt_ok || !vt_ok)
+        return set_error(TV_EUNSUPPORTED,
+                         "%s: K/V type pair (%d, %d) not built; supported pairs: (Q8_0, Q8_0), (Q8_0, Q4_0), "
+                         "(Q4_0, Q8_0), (Q4_0, Q4_0)", fn, k_type, v_type);
+    if (Lmax < 1 || Lmax > TV_MAX_NODES)
+        return set_error(TV_ERANGE, "%s: Lmax=%d not in [1, %d]", fn, Lmax, TV_MAX_NODES);
+    if (!n_past || !path || !path_len || !k_cache || !v_cache) return set_error(TV_EINVAL, "%s: null pointer argument", fn);
+    if (!aligned(k_cache, 16) || !aligned(v_cache, 16))
+        return set_error(TV_EINVAL, "%s: the caches must be 16-byte aligned", fn);
+    const int rk = D / 32 * (k_type == TV_Q8_0 ? 34 : 18), rv = D / 32 * (v_type == TV_Q8_0 ? 34 : 18);
+    if (static_cast<double>(B) * Hkv * Tcap * (rk > rv ? rk : rv) > 9.0e15)
+        return set_error(TV_ERANGE, "%s: cache sizes overflow", fn);
+    KvCompactArgs a{B, Hkv, Tcap, Lmax, rk, rv, n_past, path, path_len, k_cache, v_cache};
+    return launch_kv_compact(a, static_cast<hipStream_t>(stream));
+}
+
 }  // extern "C"

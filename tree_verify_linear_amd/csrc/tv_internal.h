@@ -58,6 +58,33 @@ struct AttnArgs {
 size_t attn_workspace_bytes(int B, int N, int Hq, int Hkv, int D, int Tcap, int window);
 int launch_attn(const AttnArgs& a, hipStream_t stream);
 
+struct AcceptArgs {
+    int B, N, V;
+    bool bf16;
+    const void* logits;
+    const int32_t* parent;
+    const int32_t* n_nodes;
+    const int32_t* tokens;
+    int32_t* target;
+    int32_t* path;
+    int32_t* path_len;
+    int32_t* next_token;
+    void* workspace;
+};
+int accept_chunks(int V, bool bf16);
+size_t accept_workspace_bytes(int B, int N, int V, bool bf16);
+int launch_accept(const AcceptArgs& a, hipStream_t stream);
+
+struct KvCompactArgs {
+    int B, Hkv, Tcap, Lmax, rk, rv;
+    const int32_t* n_past;
+    const int32_t* path;
+    const int32_t* path_len;
+    void* k_cache;
+    void* v_cache;
+};
+int launch_kv_compact(const KvCompactArgs& a, hipStream_t stream);
+
 // ---------------------------------------------------------------- device helpers
 #if defined(__HIP_DEVICE_COMPILE__) || defined(__HIPCC__)
 // Consecutive workgroup ids are dealt round-robin to the 8 XCDs (each with its own L2).

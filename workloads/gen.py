@@ -425,7 +425,8 @@ def gen_accept(cfg: int, parents, V: int, dtype: str = "bf16", match_p: float = 
         for ch in kids:
             seen = set()
             for c in ch:
-                while int(tok[c]) in seen:
+                # distinct among siblings while the vocabulary allows it
+                while int(tok[c]) in seen and len(seen) < V:
                     tok[c] = int(rt.integers(0, V))
                 seen.add(int(tok[c]))
         tokens[b] = tok
