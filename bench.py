@@ -25,6 +25,11 @@ accepted paths.  ``cpu_baseline``
 times the fp64 CPU oracle over whole sequences of the same workload for about ten
 seconds.
 
+Warm-up runs at least --warmup steps and keeps going until --min-warmup-s (0.3 s) have
+passed: the clock ramps up over the first ~40 ms of sustained work, and timings taken
+inside the ramp read up to 15% slow.  ``warmup`` in the JSON line is the number of
+warm-up steps actually run.
+
     python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline]
 """
 from __future__ import annotations
@@ -56,6 +61,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--min-warmup-s", type=float, default=0.3,
+                    help="keep running untimed warm-up steps until this many seconds have passed (the "
+                         "GPU clock ramps up over the first ~40 ms of sustained work)")
     ap.add_argument("--batch", type=int, default=64)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle timing")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU oracle sample budget")
@@ -253,8 +261,13 @@ def time_next_rows(args, tvl, torch, dev, d, A, B):
         return tvl.tree_accept_greedy(x["logits"], x["parent"], x["n_nodes"], x["tokens"], *outs, workspace=ws)
 
     reps = max(args.steps, 5)
-    for i in range(2):
+    w0 = time.perf_counter()
+    i = 0
+    while i < 2 or time.perf_counter() - w0 < args.min_warmup_s / 3:
         accept(i)
+        i += 1
+        if i % 16 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
     ev[0].record()
@@ -375,17 +388,24 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    for i in range(args.warmup):
-        step(i)
+    # Warm-up: at least --warmup steps, and untimed steps until --min-warmup-s have passed, so
+    # the timed steps run at the clock the GPU holds under sustained load.
+    w0 = time.perf_counter()
+    warm = 0
+    while warm < args.warmup or time.perf_counter() - w0 < args.min_warmup_s:
+        step(warm)
+        warm += 1
+        if warm % 16 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
-    print("# warmup done", file=sys.stderr, flush=True)
+    print(f"# warmup done: {warm} steps in {time.perf_counter() - w0:.2f} s", file=sys.stderr, flush=True)
 
     K = args.steps
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
     torch.cuda.synchronize()
     h0 = time.perf_counter()
     for i in range(K):
-        step(args.warmup + i, evs[i])
+        step(warm + i, evs[i])
     torch.cuda.synchronize()
     host_ms = (time.perf_counter() - h0) * 1e3 / K
     per = {n: [] for n in names}
@@ -431,7 +451,7 @@ def main():
         "unit": "node-layers/s",
         "n_gpus": 1,
         "steps": K,
-        "warmup": args.warmup,
+        "warmup": warm,
         "ms_per_step": round(ms_step, 4),
         "host_ms_per_step": round(host_ms, 4),
         "higher_is_better": True,
