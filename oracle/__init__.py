@@ -14,7 +14,8 @@ Sources (page title, section):
   (every 4th layer is softmax attention with 24 query / 4 KV heads of length 256, the
   rest Gated DeltaNet with a recurrent state cache); "Asymmetric K/V quantization" and
   the results table on long context (Q8_0 / Q4_0 KV cache, the FA window, 0 = full);
-  "Scope and limits" (the verify skeleton stays argmax: greedy acceptance).
+  "Scope and limits" (the verify skeleton stays argmax: greedy acceptance); the
+  tree-aware convolution window gathered along the parent chain ("How it works").
 * PR #606 "perf(qwen36): add SpecLA factor-capture speculative decoding" -- "Paper
   mapping" (the method needs scored candidates plus parent topology; a chain is a
   degenerate tree) and the review comment naming the commit / flush routines.
@@ -34,3 +35,4 @@ from .attention import (dequant_q8_0, dequant_q4_0, dequant_rows, attn_tree_veri
                         attn_tree_verify_rows, visible_slots)
 from .accept import (logits_f64, argmax_rows, greedy_walk, tree_accept_greedy,  # noqa: F401
                      kv_compact)
+from .conv import conv_tree_verify, conv_tree_commit  # noqa: F401
