@@ -53,6 +53,8 @@ KERNEL_SOURCES = {
     "attn_tree_verify": "tree_verify_linear_amd/csrc/attn_tree.hip",
     "tree_accept_greedy": "tree_verify_linear_amd/csrc/accept.hip",
     "kv_tree_compact": "tree_verify_linear_amd/csrc/accept.hip",
+    "conv_tree_verify": "tree_verify_linear_amd/csrc/conv_tree.hip",
+    "conv_tree_commit": "tree_verify_linear_amd/csrc/conv_tree.hip",
 }
 
 
@@ -122,6 +124,27 @@ def compact_bytes(path, path_len, Hkv, rk, rv) -> int:
     import numpy as np
     moved = sum(int(np.count_nonzero(path[b][:path_len[b]] != np.arange(path_len[b]))) for b in range(len(path_len)))
     return moved * Hkv * (rk + rv) * 2 + path.nbytes + path_len.nbytes
+
+
+def conv_verify_bytes(X) -> int:
+    """Every valid node's input row read once and its output row written once, the committed
+    window and the weights read once."""
+    eb = X.x.itemsize
+    nodes = int(X.n_nodes.sum())
+    B = X.x.shape[0]
+    return nodes * X.C * (eb + 4) + B * (X.K - 1) * X.C * 4 + X.C * X.K * 4 + X.parent.nbytes + X.n_nodes.nbytes
+
+
+def conv_commit_bytes(X) -> int:
+    """Per sequence with an accepted path: the K-1 new window rows read (from the window or
+    the accepted inputs) and written."""
+    eb = X.x.itemsize
+    total = 0
+    for L in X.path_len:
+        m = min(int(L), X.K - 1)
+        if L > 0:
+            total += X.C * ((X.K - 1 - m) * 4 + m * eb + (X.K - 1) * 4)
+    return total + X.path.nbytes + X.path_len.nbytes
 
 
 def attn_flops(A) -> float:
@@ -315,6 +338,54 @@ def time_next_rows(args, tvl, torch, dev, d, A, B):
                     algorithmic_MB=round(nbytes / 1e6, 3), GB_per_s=round(gbs, 1),
                     frac_hbm_peak=round(gbs / HBM_PEAK_GBS, 4), **extra)
 
+    # Tree convolution over the step's trees at the linear layer's q|k|v width (10240
+    # channels, window width 4), then the commit of its window along the accepted paths.
+    from workloads import workload_conv
+    csets = [workload_conv(B), workload_conv(B, seq_ids=list(range(B, 2 * B)))]
+    cdev = []
+    for X in csets:
+        xd = torch.from_numpy(np.ascontiguousarray(X.x).view(np.int16)).view(torch.bfloat16).to(dev)
+        cdev.append(dict(x=xd, w=torch.from_numpy(X.weight).to(dev), st=torch.from_numpy(X.state).to(dev),
+                         parent=i32(X.parent), n=i32(X.n_nodes), path=i32(X.path), plen=i32(X.path_len),
+                         y=torch.empty((B, X.x.shape[1], X.C), dtype=torch.float32, device=dev)))
+
+    def conv(i):
+        c = cdev[i % 2]
+        tvl.conv_tree_verify(c["x"], c["w"], c["st"], c["parent"], c["n"], "silu", y=c["y"])
+
+    for i in range(4):
+        conv(i)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record()
+    for i in range(reps):
+        conv(i)
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    conv_ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(reps)]
+
+    cc = cdev[0]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        tvl.conv_tree_commit(cc["st"], cc["x"], cc["path"], cc["plen"])
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    cgraph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(cgraph):
+        for _ in range(reps):
+            tvl.conv_tree_commit(cc["st"], cc["x"], cc["path"], cc["plen"])
+    cgraph.replay()
+    torch.cuda.synchronize()
+    ccommit_ms = []
+    for j in range(3):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        cgraph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ccommit_ms.append(e0.elapsed_time(e1) / reps)
+
     ab = sum(accept_bytes(X) for X in sets) / len(sets)
     cb = compact_bytes(ph, lh, A.Hkv, rk, rv)
     print(f"# timed acceptance and compaction ({reps} calls each)", file=sys.stderr, flush=True)
@@ -322,6 +393,14 @@ def time_next_rows(args, tvl, torch, dev, d, A, B):
         "tree_accept_greedy": entry(acc_ms, ab, {"counter_traffic_bytes": counter_traffic("tree_accept_greedy"),
                                                  "workload": f"{B} sequences x 22-node trees, vocabulary {V}, "
                                                              "bf16 logits (argmax + walk, two launches)"}),
+        "conv_tree_verify": entry(conv_ms, sum(conv_verify_bytes(X) for X in csets) / 2,
+                                  {"counter_traffic_bytes": counter_traffic("conv_tree_verify"),
+                                   "workload": f"{B} sequences x 22-node trees, 10240 channels, window 4, bf16 "
+                                               "inputs, SiLU"}),
+        "conv_tree_commit": entry(ccommit_ms, conv_commit_bytes(csets[0]),
+                                  {"counter_traffic_bytes": counter_traffic("conv_tree_commit"),
+                                   "workload": f"{B} sequences, 10240 channels, window 4, accepted paths; timed "
+                                               f"as graph replays of {reps} calls"}),
         "kv_tree_compact": entry(cmp_ms, cb, {"counter_traffic_bytes": counter_traffic("kv_tree_compact"),
                                               "workload": f"{B} sequences, Hkv {A.Hkv}, D {A.D}, {A.k_type}/"
                                                           f"{A.v_type}, accepted paths (mean length "

@@ -19,6 +19,12 @@
  *                       accepted root path (the path the commit calls take);
  *   kv_tree_compact     moves the accepted nodes' K/V rows to the committed prefix.
  *
+ * and two cover the short causal convolution in front of the linear layers:
+ *
+ *   conv_tree_verify    each node's convolution over its window of earlier inputs taken
+ *                       along its parent chain;
+ *   conv_tree_commit    moves the committed window to the end of the accepted path.
+ *
  * Sources (page title, section):
  *   "Luce DFlash" server README -- "How it works" (DDTree tree verify: one forward scores
  *     the whole tree through a mask derived from parent pointers; per-step rollback of the
@@ -95,6 +101,9 @@ typedef enum { TV_HEADS_CONTIGUOUS = 0, TV_HEADS_TILED = 1 } tv_head_group;
  * Q4_0: 18 bytes {fp16 d; uint8 qs[16]}, x[e] = d * ((qs[e] & 15) - 8) for e < 16 and
  *       x[e + 16] = d * ((qs[e] >> 4) - 8).                                          */
 typedef enum { TV_Q8_0 = 0, TV_Q4_0 = 1 } tv_kv_type;
+
+/* Activation after the tree convolution. */
+typedef enum { TV_ACT_NONE = 0, TV_ACT_SILU = 1 } tv_activation;
 
 /*
  * lin_tree_verify -- one gated delta-rule layer over the draft tree.
@@ -259,6 +268,55 @@ int tree_accept_greedy(int B, int N, int V, int dtype, const void* logits,
 int kv_tree_compact(int B, int Hkv, int D, int Tcap, int k_type, int v_type,
                     const int32_t* n_past, const int32_t* path, const int32_t* path_len,
                     int Lmax, void* k_cache, void* v_cache, void* stream);
+
+/*
+ * conv_tree_verify -- causal depthwise convolution of width K over the draft tree.
+ * ("Luce DFlash" README, "How it works": the recurrent state rolled back after acceptance
+ * includes the convolution window, and the tree-aware convolution gathers each node's
+ * window of earlier inputs along its parent chain, not in node order.)
+ *
+ * For sequence b, node i < n_nodes[b] and channel c:
+ *     y[b][i][c] = act( sum_{k<K} weight[c][k] * u_k )
+ * where u_{K-1} = x[b][i][c], u_{K-2} = x[b][parent(i)][c], ... up the root path, and
+ * positions above the root come from the committed window: the j-th step above the root
+ * reads conv_state[b][K-1-j][c] (oldest first, so conv_state[b][K-2] is the most recent
+ * committed input).  On a chain this is ordinary causal 1-D convolution with the window
+ * as left context.  act is the identity or SiLU (v * sigmoid(v)).
+ *
+ *   B, N       sequences; tree rows per sequence (1 <= N <= 64)
+ *   C          channels, a multiple of 8 (the linear layer's q|k|v projections)
+ *   K          convolution width, 2..8 (a model parameter)
+ *   dtype      TV_F32 or TV_BF16: element type of x
+ *   activation tv_activation
+ *   parent, n_nodes   device, see "Tree representation"
+ *   x          device, [B][N][C] of dtype
+ *   weight     device, fp32 [C][K]; weight[c][K-1] multiplies the node's own input
+ *   conv_state device, fp32 [B][K-1][C], read only
+ *   y          device, fp32 [B][N][C]
+ * x, weight, conv_state and y must be 16-byte aligned.
+ */
+int conv_tree_verify(int B, int N, int C, int K, int dtype, int activation,
+                     const int32_t* parent, const int32_t* n_nodes, const void* x,
+                     const float* weight, const float* conv_state, float* y, void* stream);
+
+/*
+ * conv_tree_commit -- moves the committed window to the end of the accepted path, in place.
+ * ("Luce DFlash" README, "How it works": after accept the window is restored to the
+ * committed prefix, which now ends with the accepted path.)
+ *
+ * With L = path_len[b] (clamped into [0, Lmax]) and the accepted inputs x[b][path[b][m]],
+ * the new window is the last K-1 entries of (conv_state[b][0..K-2], accepted inputs in path
+ * order).  L = 0 leaves it unchanged.  Path entries are clamped into [0, N-1].
+ *
+ *   B, N, C, K, dtype   as for conv_tree_verify
+ *   path, path_len      device, int32 [B][Lmax] and [B] (as for lin_tree_commit)
+ *   Lmax                row stride of path, 1 <= Lmax <= N
+ *   x                   device, [B][N][C] of dtype (the inputs the verify call saw)
+ *   conv_state          device, fp32 [B][K-1][C], in/out
+ */
+int conv_tree_commit(int B, int N, int C, int K, int dtype, const int32_t* path,
+                     const int32_t* path_len, int Lmax, const void* x, float* conv_state,
+                     void* stream);
 
 /* Host-side checks of tree metadata (host pointers).  TV_OK or TV_ETOPO / TV_EPATH /
  * TV_EINVAL / TV_ERANGE with a message naming the first offending entry. */

@@ -179,3 +179,26 @@ def test_compact_argument_errors():
     assert call(ptr=None) == tvl.TV_EINVAL
     assert call(cache=ctypes.c_void_p(4104)) == tvl.TV_EINVAL
     assert b"aligned" in L.tv_last_error()
+
+
+def test_conv_argument_errors():
+    L = tvl.lib()
+    f = _fake()
+
+    def verify(B=2, N=22, C=10240, K=4, dtype=1, act=0, ptr=f, x=None):
+        xx = f if x is None else x
+        return L.conv_tree_verify(B, N, C, K, dtype, act, ptr, ptr, xx, ptr, ptr, ptr, None)
+
+    assert verify(C=0) == tvl.TV_EINVAL
+    assert verify(N=65) == tvl.TV_ERANGE
+    assert verify(K=1) == tvl.TV_EUNSUPPORTED and b"2..8" in L.tv_last_error()
+    assert verify(K=9) == tvl.TV_EUNSUPPORTED
+    assert verify(C=10244) == tvl.TV_EUNSUPPORTED and b"multiple of 8" in L.tv_last_error()
+    assert verify(dtype=4) == tvl.TV_EUNSUPPORTED
+    assert verify(act=2) == tvl.TV_EINVAL
+    assert verify(ptr=None) == tvl.TV_EINVAL
+    assert verify(x=ctypes.c_void_p(4100)) == tvl.TV_EINVAL and b"aligned" in L.tv_last_error()
+    assert L.conv_tree_commit(2, 22, 10240, 4, 1, f, f, 0, f, f, None) == tvl.TV_ERANGE      # Lmax 0
+    assert L.conv_tree_commit(2, 22, 10240, 4, 1, f, f, 23, f, f, None) == tvl.TV_ERANGE     # Lmax > N
+    assert L.conv_tree_commit(2, 22, 10240, 4, 1, None, f, 22, f, f, None) == tvl.TV_EINVAL
+    assert L.conv_tree_commit(2, 22, 10240, 9, 1, f, f, 22, f, f, None) == tvl.TV_EUNSUPPORTED

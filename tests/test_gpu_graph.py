@@ -1,10 +1,10 @@
 """Every entry point can be captured into a HIP graph and replayed: the library launches
 only kernels on the caller's stream (no allocation, no memset, no synchronisation).
 
-The graph holds one full step on 8 sequences -- linear verify, attention, acceptance,
-linear commit and KV compaction -- and is replayed three times with eager work and host
-synchronisations in between.  The in-place buffers (state and caches) are restored
-eagerly before each replay.  Every replay must reproduce the eager results bit for bit
+The graph holds one full step on 8 sequences -- tree convolution, linear verify, attention,
+acceptance, linear commit, convolution-window commit and KV compaction -- and is replayed
+three times with eager work and host synchronisations in between.  The in-place buffers
+(states, window and caches) are restored eagerly before each replay.  Every replay must reproduce the eager results bit for bit
 (all kernels are deterministic).
 """
 import numpy as np
@@ -13,7 +13,7 @@ import torch
 
 import tree_verify_linear_amd as tvl
 from tvutil import attn_to_device, lin_to_device, t_bits, t_i32
-from workloads import workload_batched, workload_accept
+from workloads import workload_batched, workload_accept, workload_conv
 
 pytestmark = pytest.mark.gpu
 
@@ -23,41 +23,47 @@ def test_graph_capture_and_replay_of_a_full_step():
     W = workload_batched(B)
     L, A = W.lin[0], W.attn[0]
     X = workload_accept(B, V=40000)
+    CV = workload_conv(B, C=2048)
+    cx, cw, cst = t_bits(CV.x), torch.from_numpy(CV.weight).cuda(), torch.from_numpy(CV.state).cuda()
     dl, da = lin_to_device(L), attn_to_device(A)
     logits = t_bits(X.logits)
     xp, xn, xt = t_i32(X.parent), t_i32(X.n_nodes), t_i32(X.tokens)
     N = L.parent.shape[1]
     Hkv, Tcap = A.k_cache.shape[1], A.k_cache.shape[2]
 
-    state0, k0, v0 = dl["state"].clone(), da["k_cache"].clone(), da["v_cache"].clone()
+    state0, k0, v0, cst0 = dl["state"].clone(), da["k_cache"].clone(), da["v_cache"].clone(), cst.clone()
     outs = dict(
         out=torch.empty((B, N, L.Hv, L.dv), device="cuda"), cap=torch.empty((B, N, L.Hv, L.dv), device="cuda"),
         aout=torch.empty((B, N, A.Hq, A.D), device="cuda"), lse=torch.empty((B, N, A.Hq), device="cuda"),
         tgt=torch.empty((B, N), dtype=torch.int32, device="cuda"), path=torch.empty((B, N), dtype=torch.int32, device="cuda"),
-        plen=torch.empty((B,), dtype=torch.int32, device="cuda"), nxt=torch.empty((B,), dtype=torch.int32, device="cuda"))
+        plen=torch.empty((B,), dtype=torch.int32, device="cuda"), nxt=torch.empty((B,), dtype=torch.int32, device="cuda"),
+        cy=torch.empty((B, N, CV.C), device="cuda"))
     aws = torch.empty(max(tvl.attn_tree_workspace_bytes(B, N, A.Hq, Hkv, A.D, Tcap, A.window), 256),
                       dtype=torch.uint8, device="cuda")
     cws = torch.empty(max(tvl.tree_accept_workspace_bytes(B, N, X.V), 256), dtype=torch.uint8, device="cuda")
 
     def step():
         o = outs
+        tvl.conv_tree_verify(cx, cw, cst, dl["parent"], dl["n_nodes"], "silu", y=o["cy"])
         tvl.lin_tree_verify(dl["q"], dl["k"], dl["v"], dl["g"], dl["beta"], dl["state"], dl["parent"],
                             dl["n_nodes"], L.scale, out=o["out"], cap_delta=o["cap"])
         tvl.attn_tree_verify(da["q"], da["k_cache"], da["v_cache"], A.k_type, A.v_type, da["n_past"], da["parent"],
                              da["n_nodes"], A.window, A.scale, out=o["aout"], lse=o["lse"], workspace=aws)
         tvl.tree_accept_greedy(logits, xp, xn, xt, o["tgt"], o["path"], o["plen"], o["nxt"], workspace=cws)
         tvl.lin_tree_commit(dl["state"], dl["path"], dl["path_len"], dl["k"], dl["g"], o["cap"])
+        tvl.conv_tree_commit(cst, cx, o["path"], o["plen"])
         tvl.kv_tree_compact(da["k_cache"], da["v_cache"], A.k_type, A.v_type, da["n_past"], o["path"], o["plen"])
 
     def restore():
         dl["state"].copy_(state0)
         da["k_cache"].copy_(k0)
         da["v_cache"].copy_(v0)
+        cst.copy_(cst0)
 
     def snapshot():
         torch.cuda.synchronize()
         r = {k: v.clone() for k, v in outs.items()}
-        r.update(state=dl["state"].clone(), kc=da["k_cache"].clone(), vc=da["v_cache"].clone())
+        r.update(state=dl["state"].clone(), kc=da["k_cache"].clone(), vc=da["v_cache"].clone(), cst=cst.clone())
         return r
 
     for v in outs.values():
@@ -90,5 +96,5 @@ def test_graph_capture_and_replay_of_a_full_step():
         # eager work between replays
         tmp = torch.randn(1 << 20, device="cuda")
         assert np.isfinite(float(tmp.sum()))
-    print(f"[graph] 3 replays of a 5-call step identical to eager; mean path length "
+    print(f"[graph] 3 replays of a 7-call step identical to eager; mean path length "
           f"{float(eager['plen'].float().mean()):.2f}")

@@ -16,7 +16,8 @@ import torch
 
 __all__ = ["TreeVerifyError", "lib", "lib_path", "lin_tree_verify", "lin_tree_commit",
            "attn_tree_verify", "attn_tree_workspace_bytes", "tree_accept_greedy",
-           "tree_accept_workspace_bytes", "kv_tree_compact", "validate_tree", "validate_path",
+           "tree_accept_workspace_bytes", "kv_tree_compact", "conv_tree_verify", "conv_tree_commit",
+           "validate_tree", "validate_path",
            "abi_version", "KV_TYPES", "EXPORTS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -26,6 +27,7 @@ TV_OK, TV_EINVAL, TV_EUNSUPPORTED, TV_ERANGE, TV_ETOPO, TV_EPATH, TV_EDEVICE = r
 TV_F32, TV_BF16 = 0, 1
 HEAD_GROUPS = {"contiguous": 0, "tiled": 1}
 KV_TYPES = {"q8_0": 0, "q4_0": 1}
+ACTIVATIONS = {"none": 0, "silu": 1}
 KV_BLOCK_BYTES = {"q8_0": 34, "q4_0": 18}
 
 _i, _f, _p, _sz = ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
@@ -37,6 +39,8 @@ EXPORTS = {
     "tree_accept_workspace_bytes": (_sz, [_i, _i, _i, _i]),
     "tree_accept_greedy": (_i, [_i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
     "kv_tree_compact": (_i, [_i, _i, _i, _i, _i, _i, _p, _p, _p, _i, _p, _p, _p]),
+    "conv_tree_verify": (_i, [_i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p]),
+    "conv_tree_commit": (_i, [_i, _i, _i, _i, _i, _p, _p, _i, _p, _p, _p]),
     "tv_validate_tree": (_i, [_p, _p, _i, _i]),
     "tv_validate_path": (_i, [_p, _p, _p, _p, _i, _i, _i]),
     "tv_last_error": (ctypes.c_char_p, []),
@@ -221,6 +225,37 @@ def kv_tree_compact(k_cache, v_cache, k_type: str, v_type: str, n_past, path, pa
     _check(lib().kv_tree_compact(B, Hkv, D, Tcap, KV_TYPES[k_type], KV_TYPES[v_type], _ptr(n_past), _ptr(path),
                                  _ptr(path_len), path.shape[1], _ptr(k_cache), _ptr(v_cache), _stream(k_cache.device)))
     return k_cache, v_cache
+
+
+def conv_tree_verify(x, weight, conv_state, parent, n_nodes, activation: str = "none", y=None):
+    """Tree-aware causal convolution.  x ``[B][N][C]`` (bf16 or fp32), weight fp32 ``[C][K]``,
+    conv_state fp32 ``[B][K-1][C]`` (read only).  Returns y fp32 ``[B][N][C]``."""
+    B, N, C = x.shape
+    K = weight.shape[1]
+    _dev(x, "x", (torch.bfloat16, torch.float32))
+    _dev(weight, "weight", torch.float32, (C, K)); _dev(conv_state, "conv_state", torch.float32, (B, K - 1, C))
+    _dev(parent, "parent", torch.int32, (B, N)); _dev(n_nodes, "n_nodes", torch.int32, (B,))
+    if y is None:
+        y = torch.empty((B, N, C), dtype=torch.float32, device=x.device)
+    _dev(y, "y", torch.float32, (B, N, C))
+    _check(lib().conv_tree_verify(B, N, C, K, _in_dtype(x), ACTIVATIONS[activation], _ptr(parent), _ptr(n_nodes),
+                                  _ptr(x), _ptr(weight), _ptr(conv_state), _ptr(y), _stream(x.device)))
+    return y
+
+
+def conv_tree_commit(conv_state, x, path, path_len):
+    """Move the committed window (fp32 ``[B][K-1][C]``, in place) to the end of each
+    sequence's accepted path."""
+    B, Km1, C = conv_state.shape
+    N = x.shape[1]
+    _dev(conv_state, "conv_state", torch.float32)
+    _dev(x, "x", (torch.bfloat16, torch.float32), (B, N, C))
+    _dev(path, "path", torch.int32); _dev(path_len, "path_len", torch.int32, (B,))
+    if path.dim() != 2 or path.shape[0] != B:
+        raise ValueError(f"path has shape {tuple(path.shape)}, expected ({B}, Lmax)")
+    _check(lib().conv_tree_commit(B, N, C, Km1 + 1, _in_dtype(x), _ptr(path), _ptr(path_len), path.shape[1],
+                                  _ptr(x), _ptr(conv_state), _stream(x.device)))
+    return conv_state
 
 
 def _host_i32(a, name):

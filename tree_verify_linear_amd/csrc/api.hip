@@ -229,4 +229,46 @@ int kv_tree_compact(int B, int Hkv, int D, int Tcap, int k_type, int v_type, con
     return launch_kv_compact(a, static_cast<hipStream_t>(stream));
 }
 
+static int check_conv(const char* fn, int B, int N, int C, int K, int dtype) {
+    if (B <= 0 || N <= 0 || C <= 0 || K <= 0)
+        return set_error(TV_EINVAL, "%s: sizes must be positive (B=%d N=%d C=%d K=%d)", fn, B, N, C, K);
+    if (N > TV_MAX_NODES) return set_error(TV_ERANGE, "%s: N=%d exceeds %d tree nodes", fn, N, TV_MAX_NODES);
+    if (K < 2 || K > 8) return set_error(TV_EUNSUPPORTED, "%s: K=%d not built; supported widths: 2..8", fn, K);
+    if (C % 8) return set_error(TV_EUNSUPPORTED, "%s: C=%d not built; channels must be a multiple of 8", fn, C);
+    if (dtype != TV_F32 && dtype != TV_BF16)
+        return set_error(TV_EUNSUPPORTED, "%s: dtype %d not built; supported: TV_F32, TV_BF16", fn, dtype);
+    if (static_cast<double>(B) * N * C > 9.0e15) return set_error(TV_ERANGE, "%s: tensor sizes overflow", fn);
+    return TV_OK;
+}
+
+int conv_tree_verify(int B, int N, int C, int K, int dtype, int activation, const int32_t* parent,
+                     const int32_t* n_nodes, const void* x, const float* weight, const float* conv_state, float* y,
+                     void* stream) {
+    clear_error();
+    const char* fn = "conv_tree_verify";
+    const int st = check_conv(fn, B, N, C, K, dtype);
+    if (st != TV_OK) return st;
+    if (activation != TV_ACT_NONE && activation != TV_ACT_SILU)
+        return set_error(TV_EINVAL, "%s: activation %d is not TV_ACT_NONE or TV_ACT_SILU", fn, activation);
+    if (!parent || !n_nodes || !x || !weight || !conv_state || !y) return set_error(TV_EINVAL, "%s: null pointer argument", fn);
+    if (!aligned(x, 16) || !aligned(weight, 16) || !aligned(conv_state, 16) || !aligned(y, 16))
+        return set_error(TV_EINVAL, "%s: x, weight, conv_state and y must be 16-byte aligned", fn);
+    ConvVerifyArgs a{B, N, C, K, activation == TV_ACT_SILU, dtype == TV_BF16, parent, n_nodes, x, weight, conv_state, y};
+    return launch_conv_verify(a, static_cast<hipStream_t>(stream));
+}
+
+int conv_tree_commit(int B, int N, int C, int K, int dtype, const int32_t* path, const int32_t* path_len, int Lmax,
+                     const void* x, float* conv_state, void* stream) {
+    clear_error();
+    const char* fn = "conv_tree_commit";
+    const int st = check_conv(fn, B, N, C, K, dtype);
+    if (st != TV_OK) return st;
+    if (Lmax < 1 || Lmax > N) return set_error(TV_ERANGE, "%s: Lmax=%d not in [1, N=%d]", fn, Lmax, N);
+    if (!path || !path_len || !x || !conv_state) return set_error(TV_EINVAL, "%s: null pointer argument", fn);
+    if (!aligned(x, 16) || !aligned(conv_state, 16))
+        return set_error(TV_EINVAL, "%s: x and conv_state must be 16-byte aligned", fn);
+    ConvCommitArgs a{B, N, C, K, Lmax, dtype == TV_BF16, path, path_len, x, conv_state};
+    return launch_conv_commit(a, static_cast<hipStream_t>(stream));
+}
+
 }  // extern "C"

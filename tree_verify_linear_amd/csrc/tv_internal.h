@@ -85,6 +85,28 @@ struct KvCompactArgs {
 };
 int launch_kv_compact(const KvCompactArgs& a, hipStream_t stream);
 
+struct ConvVerifyArgs {
+    int B, N, C, K, silu;
+    bool bf16;
+    const int32_t* parent;
+    const int32_t* n_nodes;
+    const void* x;
+    const float* weight;
+    const float* state;
+    float* y;
+};
+int launch_conv_verify(const ConvVerifyArgs& a, hipStream_t stream);
+
+struct ConvCommitArgs {
+    int B, N, C, K, Lmax;
+    bool bf16;
+    const int32_t* path;
+    const int32_t* path_len;
+    const void* x;
+    float* state;
+};
+int launch_conv_commit(const ConvCommitArgs& a, hipStream_t stream);
+
 // ---------------------------------------------------------------- device helpers
 #if defined(__HIP_DEVICE_COMPILE__) || defined(__HIPCC__)
 // Consecutive workgroup ids are dealt round-robin to the 8 XCDs (each with its own L2).

@@ -13,6 +13,8 @@ Shapes follow the library's layouts (row-major, innermost last):
 * tree: ``parent[B][Nmax]`` int32 (``-1`` for the root and for padding rows beyond
   ``n_nodes[b]``); ``n_nodes[B]`` int32.
 * accepted path: ``path[B][Lmax]`` int32 (``-1`` padding), ``path_len[B]`` int32.
+* tree convolution: inputs ``x[B][N][C]`` (bf16 bits or fp32), weight ``[C][K]`` fp32,
+  committed window ``state[B][K-1][C]`` fp32 (oldest first).
 * acceptance: draft ``tokens[B][N]`` int32 (distinct among siblings; node 0 holds the last
   committed token) and target ``logits[B][N][V]`` (bf16 bits or fp32).
 
@@ -27,6 +29,7 @@ import numpy as np
 
 # Tensor ids used in the seed tuple.
 T_TREE, T_PATH, T_Q, T_K, T_V, T_G, T_BETA, T_STATE, T_AQ, T_KC, T_VC, T_LOGITS, T_DTOK, T_TLOGIT = range(14)
+T_CX, T_CW, T_CSTATE = 14, 15, 16
 
 QK8_0_BYTES = 34   # fp16 scale + 32 int8
 QK4_0_BYTES = 18   # fp16 scale + 16 bytes of packed nibbles
@@ -449,3 +452,45 @@ def workload_accept(B: int = 64, V: int = 151936, dtype: str = "bf16", cfg: int 
     """Greedy acceptance over the batched step's trees (same seeds as ``workload_batched``)."""
     parents, _ = trees_for(cfg, B, "ddtree", seq_ids=seq_ids)
     return gen_accept(cfg, parents, V, dtype, tie_p=tie_p, layer=50, seq_ids=seq_ids)
+
+
+# ----------------------------------------------------------------------------- tree convolution
+
+@dataclass
+class ConvInputs:
+    dtype: str
+    x: np.ndarray           # [B][N][C] bf16 bits (uint16) or float32
+    weight: np.ndarray      # [C][K] float32
+    state: np.ndarray       # [B][K-1][C] float32, oldest first
+    parent: np.ndarray
+    n_nodes: np.ndarray
+    path: np.ndarray
+    path_len: np.ndarray
+    K: int
+    C: int
+
+
+def gen_conv(cfg: int, parents, paths, C: int, K: int, dtype: str = "bf16", layer: int = 0,
+             seq_ids=None) -> ConvInputs:
+    """Inputs ~ N(0, 1) (the layer's q|k|v projections, rounded to bf16), weights ~ N(0, 1/K)
+    (one set per layer, drawn from sequence 0's stream), committed window ~ N(0, 1) fp32."""
+    seq_ids = list(range(len(parents))) if seq_ids is None else list(seq_ids)
+    parent, n_nodes = pad_trees(parents)
+    path, path_len = pad_paths(paths, lmax=parent.shape[1])
+    B, N = parent.shape
+    x = np.zeros((B, N, C), dtype=np.uint16 if dtype == "bf16" else np.float32)
+    state = np.zeros((B, K - 1, C), dtype=np.float32)
+    for b, sid in enumerate(seq_ids):
+        xb = rng_for(cfg, sid, layer, T_CX).standard_normal((N, C), dtype=np.float32)
+        x[b] = f32_to_bf16_bits(xb) if dtype == "bf16" else xb
+        state[b] = rng_for(cfg, sid, layer, T_CSTATE).standard_normal((K - 1, C), dtype=np.float32)
+    w = (rng_for(cfg, 0, layer, T_CW).standard_normal((C, K), dtype=np.float32) / np.float32(np.sqrt(K)))
+    return ConvInputs(dtype, x, w.astype(np.float32), state, parent, n_nodes, path, path_len, K, C)
+
+
+def workload_conv(B: int = 64, cfg: int = 3, C: int = 2 * 16 * 128 + 48 * 128, K: int = 4, dtype: str = "bf16",
+                  seq_ids=None) -> ConvInputs:
+    """The batched step's trees and accepted paths, at the linear layer's q|k|v width
+    (2 x 16 key heads x 128 + 48 value heads x 128 = 10240 channels), window width 4."""
+    parents, paths = trees_for(cfg, B, "ddtree", seq_ids=seq_ids)
+    return gen_conv(cfg, parents, paths, C, K, dtype, layer=60, seq_ids=seq_ids)
