@@ -19,11 +19,12 @@ timed region.
 Output: one JSON line.  ``roofline`` is for the kernel with the largest mean duration;
 its ``traffic`` is read from the committed hardware-counter summary under ``profiles/``
 when that summary was taken on the current kernel source (else null).  ``next_kernels``
-times, after the step and outside ``value``, the greedy acceptance of the step's trees
-(vocabulary 151936, bf16 logits) and the compaction of the attention cache to the
-accepted paths.  ``cpu_baseline``
-times the fp64 CPU oracle over whole sequences of the same workload for about ten
-seconds.
+times, after the step and outside ``value``, the tree convolution and its window commit,
+the greedy acceptance of the step's trees (vocabulary 151936, bf16 logits) and the
+compaction of the attention cache to the accepted paths.  ``workload2`` times the step's
+three calls on the second workload (budgets 8, 16 and 40 with a Q8_0 K cache and a Q4_0
+V cache).  ``cpu_baseline`` times the fp64 CPU oracle over whole sequences of the same
+workload for about ten seconds.
 
 Warm-up runs at least --warmup steps and keeps going until --min-warmup-s (0.3 s) have
 passed: the clock ramps up over the first ~40 ms of sustained work, and timings taken
@@ -68,6 +69,8 @@ def parse():
                          "GPU clock ramps up over the first ~40 ms of sustained work)")
     ap.add_argument("--batch", type=int, default=64)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle timing")
+    ap.add_argument("--no-workload2", action="store_true",
+                    help="skip the second workload (budgets 8/16/40, Q8_0 K + Q4_0 V)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU oracle sample budget")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one device-to-device copy of this many MiB (counter calibration)")
@@ -409,6 +412,69 @@ def time_next_rows(args, tvl, torch, dev, d, A, B):
     }
 
 
+def time_workload2(args, tvl, torch, dev, B):
+    """The second workload: budgets 8 (a chain), 16 and 40, with a Q8_0 K cache and a Q4_0 V
+    cache, through the same three calls as the step.  One input set per variant (each is
+    larger than the 256 MB last-level cache); not part of ``value``."""
+    from workloads import workload_batched
+    res = {}
+    for budget in (8, 16, 40):
+        W = workload_batched(B, budget=budget, k_type="q8_0", v_type="q4_0")
+        L, A = W.lin[0], W.attn[0]
+        d = to_device(L, A, dev)
+        N, Hkv, Tcap = A.q.shape[1], A.k_cache.shape[1], A.k_cache.shape[2]
+        ws = torch.empty(max(tvl.attn_tree_workspace_bytes(B, N, A.Hq, Hkv, A.D, Tcap, A.window), 256),
+                         dtype=torch.uint8, device=dev)
+        st0 = d["state"].clone()
+
+        def step(ev=None):
+            if ev:
+                ev[0].record()
+            tvl.lin_tree_verify(d["q"], d["k"], d["v"], d["g"], d["beta"], d["state"], d["parent"],
+                                d["n_nodes"], L.scale, out=d["out"], cap_delta=d["cap"])
+            if ev:
+                ev[1].record()
+            tvl.attn_tree_verify(d["aq"], d["kc"], d["vc"], A.k_type, A.v_type, d["n_past"], d["aparent"],
+                                 d["an_nodes"], A.window, A.scale, out=d["aout"], lse=d["lse"], workspace=ws)
+            if ev:
+                ev[2].record()
+            tvl.lin_tree_commit(d["state"], d["path"], d["path_len"], d["k"], d["g"], d["cap"])
+            if ev:
+                ev[3].record()
+
+        w0 = time.perf_counter()
+        while time.perf_counter() - w0 < 0.1:
+            step()
+            torch.cuda.synchronize()
+        K = max(args.steps, 10)
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+        for i in range(K):
+            step(evs[i])
+        torch.cuda.synchronize()
+        d["state"].copy_(st0)
+        names = ["lin_tree_verify", "attn_tree_verify", "lin_tree_commit"]
+        byts = {"lin_tree_verify": lin_verify_bytes(L), "attn_tree_verify": attn_bytes(A),
+                "lin_tree_commit": lin_commit_bytes(L)}
+        ks = {}
+        for j, nme in enumerate(names):
+            ms = sum(e[j].elapsed_time(e[j + 1]) for e in evs) / K
+            gbs = byts[nme] / (ms * 1e-3) / 1e9
+            ks[nme] = {"mean_us": round(ms * 1e3, 2), "algorithmic_MB": round(byts[nme] / 1e6, 2),
+                       "GB_per_s": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+        ms_step = evs[0][0].elapsed_time(evs[-1][3]) / K
+        nodes = int(L.n_nodes.sum())
+        res[f"budget{budget}"] = {"workload": f"{B} sequences x {budget}-node DDTree"
+                                              f"{' (a chain)' if budget == 8 else ''}, linear Hk16/Hv48 "
+                                              f"dk=dv=128 + commit, attention Hq24/Hkv4 D256 Q8_0 K / Q4_0 V "
+                                              f"T=4096 window 2048",
+                                  "ms_per_step": round(ms_step, 4),
+                                  "node_layers_per_s": round(2 * nodes / (ms_step * 1e-3), 1),
+                                  "kernels": ks}
+        del d, ws
+        print(f"# timed second workload, budget {budget}", file=sys.stderr, flush=True)
+    return res
+
+
 # ----------------------------------------------------------------------------- main
 
 def main():
@@ -519,6 +585,7 @@ def main():
                 "algorithmic_bytes_per_launch": int(byts[dom])}
 
     next_kernels = time_next_rows(args, tvl, torch, dev, pool[0], A0, B)
+    workload2 = None if args.no_workload2 else time_workload2(args, tvl, torch, dev, B)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -543,6 +610,7 @@ def main():
                    "global_batch": B, "tree_nodes": 22, "kv_type": "q8_0", "window": 2048, "n_past": 4096},
         "kernels": kernels,
         "next_kernels": next_kernels,
+        "workload2": workload2,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

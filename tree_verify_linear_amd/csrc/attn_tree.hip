@@ -21,12 +21,13 @@
 //     operand, Q in registers as the B operand, fp32 accumulate).  The partial scores of a row
 //     tile meet in LDS at the scoring wave that owns the tile's softmax.  The owner
 //     masks, runs an online softmax in the exp2 domain (the reference max moves only when a
-//     row max grows by more than 2^8; O is then rescaled) and writes P -- rounded once to
-//     fp16, the only rounding of the whole contraction -- to LDS in the PV A-operand layout
-//     (the score layout of S^T already is that layout, so no transpose).
+//     row max grows by more than 2^8; O is then rescaled) and writes P as an fp16 pair hi +
+//     lo (P to about 2^-22) to LDS in the PV A-operand layout (the score layout of S^T
+//     already is that layout, so no transpose).
 //   * PV waves (4): PV wave w owns output columns 64w .. 64w+63 of all rows.  It dequantises
 //     its columns of V into fp16 hi/lo (slot-major, the PV B operand) and accumulates
-//     O += P V_hi + P V_lo, one tile behind the scores.
+//     O += P_hi V_hi + P_hi V_lo + P_lo V_hi (the dropped P_lo V_lo is ~2^-22 relative), one
+//     tile behind the scores.
 //   * Each SIMD carries one wave of each role, and the phases pair them up: while the scoring
 //     wave issues the QK^T matrix instructions the PV wave dequantises V, and while the
 //     scoring wave runs the softmax the PV wave issues the PV matrix instructions.
@@ -152,10 +153,11 @@ struct AttnSmem {
     __align__(16) uint8_t rawk[TS * MAXROW + 16];           // K rows of the tile being scored
     __align__(16) uint8_t rawv[2][TS * MAXROW + 16];        // V rows, two tiles in flight
     __align__(16) f32x4 spart[RTMAX][3][2][64];             // partial scores from non-owners
-    __align__(16) f32x4 sdump[4][2][64];                    // the owner's copy (not read)
-    __align__(16) f16x8 pbuf[2][RTMAX][64];                 // P in the PV operand layout
+    __align__(16) f32x4 sdump[2][64];                       // wave 0's copy of row tile 8 (not read)
+    __align__(16) f16x8 pbuf[2][RTMAX][64];                 // P hi in the PV operand layout
+    __align__(16) f16x8 pbuf_lo[2][RTMAX][64];              // P lo = P - P hi, same layout
     __align__(16) _Float16 vdq[4][2][64][VST];              // [PV wave][hi, lo][column][slot]
-    __align__(16) float alpha[2][RTMAX][64];                // O rescale factor, row = index % 16
+    __align__(16) float alpha[2][RTMAX][16];                // O rescale factor per row
     int grow[2][RTMAX];                                     // row tile needs a rescale
     float mfin[ROWS_PER_BLOCK], lfin[ROWS_PER_BLOCK];
     uint64_t anc[TV_MAX_NODES];
@@ -276,9 +278,20 @@ __global__ __launch_bounds__(THREADS, 1) void attn_kernel(AttnLaunch L) {
     if (scorer) {
         // ------------------------------------------------------------ scoring waves
         // Q of all row tiles, this wave's two blocks, as the QK B operand
+        // Row tiles in this wave's own order: its softmax tiles wl and wl + 4 first, then tile 8
+        // (wave 0's third softmax tile), then the other six.  With the order fixed per wave,
+        // the partial scores the wave keeps sit at compile-time register positions.
+        auto rtile = [&](int i) -> int {
+            if (i == 0) return wl;
+            if (i == 1) return wl + 4;
+            if (i == 2) return 8;
+            const int x = (i - 3) % 3, half = (i - 3) / 3;
+            return 4 * half + (x < wl ? x : x + 1);
+        };
         f16x8 qop[RTMAX][2];
 #pragma unroll
-        for (int r = 0; r < RTMAX; ++r) {
+        for (int i = 0; i < RTMAX; ++i) {
+            const int r = rtile(i);
             const int row = rowbase + r * 16 + l16;
             const int node = row / L.G, hh = row - node * L.G;
             const bool ok = r < RT && row < L.rows && node < n;
@@ -291,8 +304,8 @@ __global__ __launch_bounds__(THREADS, 1) void attn_kernel(AttnLaunch L) {
                 const uint32_t u[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    qop[r][kb][2 * e] = static_cast<_Float16>(__uint_as_float(u[e] << 16));
-                    qop[r][kb][2 * e + 1] = static_cast<_Float16>(__uint_as_float(u[e] & 0xffff0000u));
+                    qop[i][kb][2 * e] = static_cast<_Float16>(__uint_as_float(u[e] << 16));
+                    qop[i][kb][2 * e + 1] = static_cast<_Float16>(__uint_as_float(u[e] & 0xffff0000u));
                 }
             }
         }
@@ -339,20 +352,25 @@ __global__ __launch_bounds__(THREADS, 1) void attn_kernel(AttnLaunch L) {
                         split_exact(block_ints8<KT, true>(krow, 2 * wl + 1, g4), d1, ah[1], al[1]);
                     }
 #pragma unroll
-                    for (int r = 0; r < RTMAX; ++r) {
+                    for (int i = 0; i < RTMAX; ++i) {
+                        const int r = rtile(i);
                         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                         for (int kb = 0; kb < 2; ++kb) {
-                            acc = mfma_f16(ah[kb], qop[r][kb], acc);
-                            acc = mfma_f16(al[kb], qop[r][kb], acc);
+                            acc = mfma_f16(ah[kb], qop[i][kb], acc);
+                            acc = mfma_f16(al[kb], qop[i][kb], acc);
                         }
-                        // the owner keeps its partial; its store goes to a dump slot, so the
-                        // row-tile loop stays free of branches
-                        const int owner = r & 3;
-                        if (wl == owner) own[r >> 2][st] = acc;
-                        f32x4* dst = wl == owner ? &sm.sdump[wl][st][lane]
-                                                 : &sm.spart[r][(wl - owner - 1) & 3][st][lane];
-                        *dst = acc;
+                        if (i < 2) {
+                            own[i][st] = acc;
+                        } else if (i == 2) {
+                            // row tile 8: wave 0 keeps it; the other waves' copies are what it
+                            // reads (wave 0's store goes to a dump slot, so there is no branch)
+                            own[2][st] = acc;
+                            f32x4* dst = wl == 0 ? &sm.sdump[st][lane] : &sm.spart[8][(wl - 1) & 3][st][lane];
+                            *dst = acc;
+                        } else {
+                            sm.spart[r][(wl - (r & 3) - 1) & 3][st][lane] = acc;
+                        }
                     }
                 }
             }
@@ -413,17 +431,21 @@ __global__ __launch_bounds__(THREADS, 1) void attn_kernel(AttnLaunch L) {
                     const float al = rs[j].m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(rs[j].m - mnew);
                     rs[j].m = mnew;
                     const float m = mnew == -INFINITY ? 0.f : mnew;      // then every x is -inf
-                    f16x8 p;
+                    // P = hi + lo in fp16 (lo is the rounding residual of hi), so P enters
+                    // the PV products to about 2^-22 relative
+                    f16x8 p, plo;
                     float ps = 0.f;
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
                         const float pe = __builtin_amdgcn_exp2f(x[e] - m);
                         ps += pe;
                         p[e] = static_cast<_Float16>(pe);
+                        plo[e] = static_cast<_Float16>(pe - static_cast<float>(p[e]));
                     }
                     rs[j].l = rs[j].l * al + ps;
                     sm.pbuf[bufk][r][lane] = p;
-                    sm.alpha[bufk][r][lane] = al;                      // row l16's factor
+                    sm.pbuf_lo[bufk][r][lane] = plo;
+                    if (g4 == 0) sm.alpha[bufk][r][l16] = al;          // row l16's factor
                     if (lane == 0) sm.grow[bufk][r] = anyg;
                 };
                 softmax(0);
@@ -523,28 +545,29 @@ __global__ __launch_bounds__(THREADS, 1) void attn_kernel(AttnLaunch L) {
                         for (int jj = 0; jj < 4; ++jj) oacc[r][jj] *= al;
                     }
                 }
+                // V operands of this wave's four column tiles, then P hi/lo one row tile at a
+                // time (keeps the live registers to the accumulators plus one P pair)
+                f16x8 bh[4], bl[4];
 #pragma unroll
-                for (int half = 0; half < 2; ++half) {
-                    f16x8 bh[2], bl[2];
+                for (int jj = 0; jj < 4; ++jj) {
+                    const int col = 16 * jj + l16;
+                    const f16x4 h0 = *reinterpret_cast<const f16x4*>(&sm.vdq[wl][0][col][4 * g4]);
+                    const f16x4 h1 = *reinterpret_cast<const f16x4*>(&sm.vdq[wl][0][col][16 + 4 * g4]);
+                    const f16x4 l0 = *reinterpret_cast<const f16x4*>(&sm.vdq[wl][1][col][4 * g4]);
+                    const f16x4 l1 = *reinterpret_cast<const f16x4*>(&sm.vdq[wl][1][col][16 + 4 * g4]);
+                    bh[jj] = f16x8{h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
+                    bl[jj] = f16x8{l0[0], l0[1], l0[2], l0[3], l1[0], l1[1], l1[2], l1[3]};
+                }
 #pragma unroll
-                    for (int jj = 0; jj < 2; ++jj) {
-                        const int col = 16 * (2 * half + jj) + l16;
-                        const f16x4 h0 = *reinterpret_cast<const f16x4*>(&sm.vdq[wl][0][col][4 * g4]);
-                        const f16x4 h1 = *reinterpret_cast<const f16x4*>(&sm.vdq[wl][0][col][16 + 4 * g4]);
-                        const f16x4 l0 = *reinterpret_cast<const f16x4*>(&sm.vdq[wl][1][col][4 * g4]);
-                        const f16x4 l1 = *reinterpret_cast<const f16x4*>(&sm.vdq[wl][1][col][16 + 4 * g4]);
-                        bh[jj] = f16x8{h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
-                        bl[jj] = f16x8{l0[0], l0[1], l0[2], l0[3], l1[0], l1[1], l1[2], l1[3]};
-                    }
+                for (int r = 0; r < RTMAX; ++r) {
+                    const f16x8 pa = sm.pbuf[bufp][r][lane];
+                    const f16x8 pl = sm.pbuf_lo[bufp][r][lane];
 #pragma unroll
-                    for (int r = 0; r < RTMAX; ++r) {
-                        const f16x8 pa = sm.pbuf[bufp][r][lane];
+                    for (int jj = 0; jj < 4; ++jj) oacc[r][jj] = mfma_f16(pa, bh[jj], oacc[r][jj]);
 #pragma unroll
-                        for (int jj = 0; jj < 2; ++jj) {
-                            oacc[r][2 * half + jj] = mfma_f16(pa, bh[jj], oacc[r][2 * half + jj]);
-                            oacc[r][2 * half + jj] = mfma_f16(pa, bl[jj], oacc[r][2 * half + jj]);
-                        }
-                    }
+                    for (int jj = 0; jj < 4; ++jj) oacc[r][jj] = mfma_f16(pa, bl[jj], oacc[r][jj]);
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) oacc[r][jj] = mfma_f16(pl, bh[jj], oacc[r][jj]);
                 }
             }
             __syncthreads();

@@ -369,13 +369,18 @@ def workload_attention_27b(B: int = 1, cfg: int = 2, T: int = 4096, window: int 
                     order=[("attn", 0)])
 
 
-def workload_batched(B: int = 64, cfg: int = 3, seq_ids=None) -> Workload:
+def workload_batched(B: int = 64, cfg: int = 3, seq_ids=None, budget: int = 22, k_type: str = "q8_0",
+                     v_type: str = "q8_0") -> Workload:
     """64 sequences, each with its own 22-node tree and accepted path, through one linear
-    layer (27B widths) and one attention layer (T=4096 Q8_0, window 2048)."""
-    parents, paths = trees_for(cfg, B, "ddtree", seq_ids)
+    layer (27B widths) and one attention layer (T=4096 Q8_0, window 2048).  ``budget`` and
+    the K/V types select the second workload's variants (budgets 8, 16, 40; asymmetric K/V)."""
+    kw = {} if budget == 22 else {"budget": budget}
+    parents, paths = trees_for(cfg, B, "ddtree", seq_ids, **kw)
     lin = gen_lin(cfg, parents, paths, 16, 48, 128, 128, "bf16", seq_ids=seq_ids)
-    attn = gen_attn(cfg, parents, 24, 4, 256, 4096, "q8_0", "q8_0", 2048, seq_ids=seq_ids)
-    return Workload(f"batched-b{B}", lin=[lin], attn=[attn], order=[("lin", 0), ("attn", 0)])
+    attn = gen_attn(cfg, parents, 24, 4, 256, 4096, k_type, v_type, 2048, seq_ids=seq_ids)
+    name = f"batched-b{B}" if (budget, k_type, v_type) == (22, "q8_0", "q8_0") else \
+        f"batched-b{B}-budget{budget}-{k_type}-{v_type}"
+    return Workload(name, lin=[lin], attn=[attn], order=[("lin", 0), ("attn", 0)])
 
 
 def workload_long_context(window: int = 0, T: int = 131072, n_lin: int = 16, n_attn: int = 4,
