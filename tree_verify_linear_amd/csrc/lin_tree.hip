@@ -404,130 +404,20 @@ __global__ __launch_bounds__(64, 2) void lin_verify_kernel(LinVerifyArgs a) {
     store_unit(sm, a, u, n, ctiles, CW, lane);
 }
 
-// Verify for trees of 33..64 nodes: the same math, one unit per wave, with the walk driven
-// by per-node ancestor lists and the deltas kept in LDS.
+// Verify for trees of 33..64 nodes: the same unit, with up to 512 registers per lane (one
+// wave per SIMD per workgroup slot) for the wider operand set and the longer register walk.
 template <int DK, int NT, bool BF16IN>
-__global__ __launch_bounds__(64) void lin_verify_big_kernel(LinVerifyArgs a) {
-    constexpr int KS = (DK + 31) / 32;
-    constexpr int NMAX = NT * 8;
-    constexpr int GT = (NMAX + 15) / 16;
-    constexpr int CST = 68;
-    constexpr int GST = NT * 16 + 4;
-
-    __shared__ __align__(16) float Cs[NT * 16][CST];
-    __shared__ float Gm[GT * 16][GST];
-    __shared__ float Dl[NMAX][64];
-    __shared__ float Vl[NMAX][64];
-    __shared__ float gl[NMAX], bl[NMAX];
-    __shared__ int par[NMAX], dep[NMAX];
-    __shared__ int anc[NMAX][NMAX];               // anc[i][t]: t-th strict ancestor (nearest first)
-
+__global__ __launch_bounds__(64, 1) void lin_verify_wide_kernel(LinVerifyArgs a) {
+    static_assert(NT > 4 && NT <= 8, "wide register walk is for trees of 33..64 nodes");
+    __shared__ VerifySmem<NT, BF16IN> sm;
     const int lane = threadIdx.x;
-    const int g4 = lane >> 4, l16 = lane & 15;
     const int CW = a.dv < 64 ? a.dv : 64;
-    const int MT = CW >> 4;
     const int ctiles = a.dv / CW;
-    const UnitIds id = unit_ids(a, xcd_remap(blockIdx.x, gridDim.x), ctiles, CW);
-    const int b = id.b, h = id.h, kh = id.kh, j0 = id.j0;
-    const int n = clampi(a.n_nodes[b], 0, a.N < NMAX ? a.N : NMAX);
-    if (n <= 0) return;
-
-    float4 sa[4][KS][2];
-    load_state_tile<DK>(sa, a.state + (static_cast<size_t>(b) * a.Hv + h) * a.dv * DK + static_cast<size_t>(j0) * DK,
-                        MT, l16, g4);
-    bf16x8 bh[NT][KS], bo[NT][KS];
-    {
-        const size_t esz = BF16IN ? 2 : 4;
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-            const int c = nt * 16 + l16;
-            const bool isk = c < n;
-            const bool valid = c < 2 * n;
-            const int node = valid ? (isk ? c : c - n) : 0;
-            const size_t rowoff = ((static_cast<size_t>(b) * a.N + node) * a.Hk + kh) * DK;
-            const void* row = static_cast<const char*>(isk ? a.k : a.q) + rowoff * esz;
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) load_row_operand<DK, BF16IN>(row, ks, g4, valid, bh[nt][ks], bo[nt][ks]);
-        }
-    }
-    if (lane < n) {
-        par[lane] = lane == 0 ? -1 : clampi(a.parent[static_cast<size_t>(b) * a.N + lane], 0, lane - 1);
-        const size_t gi = (static_cast<size_t>(b) * a.N + lane) * a.Hv + h;
-        gl[lane] = load_scalar<BF16IN>(a.g, gi);
-        bl[lane] = load_scalar<BF16IN>(a.beta, gi);
-    }
-    for (int i = 0; i < n; ++i) {
-        const size_t vi = ((static_cast<size_t>(b) * a.N + i) * a.Hv + h) * a.dv + j0 + lane;
-        Vl[i][lane] = lane < CW ? load_scalar<BF16IN>(a.v, vi) : 0.f;
-    }
-#pragma unroll
-    for (int gt = 0; gt < GT; ++gt) {
-        if (gt * 16 >= n) continue;
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                acc = mfma16x16x32(bh[gt][ks], bh[nt][ks], acc);
-                if constexpr (!BF16IN) {
-                    acc = mfma16x16x32(bh[gt][ks], bo[nt][ks], acc);
-                    acc = mfma16x16x32(bo[gt][ks], bh[nt][ks], acc);
-                }
-            }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) Gm[gt * 16 + 4 * g4 + e][nt * 16 + l16] = acc[e];
-        }
-    }
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-        if (mt >= MT) continue;
-        bf16x8 ah[KS], al[KS];
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) split_bf16(sa[mt][ks][0], sa[mt][ks][1], ah[ks], al[ks]);
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                acc = mfma16x16x32(ah[ks], bh[nt][ks], acc);
-                acc = mfma16x16x32(al[ks], bh[nt][ks], acc);
-                if constexpr (!BF16IN) acc = mfma16x16x32(ah[ks], bo[nt][ks], acc);
-            }
-            *reinterpret_cast<float4*>(&Cs[nt * 16 + l16][mt * 16 + 4 * g4]) = make_float4(acc[0], acc[1], acc[2], acc[3]);
-        }
-    }
-    __syncthreads();
-    if (lane < n) {
-        int t = 0;
-        for (int m = par[lane]; m >= 0; m = par[m]) anc[lane][t++] = m;
-        dep[lane] = t;
-    }
-    __syncthreads();
-
-    const int j = lane;
-    for (int i = 0; i < n; ++i) {
-        float u = 0.f, w = 0.f, gam = 1.f;
-        const int d = dep[i];
-#pragma unroll 4
-        for (int t = 0; t < d; ++t) {
-            const int m = anc[i][t];
-            const float dm = Dl[m][j];
-            u = fmaf(gam * Gm[m][i], dm, u);
-            w = fmaf(gam * Gm[m][n + i], dm, w);
-            gam *= gl[m];
-        }
-        u = fmaf(gam, Cs[i][j], u);                 // gam = G_parent
-        w = fmaf(gam, Cs[n + i][j], w);
-        const float gi = gl[i], bi = bl[i];
-        const float dl = bi * (Vl[i][j] - gi * u);
-        Dl[i][j] = dl;
-        const float o = a.scale * fmaf(gi, w, Gm[i][n + i] * dl);
-        if (j < CW) {
-            const size_t off = ((static_cast<size_t>(b) * a.N + i) * a.Hv + h) * a.dv + j0 + j;
-            a.out[off] = o;
-            a.cap_delta[off] = dl;
-        }
-    }
+    const int u = xcd_remap(blockIdx.x, gridDim.x);
+    UnitIn<DK, NT, BF16IN> in;
+    load_unit(in, a, u, ctiles, CW, lane);
+    const int n = compute_unit(in, sm, a, u, ctiles, CW, lane);
+    store_unit(sm, a, u, n, ctiles, CW, lane);
 }
 
 template <bool BF16IN>
@@ -634,8 +524,8 @@ int launch_verify_dk_nt(const LinVerifyArgs& a, bool bf16, hipStream_t stream) {
         else hipLaunchKernelGGL((lin_verify_kernel<DK, NT, false>), grid, block, 0, stream, a);
     } else {
         dim3 grid(static_cast<unsigned>(units));
-        if (bf16) hipLaunchKernelGGL((lin_verify_big_kernel<DK, NT, true>), grid, block, 0, stream, a);
-        else hipLaunchKernelGGL((lin_verify_big_kernel<DK, NT, false>), grid, block, 0, stream, a);
+        if (bf16) hipLaunchKernelGGL((lin_verify_wide_kernel<DK, NT, true>), grid, block, 0, stream, a);
+        else hipLaunchKernelGGL((lin_verify_wide_kernel<DK, NT, false>), grid, block, 0, stream, a);
     }
     return launch_status("lin_tree_verify");
 }
@@ -647,6 +537,7 @@ int launch_verify_dk(const LinVerifyArgs& a, bool bf16, hipStream_t stream) {
     if (cols <= 32) return launch_verify_dk_nt<DK, 2>(a, bf16, stream);
     if (cols <= 48) return launch_verify_dk_nt<DK, 3>(a, bf16, stream);
     if (cols <= 64) return launch_verify_dk_nt<DK, 4>(a, bf16, stream);
+    if (cols <= 80) return launch_verify_dk_nt<DK, 5>(a, bf16, stream);
     return launch_verify_dk_nt<DK, 8>(a, bf16, stream);
 }
 
