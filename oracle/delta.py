@@ -132,3 +132,23 @@ def lin_chain_recurrence(q, k, v, g, beta, S0, scale: float):
         S = g[t] * S + np.outer(k[t], d)
         outs.append(scale * (S.T @ q[t]))
     return np.array(outs), S
+
+
+def lin_tree_verify_commit(state, prev, q, k, v, g, beta, parent, n_nodes, scale: float, dtype: str = "f32",
+                           head_group: str = "contiguous"):
+    """One verify step that first commits the previous step's accepted path.
+
+    PR #606 "SpecLA factor-capture speculative decoding" (the factors captured during verify
+    are flushed into the raw state on commit; the pending-bank variant applies them while
+    the next verify loads the state).  Reading taken: the previous step's commit is the
+    plain commit of its accepted path (``lin_commit_replay``), the state is stored as fp32,
+    and this step's verify starts from that stored committed state.
+
+    ``prev`` = (path, path_len, k, v, g, beta, parent, n_nodes) of the previous step.
+    Returns ``(committed_state, out, delta)``: the committed state rounded to fp32 as the
+    stored state (float64 array of fp32 values) and this step's outputs and deltas."""
+    path, path_len, pk, pv, pg, pbeta, pparent, pn = prev
+    committed = lin_commit_replay(state, path, path_len, pk, pv, pg, pbeta, pparent, pn, dtype, head_group)
+    stored = committed.astype(np.float32)
+    out, delta = lin_tree_verify(q, k, v, g, beta, stored, parent, n_nodes, scale, dtype, head_group)
+    return stored.astype(np.float64), out, delta

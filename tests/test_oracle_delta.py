@@ -10,6 +10,7 @@ import os
 import numpy as np
 import pytest
 
+import oracle
 from oracle import lin_tree_verify, lin_commit_replay, lin_chain_recurrence, root_path
 from oracle.delta import bf16_bits_to_f64
 from workloads import (tree_small, tree_ddtree, tree_chain, random_root_leaf_path, rng_for,
@@ -258,3 +259,35 @@ def test_empty_path_commits_nothing():
     path = np.array([[0, 1]], np.int32)
     new = lin_commit_replay(state, path, np.array([0], np.int32), k, v, g, b, parent, n)
     assert np.array_equal(new, state.astype(np.float64))
+
+
+def test_verify_commit_is_commit_then_verify_and_matches_a_chain_replay():
+    """lin_tree_verify_commit: the previous step's path committed, then this step's tree
+    verified from the stored (fp32) committed state.  Pinned against (i) an empty previous
+    path (plain verify), and (ii) two chain steps, whose accepted prefix followed by the
+    new chain is one sequential recurrence over all the tokens."""
+    from workloads import gen_lin, tree_chain
+    rng = np.random.default_rng(11)
+    Hk, Hv, dk, dv = 1, 2, 16, 16
+    p1, p2 = tree_chain(6), tree_chain(5)
+    L1 = gen_lin(70, [p1], [np.arange(4, dtype=np.int32)], Hk, Hv, dk, dv, "f32")
+    L2 = gen_lin(71, [p2], [np.arange(5, dtype=np.int32)], Hk, Hv, dk, dv, "f32")
+    prev = (L1.path, L1.path_len, L1.k, L1.v, L1.g, L1.beta, L1.parent, L1.n_nodes)
+    st, out, delta = oracle.lin_tree_verify_commit(L1.state, prev, L2.q, L2.k, L2.v, L2.g, L2.beta, L2.parent,
+                                                   L2.n_nodes, L2.scale, "f32")
+    # (ii) one chain: the 4 accepted tokens of step 1, then the 5 tokens of step 2
+    for h in range(Hv):
+        q = np.concatenate([L1.q[0, :4, 0], L2.q[0, :, 0]]).astype(np.float64)
+        k = np.concatenate([L1.k[0, :4, 0], L2.k[0, :, 0]]).astype(np.float64)
+        v = np.concatenate([L1.v[0, :4, h], L2.v[0, :, h]]).astype(np.float64)
+        g = np.concatenate([L1.g[0, :4, h], L2.g[0, :, h]]).astype(np.float64)
+        bt = np.concatenate([L1.beta[0, :4, h], L2.beta[0, :, h]]).astype(np.float64)
+        o_ref, S_end = oracle.lin_chain_recurrence(q, k, v, g, bt, L1.state[0, h].T.astype(np.float64), L2.scale)
+        np.testing.assert_allclose(out[0, :, h], o_ref[4:], rtol=1e-6, atol=1e-6)   # fp32 stored state
+    # (i) nothing accepted in the previous step: the state is unchanged and the verify is plain
+    prev0 = (L1.path, np.zeros(1, np.int32), L1.k, L1.v, L1.g, L1.beta, L1.parent, L1.n_nodes)
+    st0, out0, _ = oracle.lin_tree_verify_commit(L1.state, prev0, L2.q, L2.k, L2.v, L2.g, L2.beta, L2.parent,
+                                                 L2.n_nodes, L2.scale, "f32")
+    ref0, _ = oracle.lin_tree_verify(L2.q, L2.k, L2.v, L2.g, L2.beta, L1.state, L2.parent, L2.n_nodes, L2.scale, "f32")
+    assert np.array_equal(st0, L1.state.astype(np.float64))
+    np.testing.assert_allclose(out0, ref0, rtol=1e-15, atol=1e-15)
