@@ -2,9 +2,11 @@
 """Tree-verify step benchmark on one GPU.
 
 One step takes every node of a batch of 64 draft trees (22 nodes each) through one
-gated delta-rule layer -- ``lin_tree_verify`` then ``lin_tree_commit`` of each
-sequence's accepted path -- and one tree-masked attention layer (``attn_tree_verify``,
-Q8_0 cache of 4096 committed slots, window 2048).  Widths: linear 16 key / 48 value heads
+gated delta-rule layer -- ``lin_tree_verify_commit``: the commit of the path the same
+sequences accepted in their previous step, then the verify of this step's tree, in one
+pass over the state -- and one tree-masked attention layer (``attn_tree_verify``, Q8_0
+cache of 4096 committed slots, window 2048).  ``linear_unfused`` times the separate
+``lin_tree_verify`` and ``lin_tree_commit`` calls on the same inputs.  Widths: linear 16 key / 48 value heads
 of 128, fp32 state; attention 24 query / 4 KV heads of 256.
 
 value = node-layers per second = 2 * (tree nodes in the batch) / step time, i.e. the
@@ -51,6 +53,7 @@ COUNTER_FILE = os.path.join(ROOT, "profiles", "hbm_counters_batched64.txt")
 KERNEL_SOURCES = {
     "lin_tree_verify": "tree_verify_linear_amd/csrc/lin_tree.hip",
     "lin_tree_commit": "tree_verify_linear_amd/csrc/lin_tree.hip",
+    "lin_tree_verify_commit": "tree_verify_linear_amd/csrc/lin_tree.hip",
     "attn_tree_verify": "tree_verify_linear_amd/csrc/attn_tree.hip",
     "tree_accept_greedy": "tree_verify_linear_amd/csrc/accept.hip",
     "kv_tree_compact": "tree_verify_linear_amd/csrc/accept.hip",
@@ -88,6 +91,16 @@ def lin_verify_bytes(L) -> int:
     nodes = int(L.n_nodes.sum())
     per_node = 2 * Hk * dk * eb + Hv * dv * eb + 2 * Hv * eb + 2 * Hv * dv * 4
     return B * Hv * dv * dk * 4 + nodes * per_node + L.parent.nbytes + L.n_nodes.nbytes
+
+
+def lin_verify_commit_bytes(L) -> int:
+    """The fused call: the verify's bytes, the committed state written once, and the previous
+    step's accepted k rows, captured deltas and decays (the same sequences' previous step)."""
+    B, Hv, dv, dk = L.state.shape
+    Hk = L.k.shape[2]
+    eb = 2 if L.dtype == "bf16" else 4
+    acc = int(L.path_len.sum())
+    return lin_verify_bytes(L) + B * Hv * dv * dk * 4 + acc * (Hk * dk * eb + Hv * dv * 4 + Hv * eb) + L.path.nbytes
 
 
 def lin_commit_bytes(L) -> int:
@@ -215,6 +228,7 @@ def to_device(L, A, dev):
     B, N, Hv, dv = L.v.shape
     d["out"] = torch.empty((B, N, Hv, dv), dtype=torch.float32, device=dev)
     d["cap"] = torch.empty_like(d["out"])
+    d["caps"] = [d["cap"], torch.empty_like(d["out"])]      # this step's and the previous step's deltas
     Bq, Nq, Hq, D = A.q.shape
     d["aout"] = torch.empty((Bq, Nq, Hq, D), dtype=torch.float32, device=dev)
     d["lse"] = torch.empty((Bq, Nq, Hq), dtype=torch.float32, device=dev)
@@ -412,6 +426,30 @@ def time_next_rows(args, tvl, torch, dev, d, A, B):
     }
 
 
+def time_unfused_linear(args, tvl, torch, pool, sets):
+    """The linear layer's separate calls (verify, then commit of the same step's path) on the
+    step's inputs, for comparison with the fused call."""
+    K = max(args.steps, 10)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    for i in range(K):
+        d, L = pool[i % len(pool)], sets[i % len(sets)].lin[0]
+        ev[i][0].record()
+        tvl.lin_tree_verify(d["q"], d["k"], d["v"], d["g"], d["beta"], d["state"], d["parent"], d["n_nodes"],
+                            L.scale, out=d["out"], cap_delta=d["cap"])
+        ev[i][1].record()
+        tvl.lin_tree_commit(d["state"], d["path"], d["path_len"], d["k"], d["g"], d["cap"])
+        ev[i][2].record()
+    torch.cuda.synchronize()
+    res = {}
+    for j, (nme, fn) in enumerate((("lin_tree_verify", lin_verify_bytes), ("lin_tree_commit", lin_commit_bytes))):
+        ms = sum(e[j].elapsed_time(e[j + 1]) for e in ev) / K
+        nb = sum(fn(W.lin[0]) for W in sets) / len(sets)
+        gbs = nb / (ms * 1e-3) / 1e9
+        res[nme] = {"mean_us": round(ms * 1e3, 2), "algorithmic_MB": round(nb / 1e6, 2), "GB_per_s": round(gbs, 1),
+                    "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "counter_traffic_bytes": counter_traffic(nme)}
+    return res
+
+
 def time_workload2(args, tvl, torch, dev, B):
     """The second workload: budgets 8 (a chain), 16 and 40, with a Q8_0 K cache and a Q4_0 V
     cache, through the same three calls as the step.  One input set per variant (each is
@@ -505,25 +543,31 @@ def main():
     Hkv, Tcap = A0.k_cache.shape[1], A0.k_cache.shape[2]
     ws_bytes = max(tvl.attn_tree_workspace_bytes(B, A0.q.shape[1], A0.Hq, Hkv, A0.D, Tcap, A0.window), 256)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
-    names = ["lin_tree_verify", "attn_tree_verify", "lin_tree_commit"]
+    names = ["lin_tree_verify_commit", "attn_tree_verify"]
 
     def step(i, ev=None):
+        # One step per input set: the linear layer's verify, which first commits the path the
+        # same sequences accepted in their previous step (fused), and the attention layer.
         d = pool[i % len(pool)]
         W = sets[i % len(sets)]
         L, A = W.lin[0], W.attn[0]
+        visit = i // len(pool)
+        cap, prev_cap = d["caps"][visit % 2], d["caps"][(visit + 1) % 2]
         if ev:
             ev[0].record()
-        tvl.lin_tree_verify(d["q"], d["k"], d["v"], d["g"], d["beta"], d["state"], d["parent"], d["n_nodes"],
-                            L.scale, out=d["out"], cap_delta=d["cap"])
+        if visit == 0:
+            tvl.lin_tree_verify(d["q"], d["k"], d["v"], d["g"], d["beta"], d["state"], d["parent"], d["n_nodes"],
+                                L.scale, out=d["out"], cap_delta=cap)
+        else:
+            tvl.lin_tree_verify_commit(d["q"], d["k"], d["v"], d["g"], d["beta"], d["state"], d["parent"],
+                                       d["n_nodes"], L.scale, d["path"], d["path_len"], d["k"], d["g"], prev_cap,
+                                       out=d["out"], cap_delta=cap)
         if ev:
             ev[1].record()
         tvl.attn_tree_verify(d["aq"], d["kc"], d["vc"], A.k_type, A.v_type, d["n_past"], d["aparent"],
                              d["an_nodes"], A.window, A.scale, out=d["aout"], lse=d["lse"], workspace=ws)
         if ev:
             ev[2].record()
-        tvl.lin_tree_commit(d["state"], d["path"], d["path_len"], d["k"], d["g"], d["cap"])
-        if ev:
-            ev[3].record()
 
     if args.copy_probe_mib > 0:
         n = args.copy_probe_mib * (1 << 20) // 4
@@ -537,7 +581,7 @@ def main():
     # the timed steps run at the clock the GPU holds under sustained load.
     w0 = time.perf_counter()
     warm = 0
-    while warm < args.warmup or time.perf_counter() - w0 < args.min_warmup_s:
+    while warm < max(args.warmup, 2 * len(pool)) or time.perf_counter() - w0 < args.min_warmup_s:
         step(warm)
         warm += 1
         if warm % 16 == 0:
@@ -546,7 +590,7 @@ def main():
     print(f"# warmup done: {warm} steps in {time.perf_counter() - w0:.2f} s", file=sys.stderr, flush=True)
 
     K = args.steps
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
     torch.cuda.synchronize()
     h0 = time.perf_counter()
     for i in range(K):
@@ -557,15 +601,14 @@ def main():
     for e in evs:
         for j, n in enumerate(names):
             per[n].append(e[j].elapsed_time(e[j + 1]))
-    ms_step = evs[0][0].elapsed_time(evs[-1][3]) / K
+    ms_step = evs[0][0].elapsed_time(evs[-1][2]) / K
     print(f"# timed {K} steps", file=sys.stderr, flush=True)
 
     nodes = sum(int(W.lin[0].n_nodes.sum()) for W in sets) / len(sets)
     value = 2.0 * nodes / (ms_step * 1e-3)
     byts = {
-        "lin_tree_verify": sum(lin_verify_bytes(W.lin[0]) for W in sets) / len(sets),
+        "lin_tree_verify_commit": sum(lin_verify_commit_bytes(W.lin[0]) for W in sets) / len(sets),
         "attn_tree_verify": sum(attn_bytes(W.attn[0]) for W in sets) / len(sets),
-        "lin_tree_commit": sum(lin_commit_bytes(W.lin[0]) for W in sets) / len(sets),
     }
     kernels = {}
     for n in names:
@@ -584,6 +627,7 @@ def main():
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": counter_traffic(dom),
                 "algorithmic_bytes_per_launch": int(byts[dom])}
 
+    unfused = None if args.no_workload2 else time_unfused_linear(args, tvl, torch, pool, sets)
     next_kernels = time_next_rows(args, tvl, torch, dev, pool[0], A0, B)
     workload2 = None if args.no_workload2 else time_workload2(args, tvl, torch, dev, B)
 
@@ -609,6 +653,7 @@ def main():
                                f"dk=dv=128 fp32 state + commit, attention Hq24/Hkv4 D256 Q8_0 T=4096 window 2048",
                    "global_batch": B, "tree_nodes": 22, "kv_type": "q8_0", "window": 2048, "n_past": 4096},
         "kernels": kernels,
+        "linear_unfused": unfused,
         "next_kernels": next_kernels,
         "workload2": workload2,
         "roofline": roofline,

@@ -9,7 +9,8 @@
  *                     every node's root path from the committed state and captures the
  *                     per-node factors needed to commit later;
  *   lin_tree_commit   after acceptance, moves the committed state in place to the end of
- *                     the accepted root path, using the captured factors;
+ *                     the accepted root path, using the captured factors (or, fused,
+ *                     lin_tree_verify_commit applies it inside the next step's verify);
  *   attn_tree_verify  full-attention layer: tree-masked softmax attention over a Q8_0 /
  *                     Q4_0 quantised KV cache with an optional sliding window.
  *
@@ -170,6 +171,39 @@ int lin_tree_commit(int B, int N, int Hk, int Hv, int dk, int dv, int dtype, int
  * (0 if the sizes are invalid).  The workspace holds per-split partial results.
  */
 size_t attn_tree_workspace_bytes(int B, int N, int Hq, int Hkv, int D, int Tcap, int window);
+
+/*
+ * lin_tree_verify_commit -- the previous step's commit and this step's verify in one pass.
+ * (PR #606 "SpecLA factor-capture speculative decoding": the captured factors are applied
+ * to the state while the next verify loads it, instead of a separate pass over the state.)
+ *
+ * For every (sequence, value head), the state is first moved to the end of the previous
+ * step's accepted path exactly as lin_tree_commit would (from that step's k, g and captured
+ * deltas) and stored back into `state`; then this step's tree is verified from it exactly as
+ * lin_tree_verify would.  Each state tile is read once and written once, where a separate
+ * commit would read it a second time.  A sequence with prev_path_len = 0 keeps its state
+ * (and it is not written).
+ *
+ *   B, N, Hk, Hv, dk, dv, dtype, head_group, scale, parent, n_nodes, q, k, v, g, beta, out,
+ *   cap_delta             as for lin_tree_verify (this step)
+ *   state                 device, fp32 [B][Hv][dv][dk], in/out: the committed state
+ *   prev_N                tree rows per sequence of the previous step (1..64)
+ *   prev_path, prev_path_len, prev_Lmax   the previous step's accepted paths (as for
+ *                         lin_tree_commit; prev_Lmax <= prev_N)
+ *   prev_k, prev_g        device, the previous step's k [B][prev_N][Hk][dk] and
+ *                         g [B][prev_N][Hv], of dtype
+ *   prev_cap_delta        device, fp32 [B][prev_N][Hv][dv]: the previous verify's
+ *                         cap_delta.  Must not be the same buffer as cap_delta.
+ * prev_k and prev_cap_delta must be 16-byte aligned in addition to lin_tree_verify's
+ * arguments.
+ */
+int lin_tree_verify_commit(int B, int N, int Hk, int Hv, int dk, int dv, int dtype, int head_group,
+                           float scale, const int32_t* parent, const int32_t* n_nodes,
+                           const void* q, const void* k, const void* v, const void* g,
+                           const void* beta, float* state, float* out, float* cap_delta,
+                           int prev_N, const int32_t* prev_path, const int32_t* prev_path_len,
+                           int prev_Lmax, const void* prev_k, const void* prev_g,
+                           const float* prev_cap_delta, void* stream);
 
 /*
  * attn_tree_verify -- one full-attention layer over the draft tree.

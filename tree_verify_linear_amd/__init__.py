@@ -14,7 +14,7 @@ import os
 
 import torch
 
-__all__ = ["TreeVerifyError", "lib", "lib_path", "lin_tree_verify", "lin_tree_commit",
+__all__ = ["TreeVerifyError", "lib", "lib_path", "lin_tree_verify", "lin_tree_commit", "lin_tree_verify_commit",
            "attn_tree_verify", "attn_tree_workspace_bytes", "tree_accept_greedy",
            "tree_accept_workspace_bytes", "kv_tree_compact", "conv_tree_verify", "conv_tree_commit",
            "validate_tree", "validate_path",
@@ -34,6 +34,8 @@ _i, _f, _p, _sz = ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
 EXPORTS = {
     "lin_tree_verify": (_i, [_i, _i, _i, _i, _i, _i, _i, _i, _f, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p]),
     "lin_tree_commit": (_i, [_i, _i, _i, _i, _i, _i, _i, _i, _p, _p, _i, _p, _p, _p, _p, _p]),
+    "lin_tree_verify_commit": (_i, [_i, _i, _i, _i, _i, _i, _i, _i, _f, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p,
+                                    _i, _p, _p, _i, _p, _p, _p, _p]),
     "attn_tree_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
     "attn_tree_verify": (_i, [_i, _i, _i, _i, _i, _i, _i, _i, _i, _f, _p, _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
     "tree_accept_workspace_bytes": (_sz, [_i, _i, _i, _i]),
@@ -147,6 +149,34 @@ def lin_tree_commit(state, path, path_len, k, g, cap_delta, head_group: str = "c
                                  _ptr(path_len), Lmax, _ptr(k), _ptr(g), _ptr(cap_delta), _ptr(state),
                                  _stream(state.device)))
     return state
+
+
+def lin_tree_verify_commit(q, k, v, g, beta, state, parent, n_nodes, scale: float, prev_path, prev_path_len,
+                           prev_k, prev_g, prev_cap_delta, head_group: str = "contiguous", out=None, cap_delta=None):
+    """The previous step's commit (its path, k, g and captured deltas) applied to ``state`` in
+    place, then this step's verify from the committed state.  Returns ``(out, cap_delta)``."""
+    B, N, Hk, dk = q.shape
+    Hv, dv = v.shape[2], v.shape[3]
+    dt = q.dtype
+    _dev(q, "q", dt); _dev(k, "k", dt, (B, N, Hk, dk)); _dev(v, "v", dt, (B, N, Hv, dv))
+    _dev(g, "g", dt, (B, N, Hv)); _dev(beta, "beta", dt, (B, N, Hv))
+    _dev(state, "state", torch.float32, (B, Hv, dv, dk))
+    _dev(parent, "parent", torch.int32, (B, N)); _dev(n_nodes, "n_nodes", torch.int32, (B,))
+    PN = prev_k.shape[1]
+    _dev(prev_k, "prev_k", dt, (B, PN, Hk, dk)); _dev(prev_g, "prev_g", dt, (B, PN, Hv))
+    _dev(prev_cap_delta, "prev_cap_delta", torch.float32, (B, PN, Hv, dv))
+    _dev(prev_path, "prev_path", torch.int32); _dev(prev_path_len, "prev_path_len", torch.int32, (B,))
+    if out is None:
+        out = torch.empty((B, N, Hv, dv), dtype=torch.float32, device=q.device)
+    if cap_delta is None:
+        cap_delta = torch.empty((B, N, Hv, dv), dtype=torch.float32, device=q.device)
+    _dev(out, "out", torch.float32, (B, N, Hv, dv)); _dev(cap_delta, "cap_delta", torch.float32, (B, N, Hv, dv))
+    _check(lib().lin_tree_verify_commit(B, N, Hk, Hv, dk, dv, _in_dtype(q), HEAD_GROUPS[head_group], float(scale),
+                                        _ptr(parent), _ptr(n_nodes), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                        _ptr(state), _ptr(out), _ptr(cap_delta), PN, _ptr(prev_path),
+                                        _ptr(prev_path_len), prev_path.shape[1], _ptr(prev_k), _ptr(prev_g),
+                                        _ptr(prev_cap_delta), _stream(q.device)))
+    return out, cap_delta
 
 
 def attn_tree_workspace_bytes(B: int, N: int, Hq: int, Hkv: int, D: int, Tcap: int, window: int) -> int:

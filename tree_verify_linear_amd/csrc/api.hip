@@ -118,6 +118,34 @@ int lin_tree_verify(int B, int N, int Hk, int Hv, int dk, int dv, int dtype, int
     return launch_lin_verify(a, dtype == TV_BF16, static_cast<hipStream_t>(stream));
 }
 
+int lin_tree_verify_commit(int B, int N, int Hk, int Hv, int dk, int dv, int dtype, int head_group, float scale,
+                           const int32_t* parent, const int32_t* n_nodes, const void* q, const void* k, const void* v,
+                           const void* g, const void* beta, float* state, float* out, float* cap_delta, int prev_N,
+                           const int32_t* prev_path, const int32_t* prev_path_len, int prev_Lmax, const void* prev_k,
+                           const void* prev_g, const float* prev_cap_delta, void* stream) {
+    clear_error();
+    const char* fn = "lin_tree_verify_commit";
+    int st = check_common_lin(fn, B, N, Hk, Hv, dk, dv, dtype, head_group);
+    if (st != TV_OK) return st;
+    if (prev_N < 1 || prev_N > TV_MAX_NODES) return set_error(TV_ERANGE, "%s: prev_N=%d not in [1, %d]", fn, prev_N, TV_MAX_NODES);
+    if (prev_Lmax < 1 || prev_Lmax > prev_N)
+        return set_error(TV_ERANGE, "%s: prev_Lmax=%d not in [1, prev_N=%d]", fn, prev_Lmax, prev_N);
+    if (!std::isfinite(scale)) return set_error(TV_EINVAL, "%s: scale is not finite", fn);
+    if (!parent || !n_nodes || !q || !k || !v || !g || !beta || !state || !out || !cap_delta || !prev_path ||
+        !prev_path_len || !prev_k || !prev_g || !prev_cap_delta)
+        return set_error(TV_EINVAL, "%s: null pointer argument", fn);
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(state, 16) || !aligned(out, 16) ||
+        !aligned(cap_delta, 16) || !aligned(prev_k, 16) || !aligned(prev_cap_delta, 16))
+        return set_error(TV_EINVAL, "%s: q, k, v, state, out, cap_delta, prev_k and prev_cap_delta must be 16-byte "
+                         "aligned", fn);
+    if (static_cast<const void*>(cap_delta) == static_cast<const void*>(prev_cap_delta))
+        return set_error(TV_EINVAL, "%s: cap_delta and prev_cap_delta must be different buffers", fn);
+    LinVerifyArgs a{B, N, Hk, Hv, dk, dv, Hv / Hk, head_group == TV_HEADS_TILED, scale, parent, n_nodes,
+                    q, k, v, g, beta, state, out, cap_delta, prev_N, prev_Lmax, prev_path, prev_path_len, prev_k,
+                    prev_g, prev_cap_delta, state};
+    return launch_lin_verify(a, dtype == TV_BF16, static_cast<hipStream_t>(stream));
+}
+
 int lin_tree_commit(int B, int N, int Hk, int Hv, int dk, int dv, int dtype, int head_group, const int32_t* path,
                     const int32_t* path_len, int Lmax, const void* k, const void* g, const float* cap_delta,
                     float* state, void* stream) {

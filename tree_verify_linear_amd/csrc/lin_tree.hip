@@ -30,7 +30,9 @@
 //     another's arithmetic.  No load address depends on loaded data.
 // Commit: the accepted path's captured deltas are flushed into the state in place,
 //     S <- (prod_m g_{a_m}) S0 + sum_m c_m k_{a_m} delta_{a_m}^T,  c_m = prod_{m'>m} g_{a_m'},
-//   a streaming rank-L update (HBM bound).
+//   a streaming rank-L update (HBM bound).  Fused variant: the next step's verify applies
+//   the same update to the state tile it has just loaded, stores the committed tile and
+//   verifies from it, so the state is read once per step instead of twice.
 #include "tv_internal.h"
 
 namespace tv {
@@ -137,6 +139,12 @@ struct UnitIn {
     uint4 vraw[VL];
     uint32_t graw, braw;                             // lane i: node i's g and beta, raw input bits
     int praw, nraw;                                  // lane i: parent[i]; n_nodes[b] (unclamped)
+    // a pending commit (previous step's path): its length, lane l's entry (node, decay) and
+    // the first four entries' key / delta segments (lane -> entry lane / 16, segment lane % 16)
+    int pL, pnode;
+    float pgv;
+    float pkv[8];
+    float4 pdv;
 };
 
 // Issues every load of a unit.  No address depends on loaded data (the tree size n is
@@ -192,6 +200,43 @@ __device__ __forceinline__ void load_unit(UnitIn<DK, NT, BF16IN>& in, const LinV
     }
     const float* tile = a.state + (static_cast<size_t>(id.b) * a.Hv + id.h) * a.dv * DK + static_cast<size_t>(id.j0) * DK;
     load_state_tile<DK>(in.sa, tile, CW >> 4, l16, g4);
+    in.pL = 0;
+    if (a.pend_path_len) {
+        // Issued last: the path entries, then (dependent on them) the decays and the first
+        // four entries' key and delta segments, so the other loads are already in flight.
+        const int PN = a.pend_N;
+        in.pL = clampi(((const __attribute__((address_space(4))) int32_t*)(a.pend_path_len))[id.b], 0, a.pend_Lmax);
+        int node = 0;
+        if (lane < a.pend_Lmax) node = clampi(a.pend_path[static_cast<size_t>(id.b) * a.pend_Lmax + lane], 0, PN - 1);
+        in.pnode = node;
+        in.pgv = lane < a.pend_Lmax ? load_scalar<BF16IN>(a.pend_g, (static_cast<size_t>(id.b) * PN + node) * a.Hv + id.h)
+                                    : 0.f;
+        const int q = lane >> 4, sg = lane & 15;
+        const int nq = __shfl(node, q);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) in.pkv[e] = 0.f;
+        in.pdv = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (sg * 8 < DK) {
+            const size_t ko = ((static_cast<size_t>(id.b) * PN + nq) * a.Hk + id.kh) * DK + sg * 8;
+            if constexpr (BF16IN) {
+                const uint4 w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.pend_k) + ko);
+                const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    in.pkv[2 * e] = __uint_as_float(u[e] << 16);
+                    in.pkv[2 * e + 1] = __uint_as_float(u[e] & 0xffff0000u);
+                }
+            } else {
+                const float4 x0 = *reinterpret_cast<const float4*>(static_cast<const float*>(a.pend_k) + ko);
+                const float4 x1 = *reinterpret_cast<const float4*>(static_cast<const float*>(a.pend_k) + ko + 4);
+                in.pkv[0] = x0.x; in.pkv[1] = x0.y; in.pkv[2] = x0.z; in.pkv[3] = x0.w;
+                in.pkv[4] = x1.x; in.pkv[5] = x1.y; in.pkv[6] = x1.z; in.pkv[7] = x1.w;
+            }
+        }
+        if (sg * 4 < CW)
+            in.pdv = *reinterpret_cast<const float4*>(
+                a.pend_delta + ((static_cast<size_t>(id.b) * PN + nq) * a.Hv + id.h) * a.dv + id.j0 + sg * 4);
+    }
 }
 
 // Shared memory of one verify wave.
@@ -210,6 +255,12 @@ struct VerifySmem {
             __align__(16) float Pw[NMAX][NMAX];    //   (both read by the walks)
         };
         __align__(16) float Ds[NMAX][64];           // then delta_i per value channel
+        struct {                                    // before all of those: a pending commit
+            __align__(16) float pk[4][128];         //   key rows of four accepted nodes
+            __align__(16) float pd[4][64];          //   c_l * delta_l for the unit's channels
+            int pn[TV_MAX_NODES];                   //   accepted node of entry l
+            float pg[TV_MAX_NODES], pc[TV_MAX_NODES];   // its decay; c_l = prod_{l' > l} g
+        };
     };
     __align__(16) uint8_t Vs[NMAX * 64 * (BF16IN ? 2 : 4)];   // v rows of the unit, [node][channel]
     float cv[NMAX], ca[NMAX], cb[NMAX], cd[NMAX];   // per-node scalars of the walk
@@ -386,6 +437,121 @@ __device__ __forceinline__ void store_unit(VerifySmem<NT, BF16IN>& sm, const Lin
     __syncthreads();                                // LDS is reused by the next unit
 }
 
+// Commits the previous step's accepted path a_0 .. a_{L-1} into the unit's state tile, in
+// registers, and stores the committed tile:  S <- G S + sum_l c_l k_{a_l} delta_{a_l}^T with
+// G = prod_l g_{a_l} and c_l = prod_{l' > l} g_{a_l'} (the commit's formula).  Entries are
+// staged four at a time through LDS that the unit's own computation overwrites later.
+template <int DK, int NT, bool BF16IN>
+__device__ __forceinline__ void apply_pending(UnitIn<DK, NT, BF16IN>& in, VerifySmem<NT, BF16IN>& sm,
+                                              const LinVerifyArgs& a, int unit, int ctiles, int CW, int lane) {
+    constexpr int KS = (DK + 31) / 32;
+    auto& sa = in.sa;
+    const UnitIds id = unit_ids(a, unit, ctiles, CW);
+    const int L = in.pL;
+    if (L == 0) return;                             // nothing accepted: the state is unchanged
+    const int g4 = lane >> 4, l16 = lane & 15, MT = CW >> 4;
+    const int PN = a.pend_N;
+    if (lane < L) {
+        sm.pn[lane] = in.pnode;
+        sm.pg[lane] = in.pgv;
+    }
+    __syncthreads();
+    if (lane < L) {
+        float c = 1.f;
+        for (int l = lane + 1; l < L; ++l) c *= sm.pg[l];
+        sm.pc[lane] = c;
+    }
+    __syncthreads();
+    const float G = sm.pc[0] * sm.pg[0];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                sa[mt][ks][hh].x *= G; sa[mt][ks][hh].y *= G; sa[mt][ks][hh].z *= G; sa[mt][ks][hh].w *= G;
+            }
+    for (int c0 = 0; c0 < L; c0 += 4) {
+        {   // lane -> (entry q, segment s): 8 key elements and 4 channels of c_l * delta_l
+            const int q = lane >> 4, s = lane & 15, l = c0 + q;
+            float kv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+            float4 dv4 = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (c0 == 0) {                          // loaded with the unit's inputs
+                if (l < L) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) kv[e] = in.pkv[e];
+                    const float cl = sm.pc[l];
+                    dv4 = make_float4(cl * in.pdv.x, cl * in.pdv.y, cl * in.pdv.z, cl * in.pdv.w);
+                }
+            } else if (l < L) {
+                const int node = sm.pn[l];
+                if (s * 8 < DK) {
+                    const size_t ko = ((static_cast<size_t>(id.b) * PN + node) * a.Hk + id.kh) * DK + s * 8;
+                    if constexpr (BF16IN) {
+                        const uint4 w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.pend_k) + ko);
+                        const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            kv[2 * e] = __uint_as_float(u[e] << 16);
+                            kv[2 * e + 1] = __uint_as_float(u[e] & 0xffff0000u);
+                        }
+                    } else {
+                        const float4 x0 = *reinterpret_cast<const float4*>(static_cast<const float*>(a.pend_k) + ko);
+                        const float4 x1 = *reinterpret_cast<const float4*>(static_cast<const float*>(a.pend_k) + ko + 4);
+                        kv[0] = x0.x; kv[1] = x0.y; kv[2] = x0.z; kv[3] = x0.w;
+                        kv[4] = x1.x; kv[5] = x1.y; kv[6] = x1.z; kv[7] = x1.w;
+                    }
+                }
+                if (s * 4 < CW) {
+                    const float cl = sm.pc[l];
+                    const float4 d = *reinterpret_cast<const float4*>(
+                        a.pend_delta + ((static_cast<size_t>(id.b) * PN + node) * a.Hv + id.h) * a.dv + id.j0 + s * 4);
+                    dv4 = make_float4(cl * d.x, cl * d.y, cl * d.z, cl * d.w);
+                }
+            }
+            if (s * 8 < 128) {
+                *reinterpret_cast<float4*>(&sm.pk[q][s * 8]) = make_float4(kv[0], kv[1], kv[2], kv[3]);
+                *reinterpret_cast<float4*>(&sm.pk[q][s * 8 + 4]) = make_float4(kv[4], kv[5], kv[6], kv[7]);
+            }
+            *reinterpret_cast<float4*>(&sm.pd[q][s * 4]) = dv4;
+        }
+        __syncthreads();
+        const int nq = L - c0 < 4 ? L - c0 : 4;      // entries in this chunk (wave-uniform)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            if (q >= nq) break;
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                const float dj = sm.pd[q][(mt * 16 + l16) & 63];
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    if (!kvalid<DK>(ks, g4)) continue;
+                    const float4 k0 = *reinterpret_cast<const float4*>(&sm.pk[q][ks * 32 + 8 * g4]);
+                    const float4 k1 = *reinterpret_cast<const float4*>(&sm.pk[q][ks * 32 + 8 * g4 + 4]);
+                    float4& x0 = sa[mt][ks][0];
+                    float4& x1 = sa[mt][ks][1];
+                    x0.x = fmaf(dj, k0.x, x0.x); x0.y = fmaf(dj, k0.y, x0.y);
+                    x0.z = fmaf(dj, k0.z, x0.z); x0.w = fmaf(dj, k0.w, x0.w);
+                    x1.x = fmaf(dj, k1.x, x1.x); x1.y = fmaf(dj, k1.y, x1.y);
+                    x1.z = fmaf(dj, k1.z, x1.z); x1.w = fmaf(dj, k1.w, x1.w);
+                }
+            }
+        }
+        __syncthreads();
+    }
+    // the committed tile, in place
+    float* tile = a.state_out + (static_cast<size_t>(id.b) * a.Hv + id.h) * a.dv * DK + static_cast<size_t>(id.j0) * DK;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            if (mt < MT && kvalid<DK>(ks, g4)) {
+                float* p = tile + (mt * 16 + l16) * DK + ks * 32 + 8 * g4;
+                *reinterpret_cast<float4*>(p) = sa[mt][ks][0];
+                *reinterpret_cast<float4*>(p + 4) = sa[mt][ks][1];
+            }
+}
+
 // Verify for trees of up to 32 nodes: one unit per workgroup of one wave.  The hardware
 // dispatcher keeps several units resident per CU (registers allow two waves per SIMD, the
 // LDS footprint seven workgroups per CU), so one unit's memory latency hides behind
@@ -400,6 +566,7 @@ __global__ __launch_bounds__(64, 2) void lin_verify_kernel(LinVerifyArgs a) {
     const int u = xcd_remap(blockIdx.x, gridDim.x);
     UnitIn<DK, NT, BF16IN> in;
     load_unit(in, a, u, ctiles, CW, lane);
+    if (a.pend_path_len) apply_pending<DK, NT, BF16IN>(in, sm, a, u, ctiles, CW, lane);
     const int n = compute_unit(in, sm, a, u, ctiles, CW, lane);
     store_unit(sm, a, u, n, ctiles, CW, lane);
 }
@@ -416,6 +583,7 @@ __global__ __launch_bounds__(64, 1) void lin_verify_wide_kernel(LinVerifyArgs a)
     const int u = xcd_remap(blockIdx.x, gridDim.x);
     UnitIn<DK, NT, BF16IN> in;
     load_unit(in, a, u, ctiles, CW, lane);
+    if (a.pend_path_len) apply_pending<DK, NT, BF16IN>(in, sm, a, u, ctiles, CW, lane);
     const int n = compute_unit(in, sm, a, u, ctiles, CW, lane);
     store_unit(sm, a, u, n, ctiles, CW, lane);
 }

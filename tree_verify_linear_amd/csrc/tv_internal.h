@@ -28,6 +28,15 @@ struct LinVerifyArgs {
     const float* state;
     float* out;
     float* cap_delta;
+    // The previous step's accepted path, committed into the state tile before this verify
+    // (pend_path_len == nullptr: nothing pending, the state is only read).
+    int pend_N, pend_Lmax;
+    const int32_t* pend_path;
+    const int32_t* pend_path_len;
+    const void* pend_k;
+    const void* pend_g;
+    const float* pend_delta;
+    float* state_out;                 // == state when a commit is pending
 };
 int launch_lin_verify(const LinVerifyArgs& a, bool bf16, hipStream_t stream);
 
