@@ -230,7 +230,7 @@ int lin_tree_verify_commit(int B, int N, int Hk, int Hv, int dk, int dv, int dty
  *   q          device, bf16 [B][N][Hq][D]; |q| must stay below 65504 (converted to fp16)
  *   k_cache    device, bytes [B][Hkv][Tcap][D/32 blocks of k_type]
  *   v_cache    device, bytes [B][Hkv][Tcap][D/32 blocks of v_type]
- *   out        device, fp32 [B][N][Hq][D]
+ *   out        device, fp32 [B][N][Hq][D], 16-byte aligned
  *   lse        device, fp32 [B][N][Hq] (natural log) or NULL
  *   workspace  device, >= attn_tree_workspace_bytes(...) bytes, 256-byte aligned; its
  *              contents need no initialisation and are garbage afterwards

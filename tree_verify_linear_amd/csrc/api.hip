@@ -190,8 +190,10 @@ int attn_tree_verify(int B, int N, int Hq, int Hkv, int D, int Tcap, int k_type,
     if (!std::isfinite(scale)) return set_error(TV_EINVAL, "%s: scale is not finite", fn);
     if (!parent || !n_nodes || !n_past || !q || !k_cache || !v_cache || !out || !workspace)
         return set_error(TV_EINVAL, "%s: null pointer argument", fn);
-    if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(workspace, 256))
-        return set_error(TV_EINVAL, "%s: q and the caches must be 16-byte aligned, workspace 256-byte aligned", fn);
+    if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
+        !aligned(workspace, 256))
+        return set_error(TV_EINVAL, "%s: q, the caches and out must be 16-byte aligned, workspace 256-byte aligned",
+                         fn);
     const size_t need = attn_workspace_bytes(B, N, Hq, Hkv, D, Tcap, window);
     if (need == 0) return set_error(TV_ERANGE, "%s: sizes overflow", fn);
     if (workspace_bytes < need)

@@ -33,6 +33,7 @@
 //     scoring wave runs the softmax the PV wave issues the PV matrix instructions.
 //   * Each split writes unnormalised O, its running max and sum; a combine pass rescales and
 //     sums the splits.  With a single split the kernel normalises and writes the output.
+#include <cfloat>
 #include <cmath>
 
 #include "tv_internal.h"
@@ -53,7 +54,6 @@ constexpr int RTMAX = 9;                     // row tiles per row block
 constexpr int OWNMAX = (RTMAX + 3) / 4;      // softmax tiles owned per scoring wave
 constexpr int ROWS_PER_BLOCK = RTMAX * 16;   // 144
 constexpr int MAXROW = 8 * 34;               // bytes of one slot's row (Q8_0, the larger)
-constexpr int VST = TS + 4;                  // fp16 stride of a transposed V column
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -128,6 +128,18 @@ __device__ __forceinline__ f16x8 block_ints8(const uint8_t* row, int kb, int g) 
     return f16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
+// Two probabilities as fp16 pairs: hi = RN(p) (packed convert) and lo = RN(p - hi), the
+// residual taken in fp32 by v_fma_mix (hi widened exactly) and written straight into the
+// halves of one register.
+__device__ __forceinline__ void split_p2(float p0, float p1, uint32_t& hi, uint32_t& lo) {
+    const f16x2 h = {static_cast<_Float16>(p0), static_cast<_Float16>(p1)};
+    hi = __builtin_bit_cast(uint32_t, h);
+    uint32_t l;
+    asm("v_fma_mixlo_f16 %0, %1, 1.0, -%2 op_sel_hi:[0,0,1]" : "=v"(l) : "v"(p0), "v"(hi));
+    asm("v_fma_mixhi_f16 %0, %1, 1.0, -%2 op_sel:[0,0,1] op_sel_hi:[0,0,1]" : "+v"(l) : "v"(p1), "v"(hi));
+    lo = l;
+}
+
 // d*q = hi + lo exactly (see the file comment): hi rounds the exact product once, the fused
 // multiply-add returns the residual, which needs at most 8 significant bits.
 template <typename V>
@@ -156,7 +168,6 @@ struct AttnSmem {
     __align__(16) f32x4 sdump[2][64];                       // wave 0's copy of row tile 8 (not read)
     __align__(16) f16x8 pbuf[2][RTMAX][64];                 // P hi in the PV operand layout
     __align__(16) f16x8 pbuf_lo[2][RTMAX][64];              // P lo = P - P hi, same layout
-    __align__(16) _Float16 vdq[4][2][64][VST];              // [PV wave][hi, lo][column][slot]
     __align__(16) float alpha[2][RTMAX][16];                // O rescale factor per row
     int grow[2][RTMAX];                                     // row tile needs a rescale
     float mfin[ROWS_PER_BLOCK], lfin[ROWS_PER_BLOCK];
@@ -288,6 +299,9 @@ __global__ __launch_bounds__(THREADS, 1) void attn_kernel(AttnLaunch L) {
             const int x = (i - 3) % 3, half = (i - 3) / 3;
             return 4 * half + (x < wl ? x : x + 1);
         };
+        // The sign of the scale is folded into Q (exact), so the scores are scaled by a positive
+        // factor and the row maximum can be taken before scaling.
+        const uint32_t qflip = a.scale < 0.f ? 0x80008000u : 0u;
         f16x8 qop[RTMAX][2];
 #pragma unroll
         for (int i = 0; i < RTMAX; ++i) {
@@ -301,7 +315,7 @@ __global__ __launch_bounds__(THREADS, 1) void attn_kernel(AttnLaunch L) {
             for (int kb = 0; kb < 2; ++kb) {
                 uint4 w = make_uint4(0, 0, 0, 0);
                 if (ok) w = *reinterpret_cast<const uint4*>(qrow + (2 * wl + kb) * 32 + 8 * g4);
-                const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+                const uint32_t u[4] = {w.x ^ qflip, w.y ^ qflip, w.z ^ qflip, w.w ^ qflip};
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     qop[i][kb][2 * e] = static_cast<_Float16>(__uint_as_float(u[e] << 16));
@@ -336,7 +350,9 @@ __global__ __launch_bounds__(THREADS, 1) void attn_kernel(AttnLaunch L) {
             rlo_max[j] = __builtin_amdgcn_readfirstlane(rm);
             own[j][0] = own[j][1] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
-        const float sl2 = a.scale * kLog2e;
+        // |scale| * log2(e), kept positive (a zero scale becomes the smallest normal float: the
+        // scores then vanish and the weights are uniform, as they are for scale 0)
+        const float sl2 = fmaxf(fabsf(a.scale) * kLog2e, FLT_MIN);
 
         for (int k = 0; k <= ntiles; ++k) {
             // phase 1: partial scores of tile k
@@ -390,11 +406,11 @@ __global__ __launch_bounds__(THREADS, 1) void attn_kernel(AttnLaunch L) {
                     }
                     const f32x4 sa = (own[j][0] + pa_[0]) + (pa_[1] + pa_[2]);
                     const f32x4 sb = (own[j][1] + pb_[0]) + (pb_[1] + pb_[2]);
-                    float x[8];
+                    float x[8];        // unscaled scores
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        x[e] = sa[e] * sl2;
-                        x[4 + e] = sb[e] * sl2;
+                        x[e] = sa[e];
+                        x[4 + e] = sb[e];
                     }
                     const bool fast = t0 + TS <= (T < s1 ? T : s1) && t0 >= rlo_max[j];
                     if (!fast) {
@@ -411,10 +427,9 @@ __global__ __launch_bounds__(THREADS, 1) void attn_kernel(AttnLaunch L) {
                             }
                             x[e] = vis ? x[e] : -INFINITY;
                         }
-                    } else if (!rs[j].on) {
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) x[e] = -INFINITY;
                     }
+                    // (rows past the tree are not masked on unmasked tiles: their Q is zero,
+                    // so their weights stay finite, and nothing reads their results)
                     float mt = x[0];
 #pragma unroll
                     for (int e = 1; e < 8; ++e) mt = fmaxf(mt, x[e]);
@@ -422,7 +437,7 @@ __global__ __launch_bounds__(THREADS, 1) void attn_kernel(AttnLaunch L) {
                     const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(mt), __float_as_uint(mt), false, false);
                     mt = fmaxf(__uint_as_float(s16[0]), __uint_as_float(s16[1]));
                     const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt), false, false);
-                    mt = fmaxf(__uint_as_float(s32[0]), __uint_as_float(s32[1]));
+                    mt = fmaxf(__uint_as_float(s32[0]), __uint_as_float(s32[1])) * sl2;
                     // Lazy rescaling: P is taken against a reference max that moves only when
                     // the row max grows by more than 2^8 (so P <= 256); alpha is 1 otherwise.
                     const bool grow = mt > rs[j].m + 8.f;
@@ -433,18 +448,19 @@ __global__ __launch_bounds__(THREADS, 1) void attn_kernel(AttnLaunch L) {
                     const float m = mnew == -INFINITY ? 0.f : mnew;      // then every x is -inf
                     // P = hi + lo in fp16 (lo is the rounding residual of hi), so P enters
                     // the PV products to about 2^-22 relative
-                    f16x8 p, plo;
+                    float pe[8];
                     float ps = 0.f;
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
-                        const float pe = __builtin_amdgcn_exp2f(x[e] - m);
-                        ps += pe;
-                        p[e] = static_cast<_Float16>(pe);
-                        plo[e] = static_cast<_Float16>(pe - static_cast<float>(p[e]));
+                        pe[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[e], sl2, -m));
+                        ps += pe[e];
                     }
+                    uint32_t ph[4], pl[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) split_p2(pe[2 * e], pe[2 * e + 1], ph[e], pl[e]);
                     rs[j].l = rs[j].l * al + ps;
-                    sm.pbuf[bufk][r][lane] = p;
-                    sm.pbuf_lo[bufk][r][lane] = plo;
+                    *reinterpret_cast<uint4*>(&sm.pbuf[bufk][r][lane]) = make_uint4(ph[0], ph[1], ph[2], ph[3]);
+                    *reinterpret_cast<uint4*>(&sm.pbuf_lo[bufk][r][lane]) = make_uint4(pl[0], pl[1], pl[2], pl[3]);
                     if (g4 == 0) sm.alpha[bufk][r][l16] = al;          // row l16's factor
                     if (lane == 0) sm.grow[bufk][r] = anyg;
                 };
@@ -481,50 +497,41 @@ __global__ __launch_bounds__(THREADS, 1) void attn_kernel(AttnLaunch L) {
             for (int jj = 0; jj < 4; ++jj) oacc[r][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
 
         for (int k = 0; k <= ntiles; ++k) {
-            // phase 1: this wave's 64 columns of V for tile k-1 into fp16 hi/lo, slot-major.
-            // Lane: 4 slots x 4 columns of one block per pass; the bytes are transposed first
-            // (slot pairs per column), so the fp16 pairs come out slot-major.
+            // phase 1: this wave's 64 columns of V for tile k-1 as the PV B operands, fp16 hi/lo,
+            // straight from the raw rows into registers.  Column tile jj, lane (g4, l16) holds
+            // column 4*l16 + jj of the wave's 64 (four adjacent columns = one dword per slot)
+            // at the slots of the P operand's lane group: 4g4 .. 4g4+3 and 16+4g4 .. 16+4g4+3.
+            f16x8 bh[4], bl[4];
             if (k >= 1) {
                 const uint8_t* raw = sm.rawv[(k - 1) & 1];
-                const int hb = lane >> 5, sq = (lane >> 3) & 3, cq = lane & 7;
-                const int kb = 2 * wl + hb, e0 = 4 * cq;
-                const int o = VT == TV_Q8_0 ? 34 * kb + 2 + e0 : 18 * kb + 2 + (e0 & 15);
-                const int sh = e0 >= 16 ? 4 : 0;
+                const int kb = 2 * wl + (l16 >> 3), c4 = 4 * (l16 & 7);
+                const int o = VT == TV_Q8_0 ? 34 * kb + 2 + c4 : 18 * kb + 2 + (c4 & 15);
+                const int sh = c4 >= 16 ? 4 : 0;
                 const f16x2 bias = static_cast<_Float16>(ints_bias<VT>());
+                uint32_t w[8];
+                _Float16 dd[8];
 #pragma unroll
-                for (int pass = 0; pass < 2; ++pass) {
-                    const int sbase = 16 * pass + 4 * sq;
-                    uint32_t w[4];
-                    _Float16 dd[4];
+                for (int t = 0; t < 8; ++t) {
+                    const uint8_t* row = raw + (t < 4 ? 4 * g4 + t : 12 + 4 * g4 + t) * VF::ROW;
+                    w[t] = to_biased<VT>(bytes4_rt(row, o), sh);
+                    dd[t] = block_scale(row + kb * VF::BLK);
+                }
 #pragma unroll
-                    for (int s = 0; s < 4; ++s) {
-                        const uint8_t* row = raw + (sbase + s) * VF::ROW;
-                        w[s] = to_biased<VT>(bytes4_rt(row, o), sh);
-                        dd[s] = block_scale(row + kb * VF::BLK);
-                    }
-                    f16x4 hc[4], lc[4];
-#pragma unroll
-                    for (int pp = 0; pp < 2; ++pp) {
-                        // u0 = [w_a.b0, w_b.b0, w_a.b1, w_b.b1], u1 = the same for bytes 2, 3
-                        const uint32_t u0 = __builtin_amdgcn_perm(w[2 * pp + 1], w[2 * pp], 0x05010400u);
-                        const uint32_t u1 = __builtin_amdgcn_perm(w[2 * pp + 1], w[2 * pp], 0x07030602u);
-                        const f16x2 q[4] = {biased_lo(u0) - bias, biased_hi(u0) - bias, biased_lo(u1) - bias,
-                                            biased_hi(u1) - bias};
-                        const f16x2 d2 = {dd[2 * pp], dd[2 * pp + 1]};
-#pragma unroll
-                        for (int c = 0; c < 4; ++c) {
-                            f16x2 h, l;
-                            split_exact(q[c], d2, h, l);
-                            hc[c][2 * pp] = h[0];
-                            hc[c][2 * pp + 1] = h[1];
-                            lc[c][2 * pp] = l[0];
-                            lc[c][2 * pp + 1] = l[1];
-                        }
-                    }
+                for (int pp = 0; pp < 4; ++pp) {
+                    // u0 = [w_a.b0, w_b.b0, w_a.b1, w_b.b1], u1 = the same for bytes 2, 3
+                    const uint32_t u0 = __builtin_amdgcn_perm(w[2 * pp + 1], w[2 * pp], 0x05010400u);
+                    const uint32_t u1 = __builtin_amdgcn_perm(w[2 * pp + 1], w[2 * pp], 0x07030602u);
+                    const f16x2 q[4] = {biased_lo(u0) - bias, biased_hi(u0) - bias, biased_lo(u1) - bias,
+                                        biased_hi(u1) - bias};
+                    const f16x2 d2 = {dd[2 * pp], dd[2 * pp + 1]};
 #pragma unroll
                     for (int c = 0; c < 4; ++c) {
-                        *reinterpret_cast<f16x4*>(&sm.vdq[wl][0][32 * hb + e0 + c][sbase]) = hc[c];
-                        *reinterpret_cast<f16x4*>(&sm.vdq[wl][1][32 * hb + e0 + c][sbase]) = lc[c];
+                        f16x2 h, l;
+                        split_exact(q[c], d2, h, l);
+                        bh[c][2 * pp] = h[0];
+                        bh[c][2 * pp + 1] = h[1];
+                        bl[c][2 * pp] = l[0];
+                        bl[c][2 * pp + 1] = l[1];
                     }
                 }
             }
@@ -545,19 +552,7 @@ __global__ __launch_bounds__(THREADS, 1) void attn_kernel(AttnLaunch L) {
                         for (int jj = 0; jj < 4; ++jj) oacc[r][jj] *= al;
                     }
                 }
-                // V operands of this wave's four column tiles, then P hi/lo one row tile at a
-                // time (keeps the live registers to the accumulators plus one P pair)
-                f16x8 bh[4], bl[4];
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    const int col = 16 * jj + l16;
-                    const f16x4 h0 = *reinterpret_cast<const f16x4*>(&sm.vdq[wl][0][col][4 * g4]);
-                    const f16x4 h1 = *reinterpret_cast<const f16x4*>(&sm.vdq[wl][0][col][16 + 4 * g4]);
-                    const f16x4 l0 = *reinterpret_cast<const f16x4*>(&sm.vdq[wl][1][col][4 * g4]);
-                    const f16x4 l1 = *reinterpret_cast<const f16x4*>(&sm.vdq[wl][1][col][16 + 4 * g4]);
-                    bh[jj] = f16x8{h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
-                    bl[jj] = f16x8{l0[0], l0[1], l0[2], l0[3], l1[0], l1[1], l1[2], l1[3]};
-                }
+                // P hi/lo one row tile at a time against the V operands held since phase 1
 #pragma unroll
                 for (int r = 0; r < RTMAX; ++r) {
                     const f16x8 pa = sm.pbuf[bufp][r][lane];
@@ -587,15 +582,15 @@ __global__ __launch_bounds__(THREADS, 1) void attn_kernel(AttnLaunch L) {
                     const float lsum = sm.lfin[rl];
                     const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
                     float* orow = a.out + ((static_cast<size_t>(b) * N + node) * a.Hq + kvh * L.G + hh) * D + 64 * wl;
-#pragma unroll
-                    for (int jj = 0; jj < 4; ++jj) orow[16 * jj + l16] = oacc[r][jj][e] * inv;
+                    *reinterpret_cast<float4*>(orow + 4 * l16) =
+                        make_float4(oacc[r][0][e] * inv, oacc[r][1][e] * inv, oacc[r][2][e] * inv, oacc[r][3][e] * inv);
                     if (a.lse && wl == 0 && l16 == 0)
                         a.lse[(static_cast<size_t>(b) * N + node) * a.Hq + kvh * L.G + hh] =
                             (sm.mfin[rl] + log2f(lsum)) * kLn2;
                 } else {
                     float* op = L.opart + (part * L.rows_pad + row) * D + 64 * wl;
-#pragma unroll
-                    for (int jj = 0; jj < 4; ++jj) op[16 * jj + l16] = oacc[r][jj][e];
+                    *reinterpret_cast<float4*>(op + 4 * l16) =
+                        make_float4(oacc[r][0][e], oacc[r][1][e], oacc[r][2][e], oacc[r][3][e]);
                 }
             }
         }
