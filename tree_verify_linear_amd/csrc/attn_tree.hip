@@ -25,16 +25,18 @@
 //     lo (P to about 2^-22) to LDS in the PV A-operand layout (the score layout of S^T
 //     already is that layout, so no transpose).
 //   * PV waves (4): PV wave w owns output columns 64w .. 64w+63 of all rows.  It dequantises
-//     its columns of V into fp16 hi/lo (slot-major, the PV B operand) and accumulates
+//     its columns of V into fp16 hi/lo registers (the PV B operand) and accumulates
 //     O += P_hi V_hi + P_hi V_lo + P_lo V_hi (the dropped P_lo V_lo is ~2^-22 relative), one
 //     tile behind the scores.
 //   * Each SIMD carries one wave of each role, and the phases pair them up: while the scoring
-//     wave issues the QK^T matrix instructions the PV wave dequantises V, and while the
-//     scoring wave runs the softmax the PV wave issues the PV matrix instructions.
+//     wave issues the QK^T matrix instructions the PV wave dequantises V and issues the first
+//     PV_EARLY row tiles of PV, and while the scoring wave runs the softmax the PV wave issues
+//     the remaining row tiles.
 //   * Each split writes unnormalised O, its running max and sum; a combine pass rescales and
 //     sums the splits.  With a single split the kernel normalises and writes the output.
 #include <cfloat>
 #include <cmath>
+#include <type_traits>
 
 #include "tv_internal.h"
 
@@ -53,6 +55,7 @@ constexpr int THREADS = 64 * WAVES;
 constexpr int RTMAX = 9;                     // row tiles per row block
 constexpr int OWNMAX = (RTMAX + 3) / 4;      // softmax tiles owned per scoring wave
 constexpr int ROWS_PER_BLOCK = RTMAX * 16;   // 144
+constexpr int PV_EARLY = 2;                  // PV row tiles issued in phase 1 (the rest in phase 2)
 constexpr int MAXROW = 8 * 34;               // bytes of one slot's row (Q8_0, the larger)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -396,77 +399,99 @@ __global__ __launch_bounds__(THREADS, 1) void attn_kernel(AttnLaunch L) {
             if (k < ntiles) {
                 const int t0 = s0 + k * TS;
                 const int bufk = k & 1;
-                auto softmax = [&](int j) {
-                    const int r = wl + 4 * j;
-                    f32x4 pa_[3], pb_[3];
+                // The owned row tiles (two, three for wave 0) go through each step together, so
+                // their independent chains interleave.
+                auto softmax = [&](auto njc) {
+                    constexpr int NJ = decltype(njc)::value;
+                    float x[NJ][8];        // unscaled scores
 #pragma unroll
-                    for (int src = 0; src < 3; ++src) {
-                        pa_[src] = sm.spart[r][src][0][lane];
-                        pb_[src] = sm.spart[r][src][1][lane];
+                    for (int j = 0; j < NJ; ++j) {
+                        const int r = wl + 4 * j;
+                        f32x4 pa_[3], pb_[3];
+#pragma unroll
+                        for (int src = 0; src < 3; ++src) {
+                            pa_[src] = sm.spart[r][src][0][lane];
+                            pb_[src] = sm.spart[r][src][1][lane];
+                        }
+                        const f32x4 sa = (own[j][0] + pa_[0]) + (pa_[1] + pa_[2]);
+                        const f32x4 sb = (own[j][1] + pb_[0]) + (pb_[1] + pb_[2]);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            x[j][e] = sa[e];
+                            x[j][4 + e] = sb[e];
+                        }
                     }
-                    const f32x4 sa = (own[j][0] + pa_[0]) + (pa_[1] + pa_[2]);
-                    const f32x4 sb = (own[j][1] + pb_[0]) + (pb_[1] + pb_[2]);
-                    float x[8];        // unscaled scores
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        x[e] = sa[e];
-                        x[4 + e] = sb[e];
-                    }
-                    const bool fast = t0 + TS <= (T < s1 ? T : s1) && t0 >= rlo_max[j];
-                    if (!fast) {
+                    for (int j = 0; j < NJ; ++j) {
+                        const bool fast = t0 + TS <= (T < s1 ? T : s1) && t0 >= rlo_max[j];
+                        if (!fast) {
 #pragma unroll
-                        for (int e = 0; e < 8; ++e) {
-                            const int slot = t0 + (e < 4 ? 4 * g4 + e : 16 + 4 * g4 + (e - 4));
-                            bool vis = rs[j].on && slot < s1;
-                            if (slot < T) {
-                                vis = vis && slot >= rs[j].rlo;
-                            } else {
-                                const int jn = slot - T;     // < n <= 64 whenever slot < s1
-                                vis = vis && jn < TV_MAX_NODES && ((rs[j].anc >> (jn & 63)) & 1ull) &&
-                                      (W == 0 || rs[j].dep - sm.dep[jn & 63] < W);
+                            for (int e = 0; e < 8; ++e) {
+                                const int slot = t0 + (e < 4 ? 4 * g4 + e : 16 + 4 * g4 + (e - 4));
+                                bool vis = rs[j].on && slot < s1;
+                                if (slot < T) {
+                                    vis = vis && slot >= rs[j].rlo;
+                                } else {
+                                    const int jn = slot - T;     // < n <= 64 whenever slot < s1
+                                    vis = vis && jn < TV_MAX_NODES && ((rs[j].anc >> (jn & 63)) & 1ull) &&
+                                          (W == 0 || rs[j].dep - sm.dep[jn & 63] < W);
+                                }
+                                x[j][e] = vis ? x[j][e] : -INFINITY;
                             }
-                            x[e] = vis ? x[e] : -INFINITY;
                         }
                     }
                     // (rows past the tree are not masked on unmasked tiles: their Q is zero,
                     // so their weights stay finite, and nothing reads their results)
-                    float mt = x[0];
+                    float mt[NJ];
 #pragma unroll
-                    for (int e = 1; e < 8; ++e) mt = fmaxf(mt, x[e]);
-                    // the row's 32 slots sit in the four lane groups: max over l, l^16, l^32
-                    const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(mt), __float_as_uint(mt), false, false);
-                    mt = fmaxf(__uint_as_float(s16[0]), __uint_as_float(s16[1]));
-                    const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt), false, false);
-                    mt = fmaxf(__uint_as_float(s32[0]), __uint_as_float(s32[1])) * sl2;
-                    // Lazy rescaling: P is taken against a reference max that moves only when
-                    // the row max grows by more than 2^8 (so P <= 256); alpha is 1 otherwise.
-                    const bool grow = mt > rs[j].m + 8.f;
-                    const bool anyg = __builtin_amdgcn_ballot_w64(grow) != 0;
-                    const float mnew = grow ? mt : rs[j].m;
-                    const float al = rs[j].m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(rs[j].m - mnew);
-                    rs[j].m = mnew;
-                    const float m = mnew == -INFINITY ? 0.f : mnew;      // then every x is -inf
-                    // P = hi + lo in fp16 (lo is the rounding residual of hi), so P enters
-                    // the PV products to about 2^-22 relative
-                    float pe[8];
-                    float ps = 0.f;
+                    for (int j = 0; j < NJ; ++j) {
+                        mt[j] = x[j][0];
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        pe[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[e], sl2, -m));
-                        ps += pe[e];
+                        for (int e = 1; e < 8; ++e) mt[j] = fmaxf(mt[j], x[j][e]);
                     }
-                    uint32_t ph[4], pl[4];
+                    // the row's 32 slots sit in the four lane groups: max over l, l^16, l^32
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) split_p2(pe[2 * e], pe[2 * e + 1], ph[e], pl[e]);
-                    rs[j].l = rs[j].l * al + ps;
-                    *reinterpret_cast<uint4*>(&sm.pbuf[bufk][r][lane]) = make_uint4(ph[0], ph[1], ph[2], ph[3]);
-                    *reinterpret_cast<uint4*>(&sm.pbuf_lo[bufk][r][lane]) = make_uint4(pl[0], pl[1], pl[2], pl[3]);
-                    if (g4 == 0) sm.alpha[bufk][r][l16] = al;          // row l16's factor
-                    if (lane == 0) sm.grow[bufk][r] = anyg;
+                    for (int j = 0; j < NJ; ++j) {
+                        const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(mt[j]), __float_as_uint(mt[j]), false, false);
+                        mt[j] = fmaxf(__uint_as_float(s16[0]), __uint_as_float(s16[1]));
+                    }
+#pragma unroll
+                    for (int j = 0; j < NJ; ++j) {
+                        const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt[j]), __float_as_uint(mt[j]), false, false);
+                        mt[j] = fmaxf(__uint_as_float(s32[0]), __uint_as_float(s32[1])) * sl2;
+                    }
+#pragma unroll
+                    for (int j = 0; j < NJ; ++j) {
+                        const int r = wl + 4 * j;
+                        // Lazy rescaling: P is taken against a reference max that moves only when
+                        // the row max grows by more than 2^8 (so P <= 256); alpha is 1 otherwise.
+                        const bool grow = mt[j] > rs[j].m + 8.f;
+                        const bool anyg = __builtin_amdgcn_ballot_w64(grow) != 0;
+                        const float mnew = grow ? mt[j] : rs[j].m;
+                        const float al = rs[j].m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(rs[j].m - mnew);
+                        rs[j].m = mnew;
+                        const float m = mnew == -INFINITY ? 0.f : mnew;      // then every x is -inf
+                        // P = hi + lo in fp16 (lo is the rounding residual of hi), so P enters
+                        // the PV products to about 2^-22 relative
+                        float pe[8];
+                        float ps = 0.f;
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            pe[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[j][e], sl2, -m));
+                            ps += pe[e];
+                        }
+                        uint32_t ph[4], pl[4];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) split_p2(pe[2 * e], pe[2 * e + 1], ph[e], pl[e]);
+                        rs[j].l = rs[j].l * al + ps;
+                        *reinterpret_cast<uint4*>(&sm.pbuf[bufk][r][lane]) = make_uint4(ph[0], ph[1], ph[2], ph[3]);
+                        *reinterpret_cast<uint4*>(&sm.pbuf_lo[bufk][r][lane]) = make_uint4(pl[0], pl[1], pl[2], pl[3]);
+                        if (g4 == 0) sm.alpha[bufk][r][l16] = al;          // row l16's factor
+                        if (lane == 0) sm.grow[bufk][r] = anyg;
+                    }
                 };
-                softmax(0);
-                softmax(1);
-                if (wl + 8 < RTMAX) softmax(2);                       // row tile 8: wave 0
+                if (wl == 0) softmax(std::integral_constant<int, OWNMAX>{});    // row tile 8 too
+                else softmax(std::integral_constant<int, 2>{});
             }
             __syncthreads();
         }
@@ -496,6 +521,17 @@ __global__ __launch_bounds__(THREADS, 1) void attn_kernel(AttnLaunch L) {
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) oacc[r][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+        // O += P V for one row tile of tile k-1 (P hi/lo from LDS, V operands in registers)
+        auto pv_rowtile = [&](int r, int bufp, const f16x8 (&bh)[4], const f16x8 (&bl)[4]) {
+            const f16x8 pa = sm.pbuf[bufp][r][lane];
+            const f16x8 pl = sm.pbuf_lo[bufp][r][lane];
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) oacc[r][jj] = mfma_f16(pa, bh[jj], oacc[r][jj]);
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) oacc[r][jj] = mfma_f16(pa, bl[jj], oacc[r][jj]);
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) oacc[r][jj] = mfma_f16(pl, bh[jj], oacc[r][jj]);
+        };
         for (int k = 0; k <= ntiles; ++k) {
             // phase 1: this wave's 64 columns of V for tile k-1 as the PV B operands, fp16 hi/lo,
             // straight from the raw rows into registers.  Column tile jj, lane (g4, l16) holds
@@ -534,11 +570,8 @@ __global__ __launch_bounds__(THREADS, 1) void attn_kernel(AttnLaunch L) {
                         bl[c][2 * pp + 1] = l[1];
                     }
                 }
-            }
-            __syncthreads();
-            // phase 2: stage the next tile; O += P V for tile k-1
-            stage(k);
-            if (k >= 1) {
+                // O rescale for tile k-1, then its first PV_EARLY row tiles: the matrix cores
+                // are shared with the scoring waves' QK^T work in this phase
                 const int bufp = (k - 1) & 1;
                 int anyg = 0;
 #pragma unroll
@@ -552,18 +585,16 @@ __global__ __launch_bounds__(THREADS, 1) void attn_kernel(AttnLaunch L) {
                         for (int jj = 0; jj < 4; ++jj) oacc[r][jj] *= al;
                     }
                 }
-                // P hi/lo one row tile at a time against the V operands held since phase 1
 #pragma unroll
-                for (int r = 0; r < RTMAX; ++r) {
-                    const f16x8 pa = sm.pbuf[bufp][r][lane];
-                    const f16x8 pl = sm.pbuf_lo[bufp][r][lane];
+                for (int r = 0; r < PV_EARLY; ++r) pv_rowtile(r, bufp, bh, bl);
+            }
+            __syncthreads();
+            // phase 2: stage the next tile; O += P V for tile k-1
+            stage(k);
+            if (k >= 1) {
+                const int bufp = (k - 1) & 1;
 #pragma unroll
-                    for (int jj = 0; jj < 4; ++jj) oacc[r][jj] = mfma_f16(pa, bh[jj], oacc[r][jj]);
-#pragma unroll
-                    for (int jj = 0; jj < 4; ++jj) oacc[r][jj] = mfma_f16(pa, bl[jj], oacc[r][jj]);
-#pragma unroll
-                    for (int jj = 0; jj < 4; ++jj) oacc[r][jj] = mfma_f16(pl, bh[jj], oacc[r][jj]);
-                }
+                for (int r = PV_EARLY; r < RTMAX; ++r) pv_rowtile(r, bufp, bh, bl);
             }
             __syncthreads();
         }
