@@ -360,16 +360,21 @@ __global__ __launch_bounds__(THREADS, 1) void attn_kernel(AttnLaunch L) {
         for (int k = 0; k <= ntiles; ++k) {
             // phase 1: partial scores of tile k
             if (k < ntiles) {
+                // both slot halves' K operands first, so the second half's LDS reads and
+                // dequantisation overlap the first half's matrix work
+                f16x8 kh[2][2], kl[2][2];
 #pragma unroll
                 for (int st = 0; st < 2; ++st) {
-                    f16x8 ah[2], al[2];
                     const uint8_t* krow = &sm.rawk[(16 * st + l16) * KF::ROW];
-                    {
-                        const f16x8 d0 = block_scale(krow + 2 * wl * KF::BLK);
-                        const f16x8 d1 = block_scale(krow + (2 * wl + 1) * KF::BLK);
-                        split_exact(block_ints8<KT, false>(krow, 2 * wl, g4), d0, ah[0], al[0]);
-                        split_exact(block_ints8<KT, true>(krow, 2 * wl + 1, g4), d1, ah[1], al[1]);
-                    }
+                    const f16x8 d0 = block_scale(krow + 2 * wl * KF::BLK);
+                    const f16x8 d1 = block_scale(krow + (2 * wl + 1) * KF::BLK);
+                    split_exact(block_ints8<KT, false>(krow, 2 * wl, g4), d0, kh[st][0], kl[st][0]);
+                    split_exact(block_ints8<KT, true>(krow, 2 * wl + 1, g4), d1, kh[st][1], kl[st][1]);
+                }
+#pragma unroll
+                for (int st = 0; st < 2; ++st) {
+                    const f16x8 (&ah)[2] = kh[st];
+                    const f16x8 (&al)[2] = kl[st];
 #pragma unroll
                     for (int i = 0; i < RTMAX; ++i) {
                         const int r = rtile(i);
