@@ -239,22 +239,28 @@ __device__ __forceinline__ void load_unit(UnitIn<DK, NT, BF16IN>& in, const LinV
     }
 }
 
-// Shared memory of one verify wave.
+// Shared memory of one verify wave, kept at or under 20 KiB for trees of up to 24 nodes so
+// that eight units stay resident per CU (the LDS is allocated in 512-byte granules).
 template <int NT, bool BF16IN>
 struct VerifySmem {
     static constexpr int NMAX = NT * 8;
     static constexpr int GT = (NMAX + 15) / 16;
-    static constexpr int CST = 68;                  // padded row stride of Cs (floats)
-    static constexpr int GST = NT * 16 + 4;         // padded row stride of Gm
-    __align__(16) float Cs[NT * 16][CST];          // Cs[c][j] = (S0^T x_c)[j0 + j]; rows n.. become outputs
+    static constexpr int GC = NT * 16;              // Gm columns: x_0 .. x_{2N-1} and padding
+    static constexpr int GST = GC + 4;              // padded row stride of Gm
+    // Cs[c][j] = (S0^T x_c)[j0 + j], rows of 64 floats with the float4 slots of row c permuted
+    // by c mod 16 (see cs_at), so the matrix-core stores of 16 rows spread over the banks.
+    // Rows N.. become the outputs, rows 0.. the deltas once the walks have read them.
+    __align__(16) float Cs[NT * 16][64];
     // Three lifetimes in one place (one wave reads each before the next is written):
     union {
-        float Gm[GT * 16][GST];                     // Gm[m][c] = k_m . x_c, until the coefficients are built
+        // Gm[m][c] = k_m . x_c, until the coefficients are built; column GC holds node m's
+        // decay and column GC + 1 its parent
+        float Gm[NMAX][GST];
         struct {
             __align__(16) float Pu[NMAX][NMAX];    // Pu[i][m], zero unless m is a strict ancestor of i
             __align__(16) float Pw[NMAX][NMAX];    //   (both read by the walks)
+            float cv[NMAX], ca[NMAX], cb[NMAX], cd[NMAX];   // per-node scalars of the walks
         };
-        __align__(16) float Ds[NMAX][64];           // then delta_i per value channel
         struct {                                    // before all of those: a pending commit
             __align__(16) float pk[4][128];         //   key rows of four accepted nodes
             __align__(16) float pd[4][64];          //   c_l * delta_l for the unit's channels
@@ -263,10 +269,13 @@ struct VerifySmem {
         };
     };
     __align__(16) uint8_t Vs[NMAX * 64 * (BF16IN ? 2 : 4)];   // v rows of the unit, [node][channel]
-    float cv[NMAX], ca[NMAX], cb[NMAX], cd[NMAX];   // per-node scalars of the walk
-    float gl[NMAX];
-    int par[NMAX];
 };
+
+// Element (row, col) of Cs; col % 4 == 0 addresses a whole float4 slot.
+template <typename SM>
+__device__ __forceinline__ float* cs_at(SM& sm, int row, int col) {
+    return &sm.Cs[row][col ^ ((row & 15) << 2)];
+}
 
 template <int DK, int NT, bool BF16IN>
 __device__ __forceinline__ int compute_unit(const UnitIn<DK, NT, BF16IN>& in, VerifySmem<NT, BF16IN>& sm,
@@ -291,9 +300,10 @@ __device__ __forceinline__ int compute_unit(const UnitIn<DK, NT, BF16IN>& in, Ve
     }
 
     // 1. tree metadata and v rows into LDS; the key Gram matrix.
+    constexpr int GC = VerifySmem<NT, BF16IN>::GC;
     if (lane < NMAX) {
-        sm.par[lane] = pme;
-        sm.gl[lane] = gme;
+        sm.Gm[lane][GC] = gme;
+        sm.Gm[lane][GC + 1] = __int_as_float(pme);
     }
     {
         const int epl = 16 / U::ESZ, lpr = CW / epl, rpi = 64 / lpr;
@@ -317,8 +327,10 @@ __device__ __forceinline__ int compute_unit(const UnitIn<DK, NT, BF16IN>& in, Ve
                     acc = mfma16x16x32(in.bo[gt][ks], in.bh[nt][ks], acc);
                 }
             }
+            if (gt * 16 + 4 * g4 < NMAX) {          // rows past the largest tree are not kept
 #pragma unroll
-            for (int e = 0; e < 4; ++e) sm.Gm[gt * 16 + 4 * g4 + e][nt * 16 + l16] = acc[e];
+                for (int e = 0; e < 4; ++e) sm.Gm[gt * 16 + 4 * g4 + e][nt * 16 + l16] = acc[e];
+            }
         }
     }
 
@@ -338,7 +350,7 @@ __device__ __forceinline__ int compute_unit(const UnitIn<DK, NT, BF16IN>& in, Ve
                 acc = mfma16x16x32(al[ks], in.bh[nt][ks], acc);
                 if constexpr (!BF16IN) acc = mfma16x16x32(ah[ks], in.bo[nt][ks], acc);
             }
-            *reinterpret_cast<float4*>(&sm.Cs[nt * 16 + l16][mt * 16 + 4 * g4]) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+            *reinterpret_cast<float4*>(cs_at(sm, nt * 16 + l16, mt * 16 + 4 * g4)) = make_float4(acc[0], acc[1], acc[2], acc[3]);
         }
     }
     __syncthreads();
@@ -347,7 +359,7 @@ __device__ __forceinline__ int compute_unit(const UnitIn<DK, NT, BF16IN>& in, Ve
     //    of LDS so the walk reads four of them per broadcast load.
     if (lane < NMAX) {
         uint64_t am = 0;
-        for (int m = pme; m >= 0; m = sm.par[m]) am |= 1ull << m;
+        for (int m = pme; m >= 0; m = __float_as_int(sm.Gm[m][GC + 1])) am |= 1ull << m;
         const int li = real ? lane : 0;
         const float cdv = a.scale * sm.Gm[li][N + li];   // before the rows below replace Gm
         float run = 1.f;                            // product of g over ancestors below m
@@ -357,7 +369,7 @@ __device__ __forceinline__ int compute_unit(const UnitIn<DK, NT, BF16IN>& in, Ve
             const bool an = (am >> m) & 1ull;
             pu[m] = an ? -bme * gme * run * sm.Gm[m][li] : 0.f;
             pw[m] = an ? a.scale * gme * run * sm.Gm[m][N + li] : 0.f;
-            run = an ? run * sm.gl[m < n ? m : 0] : run;
+            run = an ? run * sm.Gm[m < n ? m : 0][GC] : run;
         }
 #pragma unroll
         for (int m = 0; m < NMAX; m += 4) {
@@ -381,7 +393,7 @@ __device__ __forceinline__ int compute_unit(const UnitIn<DK, NT, BF16IN>& in, Ve
     float dr[NMAX];
 #pragma unroll
     for (int i = 0; i < NMAX; ++i) {
-        float d0 = sm.cv[i] * v_of(i) - sm.ca[i] * sm.Cs[i][lane], d1 = 0.f;
+        float d0 = sm.cv[i] * v_of(i) - sm.ca[i] * *cs_at(sm, i, lane), d1 = 0.f;
 #pragma unroll
         for (int m = 0; m + 1 < i; m += 2) {
             d0 = fmaf(sm.Pu[i][m], dr[m], d0);
@@ -395,7 +407,7 @@ __device__ __forceinline__ int compute_unit(const UnitIn<DK, NT, BF16IN>& in, Ve
     float orow[NMAX];
 #pragma unroll
     for (int i = 0; i < NMAX; ++i) {
-        float o0 = fmaf(sm.cb[i], sm.Cs[N + i][lane], sm.cd[i] * dr[i]), o1 = 0.f;
+        float o0 = fmaf(sm.cb[i], *cs_at(sm, N + i, lane), sm.cd[i] * dr[i]), o1 = 0.f;
 #pragma unroll
         for (int m = 0; m + 1 < i; m += 2) {
             o0 = fmaf(sm.Pw[i][m], dr[m], o0);
@@ -404,18 +416,19 @@ __device__ __forceinline__ int compute_unit(const UnitIn<DK, NT, BF16IN>& in, Ve
         if (i & 1) o0 = fmaf(sm.Pw[i][i - 1], dr[i - 1], o0);
         orow[i] = o0 + o1;
     }
-    // no LDS writes inside the walks (they would order every later read after them)
+    // No LDS writes inside the walks (they would order every later read after them).  Both
+    // walks are done with the rows: row i < n now holds delta_i, row N + i holds o_i (the
+    // outputs go second, so they win where a padding row i >= N meets output row N + i - N).
 #pragma unroll
-    for (int i = 0; i < NMAX; ++i) {
-        sm.Ds[i][lane] = dr[i];
-        sm.Cs[N + i][lane] = orow[i];               // b_i is consumed: row N + i now holds o_i
-    }
+    for (int i = 0; i < NMAX; ++i) *cs_at(sm, i, lane) = dr[i];
+#pragma unroll
+    for (int i = 0; i < NMAX; ++i) *cs_at(sm, N + i, lane) = orow[i];
     __syncthreads();
 
     return n;
 }
 
-// The unit's deltas (Ds rows 0..n-1) and outputs (Cs rows N..N+n-1): 16-byte stores, four
+// The unit's deltas (Cs rows 0..n-1) and outputs (Cs rows N..N+n-1): 16-byte stores, four
 // rows per instruction.  Issued after the next unit's inputs have landed, so the wait for
 // those inputs never includes these stores.
 template <int NT, bool BF16IN>
@@ -431,7 +444,7 @@ __device__ __forceinline__ void store_unit(VerifySmem<NT, BF16IN>& sm, const Lin
         const int i = isd ? r : r - n;
         if (c4 < CW) {
             float* dst = (isd ? a.cap_delta : a.out) + rowbase + i * ostep + c4;
-            *reinterpret_cast<float4*>(dst) = *reinterpret_cast<const float4*>(isd ? &sm.Ds[i][c4] : &sm.Cs[N + i][c4]);
+            *reinterpret_cast<float4*>(dst) = *reinterpret_cast<const float4*>(cs_at(sm, isd ? i : N + i, c4));
         }
     }
     __syncthreads();                                // LDS is reused by the next unit
