@@ -25,7 +25,10 @@ times, after the step and outside ``value``, the tree convolution and its window
 the greedy acceptance of the step's trees (vocabulary 151936, bf16 logits) and the
 compaction of the attention cache to the accepted paths.  ``workload2`` times the step's
 three calls on the second workload (budgets 8, 16 and 40 with a Q8_0 K cache and a Q4_0
-V cache).  ``cpu_baseline`` times the fp64 CPU oracle over whole sequences of the same
+V cache).  ``long_context`` times one step of a long-context model at one sequence (16
+linear and 4 attention layers, 131072 committed Q4_0 slots, windows 0 and 2048); its
+full-window attention is the matrix-core-bound case and also reports its fraction of the
+fp16 matrix peak.  ``cpu_baseline`` times the fp64 CPU oracle over whole sequences of the same
 workload for about ten seconds.
 
 Warm-up runs at least --warmup steps and keeps going until --min-warmup-s (0.3 s) have
@@ -74,6 +77,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle timing")
     ap.add_argument("--no-workload2", action="store_true",
                     help="skip the second workload (budgets 8/16/40, Q8_0 K + Q4_0 V)")
+    ap.add_argument("--no-long-context", action="store_true",
+                    help="skip the long-context model step (131072 committed Q4_0 slots, 16 linear + 4 attention layers)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU oracle sample budget")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one device-to-device copy of this many MiB (counter calibration)")
@@ -513,6 +518,119 @@ def time_workload2(args, tvl, torch, dev, B):
     return res
 
 
+MFMA_F16_PEAK_TFLOPS = 2500.0   # MI355X dense fp16/bf16 matrix peak, vendor figure
+
+
+def time_long_context(args, tvl, torch, dev):
+    """One decoding step of a long-context model at one sequence: four groups of four linear
+    layers (27B widths, fused commit + verify) followed by one attention layer over 131072
+    committed slots in Q4_0 (K and V), with one shared 22-node tree; full attention
+    (window 0) and window 2048.  Two distinct attention layers are generated (302 MB of
+    cache, above the 256 MB last-level cache) and alternate between the four attention
+    positions.  Not part of ``value``."""
+    import dataclasses
+    import numpy as np
+    from workloads import workload_long_context
+
+    t0 = time.perf_counter()
+    W = workload_long_context(window=0, n_lin=16, n_attn=2)
+    print(f"# generated the long-context layers in {time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
+
+    def bits(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    def i32(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+
+    lins = []
+    for L in W.lin:
+        d = dict(q=bits(L.q), k=bits(L.k), v=bits(L.v), g=bits(L.g), beta=bits(L.beta),
+                 state=torch.from_numpy(L.state).to(dev), parent=i32(L.parent), n_nodes=i32(L.n_nodes),
+                 path=i32(L.path), path_len=i32(L.path_len))
+        d["out"] = torch.empty(tuple(L.v.shape), dtype=torch.float32, device=dev)
+        d["caps"] = [torch.empty_like(d["out"]), torch.empty_like(d["out"])]
+        lins.append(d)
+    attns = []
+    for A in W.attn:
+        B, N, Hq, D = A.q.shape
+        Hkv, Tcap = A.k_cache.shape[1], A.k_cache.shape[2]
+        ws_bytes = max(max(tvl.attn_tree_workspace_bytes(B, N, Hq, Hkv, D, Tcap, w) for w in (0, 2048)), 256)
+        attns.append(dict(q=bits(A.q), kc=torch.from_numpy(A.k_cache).to(dev), vc=torch.from_numpy(A.v_cache).to(dev),
+                          n_past=i32(A.n_past), parent=i32(A.parent), n_nodes=i32(A.n_nodes),
+                          out=torch.empty((B, N, Hq, D), dtype=torch.float32, device=dev),
+                          lse=torch.empty((B, N, Hq), dtype=torch.float32, device=dev),
+                          ws=torch.empty(ws_bytes, dtype=torch.uint8, device=dev)))
+    order = []
+    for a in range(4):
+        order += [("lin", 4 * a + j) for j in range(4)] + [("attn", a % 2)]
+    # the first visit of each linear layer has no previous path: a plain verify fills its deltas
+    for i, d in enumerate(lins):
+        L = W.lin[i]
+        tvl.lin_tree_verify(d["q"], d["k"], d["v"], d["g"], d["beta"], d["state"], d["parent"], d["n_nodes"],
+                            L.scale, out=d["out"], cap_delta=d["caps"][0])
+    torch.cuda.synchronize()
+    visit = [1]
+
+    def call(kind, idx, window):
+        if kind == "lin":
+            d, L = lins[idx], W.lin[idx]
+            v = visit[0]
+            tvl.lin_tree_verify_commit(d["q"], d["k"], d["v"], d["g"], d["beta"], d["state"], d["parent"],
+                                       d["n_nodes"], L.scale, d["path"], d["path_len"], d["k"], d["g"],
+                                       d["caps"][(v + 1) % 2], out=d["out"], cap_delta=d["caps"][v % 2])
+        else:
+            x, A = attns[idx], W.attn[idx]
+            tvl.attn_tree_verify(x["q"], x["kc"], x["vc"], A.k_type, A.v_type, x["n_past"], x["parent"],
+                                 x["n_nodes"], window, A.scale, out=x["out"], lse=x["lse"], workspace=x["ws"])
+
+    res = {"workload": "one sequence, 22-node DDTree, [4 linear layers (Hk16/Hv48 dk=dv=128, fused commit + "
+                       "verify), 1 attention layer (Hq24/Hkv4 D256, K and V Q4_0, 131072 committed slots)] x 4"}
+    lin_b = sum(lin_verify_commit_bytes(L) for L in W.lin) / len(W.lin)
+    nodes = int(W.lin[0].n_nodes.sum())
+    for window in (0, 2048):
+        steps = max(args.steps, 10)
+        w0 = time.perf_counter()
+        while time.perf_counter() - w0 < 0.2:
+            for kind, idx in order:
+                call(kind, idx, window)
+            visit[0] += 1
+            torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(order) + 1)] for _ in range(steps)]
+        for k in range(steps):
+            evs[k][0].record()
+            for j, (kind, idx) in enumerate(order):
+                call(kind, idx, window)
+                evs[k][j + 1].record()
+            visit[0] += 1
+        torch.cuda.synchronize()
+        lin_ms, attn_ms = [], []
+        for e in evs:
+            for j, (kind, _) in enumerate(order):
+                (lin_ms if kind == "lin" else attn_ms).append(e[j].elapsed_time(e[j + 1]))
+        step_ms = sum(e[0].elapsed_time(e[-1]) for e in evs) / steps
+        la = sum(lin_ms) / len(lin_ms)
+        aa = sum(attn_ms) / len(attn_ms)
+        Aw = [dataclasses.replace(A, window=window) for A in W.attn]
+        ab = sum(attn_bytes(A) for A in Aw) / len(Aw)
+        af = sum(attn_flops(A) for A in Aw) / len(Aw)
+        a_gbs = ab / (aa * 1e-3) / 1e9
+        a_tfs = af / (aa * 1e-3) / 1e12
+        l_gbs = lin_b / (la * 1e-3) / 1e9
+        res[f"window{window}"] = {
+            "ms_per_step": round(step_ms, 4),
+            "node_layers_per_s": round(20 * nodes / (step_ms * 1e-3), 1),
+            "lin_tree_verify_commit": {"mean_us": round(la * 1e3, 2), "algorithmic_MB": round(lin_b / 1e6, 3),
+                                       "GB_per_s": round(l_gbs, 1), "frac_hbm_peak": round(l_gbs / HBM_PEAK_GBS, 4)},
+            "attn_tree_verify": {"mean_us": round(aa * 1e3, 2), "algorithmic_MB": round(ab / 1e6, 3),
+                                 "GB_per_s": round(a_gbs, 1), "frac_hbm_peak": round(a_gbs / HBM_PEAK_GBS, 4),
+                                 "TFLOP_per_s": round(a_tfs, 1),
+                                 "frac_mfma_f16_peak": round(a_tfs / MFMA_F16_PEAK_TFLOPS, 4)},
+        }
+        print(f"# timed the long-context step, window {window}", file=sys.stderr, flush=True)
+    del lins, attns
+    return res
+
+
 # ----------------------------------------------------------------------------- main
 
 def main():
@@ -630,6 +748,7 @@ def main():
     unfused = None if args.no_workload2 else time_unfused_linear(args, tvl, torch, pool, sets)
     next_kernels = time_next_rows(args, tvl, torch, dev, pool[0], A0, B)
     workload2 = None if args.no_workload2 else time_workload2(args, tvl, torch, dev, B)
+    long_context = None if args.no_long_context else time_long_context(args, tvl, torch, dev)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -656,6 +775,7 @@ def main():
         "linear_unfused": unfused,
         "next_kernels": next_kernels,
         "workload2": workload2,
+        "long_context": long_context,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
