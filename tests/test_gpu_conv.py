@@ -70,6 +70,14 @@ def test_conv_widths_deep_and_shallow(K):
     check(gen_conv(91, parents, paths, 520, K, "bf16"), "silu", f"K{K}")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_conv_ragged_channel_chunk(dtype):
+    """3080 channels: one full 2048-channel workgroup, then one whose first 1024 channels are
+    all present and whose second half holds only 8 (a thread's two channel quads split)."""
+    parents, paths = trees_for(92, 3, "ddtree")
+    check(gen_conv(92, parents, paths, 3080, 4, dtype), "silu", f"C3080 {dtype}")
+
+
 def test_conv_deterministic():
     X = workload_conv(4, C=2048)
     d = to_dev(X)

@@ -7,10 +7,12 @@
 //   y_i[c] = sum_{k<K} w[c][k] * u_{i,k}[c],  u_{i,K-1} = x_i, u_{i,K-2} = x_parent(i), ...,
 //   above the root the committed window (oldest first); optionally SiLU.
 //
-// Both kernels are bandwidth work: one thread handles 8 consecutive channels (one 16-byte
-// load of bf16 inputs), the weights of those channels stay in registers, and every input row
-// a node's window needs is read with coalesced vector loads (a parent's row is usually still
-// in L2 from the parent's own thread).
+// Both kernels are bandwidth work: one thread handles 8 channels, four at 4t .. 4t+3 and four
+// at 1024 + 4t .. 1024 + 4t + 3 of its workgroup's 2048, so every load and store instruction
+// of a wave covers one contiguous run of memory (whole 128-byte lines of the fp32 outputs).
+// The weights of those channels stay in registers, and every input row a node's window needs
+// is read with coalesced vector loads (a parent's row is usually still in L2 from the
+// parent's own thread).
 #include "tv_internal.h"
 
 namespace tv {
@@ -33,33 +35,44 @@ struct ConvArgs {
     const int32_t* path_len;
 };
 
+constexpr int HALF = CONV_THREADS * CPT / 2;    // offset of a thread's second four channels
+
+// A thread's channels: c0 .. c0+3 and c0+HALF .. c0+HALF+3 (c0 = chunk base + 4t), present
+// as whole halves (C is a multiple of 8).  Absent halves read as zero and are not stored.
 template <bool BF16>
-__device__ __forceinline__ void load8(const void* base, size_t elem, float (&u)[CPT]) {
+__device__ __forceinline__ void load8(const void* base, size_t elem, bool okb, float (&u)[CPT]) {
     if constexpr (BF16) {
-        const uint4 v = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + elem);
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        const uint16_t* p = static_cast<const uint16_t*>(base) + elem;
+        const uint2 a = *reinterpret_cast<const uint2*>(p);
+        uint2 b = make_uint2(0u, 0u);
+        if (okb) b = *reinterpret_cast<const uint2*>(p + HALF);
+        const uint32_t w[4] = {a.x, a.y, b.x, b.y};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             u[2 * e] = __uint_as_float(w[e] << 16);
             u[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
         }
     } else {
-        const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + elem);
-        const float4 a = p[0], b = p[1];
+        const float* p = static_cast<const float*>(base) + elem;
+        const float4 a = *reinterpret_cast<const float4*>(p);
+        float4 b = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (okb) b = *reinterpret_cast<const float4*>(p + HALF);
         u[0] = a.x; u[1] = a.y; u[2] = a.z; u[3] = a.w;
         u[4] = b.x; u[5] = b.y; u[6] = b.z; u[7] = b.w;
     }
 }
 
-__device__ __forceinline__ void load8f(const float* p, float (&u)[CPT]) {
-    const float4 a = reinterpret_cast<const float4*>(p)[0], b = reinterpret_cast<const float4*>(p)[1];
+__device__ __forceinline__ void load8f(const float* p, bool okb, float (&u)[CPT]) {
+    const float4 a = *reinterpret_cast<const float4*>(p);
+    float4 b = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (okb) b = *reinterpret_cast<const float4*>(p + HALF);
     u[0] = a.x; u[1] = a.y; u[2] = a.z; u[3] = a.w;
     u[4] = b.x; u[5] = b.y; u[6] = b.z; u[7] = b.w;
 }
 
-__device__ __forceinline__ void store8f(float* p, const float (&u)[CPT]) {
-    reinterpret_cast<float4*>(p)[0] = make_float4(u[0], u[1], u[2], u[3]);
-    reinterpret_cast<float4*>(p)[1] = make_float4(u[4], u[5], u[6], u[7]);
+__device__ __forceinline__ void store8f(float* p, bool okb, const float (&u)[CPT]) {
+    *reinterpret_cast<float4*>(p) = make_float4(u[0], u[1], u[2], u[3]);
+    if (okb) *reinterpret_cast<float4*>(p + HALF) = make_float4(u[4], u[5], u[6], u[7]);
 }
 
 // SiLU with the hardware exp2 and reciprocal (each about 1 ulp).
@@ -84,15 +97,18 @@ __global__ __launch_bounds__(CONV_THREADS) void conv_tree_kernel(ConvArgs a) {
     // parents clamped to an earlier node, so every walk moves toward the root
     if (t < n) par[t] = t == 0 ? -1 : clampi(a.parent[static_cast<size_t>(b) * a.N + t], 0, t - 1);
     __syncthreads();
-    const int c0 = (chunk * CONV_THREADS + t) * CPT;
+    const int c0 = chunk * CONV_THREADS * CPT + 4 * t;
+    const bool okb = c0 + HALF < a.C;
     const int i0 = nb * NPW;
     if (c0 >= a.C || i0 >= n) return;
 
     float w[CPT][K];
 #pragma unroll
-    for (int e = 0; e < CPT; ++e)
+    for (int e = 0; e < CPT; ++e) {
+        const int ch = e < 4 ? c0 + e : (okb ? c0 + HALF + e - 4 : c0);
 #pragma unroll
-        for (int k = 0; k < K; ++k) w[e][k] = a.weight[static_cast<size_t>(c0 + e) * K + k];
+        for (int k = 0; k < K; ++k) w[e][k] = a.weight[static_cast<size_t>(ch) * K + k];
+    }
 
     const size_t xrow = static_cast<size_t>(b) * a.N;
     const float* win = a.state + static_cast<size_t>(b) * (K - 1) * a.C + c0;
@@ -109,11 +125,11 @@ __global__ __launch_bounds__(CONV_THREADS) void conv_tree_kernel(ConvArgs a) {
         for (int k = K - 1; k >= 0; --k) {
             float u[CPT];
             if (node >= 0) {
-                load8<BF16>(a.x, (xrow + node) * a.C + c0, u);
+                load8<BF16>(a.x, (xrow + node) * a.C + c0, okb, u);
                 node = node > 0 ? par[node] : -1;
             } else {
                 ++above;
-                load8f(win + static_cast<size_t>(K - 1 - above) * a.C, u);
+                load8f(win + static_cast<size_t>(K - 1 - above) * a.C, okb, u);
             }
 #pragma unroll
             for (int e = 0; e < CPT; ++e) acc[e] = __builtin_fmaf(w[e][k], u[e], acc[e]);
@@ -122,7 +138,7 @@ __global__ __launch_bounds__(CONV_THREADS) void conv_tree_kernel(ConvArgs a) {
 #pragma unroll
             for (int e = 0; e < CPT; ++e) acc[e] = silu(acc[e]);
         }
-        if (i0 + q < n) store8f(a.y + (xrow + i) * a.C + c0, acc);
+        if (i0 + q < n) store8f(a.y + (xrow + i) * a.C + c0, okb, acc);
     }
 }
 
@@ -133,7 +149,8 @@ __global__ __launch_bounds__(CONV_THREADS) void conv_commit_kernel(ConvArgs a) {
     const int chunks = (a.C + CONV_THREADS * CPT - 1) / (CONV_THREADS * CPT);
     const int wg = blockIdx.x;
     const int b = wg / chunks;
-    const int c0 = ((wg % chunks) * CONV_THREADS + threadIdx.x) * CPT;
+    const int c0 = (wg % chunks) * CONV_THREADS * CPT + 4 * static_cast<int>(threadIdx.x);
+    const bool okb = c0 + HALF < a.C;
     const int L = clampi(a.path_len[b], 0, a.Lmax);
     if (c0 >= a.C || L == 0) return;
     float* st = a.state_rw + static_cast<size_t>(b) * (K - 1) * a.C + c0;
@@ -142,14 +159,14 @@ __global__ __launch_bounds__(CONV_THREADS) void conv_commit_kernel(ConvArgs a) {
     for (int j = 0; j < K - 1; ++j) {
         const int s = j + L;          // position in (committed window, accepted inputs)
         if (s < K - 1) {
-            load8f(st + static_cast<size_t>(s) * a.C, rows[j]);
+            load8f(st + static_cast<size_t>(s) * a.C, okb, rows[j]);
         } else {
             const int node = clampi(a.path[static_cast<size_t>(b) * a.Lmax + (s - (K - 1))], 0, a.N - 1);
-            load8<BF16>(a.x, (static_cast<size_t>(b) * a.N + node) * a.C + c0, rows[j]);
+            load8<BF16>(a.x, (static_cast<size_t>(b) * a.N + node) * a.C + c0, okb, rows[j]);
         }
     }
 #pragma unroll
-    for (int j = 0; j < K - 1; ++j) store8f(st + static_cast<size_t>(j) * a.C, rows[j]);
+    for (int j = 0; j < K - 1; ++j) store8f(st + static_cast<size_t>(j) * a.C, okb, rows[j]);
 }
 
 template <bool BF16>
