@@ -25,7 +25,9 @@ times, after the step and outside ``value``, the tree convolution and its window
 the greedy acceptance of the step's trees (vocabulary 151936, bf16 logits) and the
 compaction of the attention cache to the accepted paths.  ``workload2`` times the step's
 three calls on the second workload (budgets 8, 16 and 40 with a Q8_0 K cache and a Q4_0
-V cache).  ``long_context`` times one step of a long-context model at one sequence (16
+V cache).  ``single_sequence`` times one
+sequence through each layer on its own (the tiny layer, the 27B-width linear and attention
+layers) as HIP-graph replays.  ``long_context`` times one step of a long-context model at one sequence (16
 linear and 4 attention layers, 131072 committed Q4_0 slots, windows 0 and 2048); its
 full-window attention is the matrix-core-bound case and also reports its fraction of the
 fp16 matrix peak.  ``cpu_baseline`` times the fp64 CPU oracle over whole sequences of the same
@@ -77,6 +79,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle timing")
     ap.add_argument("--no-workload2", action="store_true",
                     help="skip the second workload (budgets 8/16/40, Q8_0 K + Q4_0 V)")
+    ap.add_argument("--no-single-sequence", action="store_true",
+                    help="skip the single-sequence layer timings (tiny layer, 27B-width linear and attention layers)")
     ap.add_argument("--no-long-context", action="store_true",
                     help="skip the long-context model step (131072 committed Q4_0 slots, 16 linear + 4 attention layers)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU oracle sample budget")
@@ -521,6 +525,114 @@ def time_workload2(args, tvl, torch, dev, B):
 MFMA_F16_PEAK_TFLOPS = 2500.0   # MI355X dense fp16/bf16 matrix peak, vendor figure
 
 
+def graph_us(torch, fn, reps=20):
+    """Median microseconds per call of ``fn`` over replays of a HIP graph holding ``reps``
+    calls (one sequence's calls are latency-bound: the graph removes the launch cost)."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(reps):
+            fn()
+    w0 = time.perf_counter()
+    while time.perf_counter() - w0 < 0.05:
+        g.replay()
+        torch.cuda.synchronize()
+    ts = []
+    for _ in range(7):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e3 / reps)
+    return sorted(ts)[len(ts) // 2]
+
+
+def time_single_sequence(args, tvl, torch, dev):
+    """One sequence through each layer on its own: the tiny linear layer (1 head, dk = dv =
+    16, fp32, 8 nodes), the 27B-width linear layer (22-node tree: verify, commit, and the fused
+    call) and the 27B-width attention layer (Q8_0, 4096 committed slots, windows 2048 and 0).
+    These calls are latency-bound (a handful of workgroups); each is timed as HIP-graph replays
+    of 20 calls.  Not part of ``value``."""
+    import numpy as np
+    from workloads import workload_tiny_linear, workload_linear_27b, workload_attention_27b
+
+    def t(a, bf16):
+        if bf16:
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
+
+    def i32(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+
+    res = {}
+    for name, W in (("tiny_linear", workload_tiny_linear()), ("linear_27b", workload_linear_27b(1))):
+        L = W.lin[0]
+        bf = L.dtype == "bf16"
+        d = dict(q=t(L.q, bf), k=t(L.k, bf), v=t(L.v, bf), g=t(L.g, bf), beta=t(L.beta, bf),
+                 state=torch.from_numpy(L.state).to(dev), parent=i32(L.parent), n_nodes=i32(L.n_nodes),
+                 path=i32(L.path), path_len=i32(L.path_len))
+        d["out"] = torch.empty(tuple(L.v.shape), dtype=torch.float32, device=dev)
+        d["cap"] = torch.empty_like(d["out"])
+        d["cap2"] = torch.empty_like(d["out"])
+
+        def verify():
+            tvl.lin_tree_verify(d["q"], d["k"], d["v"], d["g"], d["beta"], d["state"], d["parent"], d["n_nodes"],
+                                L.scale, out=d["out"], cap_delta=d["cap"])
+
+        def commit():
+            tvl.lin_tree_commit(d["state"], d["path"], d["path_len"], d["k"], d["g"], d["cap"])
+
+        def fused():
+            tvl.lin_tree_verify_commit(d["q"], d["k"], d["v"], d["g"], d["beta"], d["state"], d["parent"],
+                                       d["n_nodes"], L.scale, d["path"], d["path_len"], d["k"], d["g"], d["cap"],
+                                       out=d["out"], cap_delta=d["cap2"])
+
+        verify()
+        n = int(L.n_nodes.sum())
+        entry = {}
+        for cname, fn in (("lin_tree_verify", verify), ("lin_tree_commit", commit), ("lin_tree_verify_commit", fused)):
+            us = graph_us(torch, fn)
+            entry[cname] = {"us": round(us, 2), "nodes_per_s": round(n / (us * 1e-6), 1)}
+        entry["workload"] = (f"1 sequence, {n}-node tree, Hk{L.q.shape[2]}/Hv{L.v.shape[2]} dk={L.q.shape[3]} "
+                             f"dv={L.v.shape[3]}, {L.dtype} inputs, fp32 state; path of {int(L.path_len[0])}")
+        res[name] = entry
+        del d
+    for window in (2048, 0):
+        W = workload_attention_27b(1, window=window)
+        A = W.attn[0]
+        B, N, Hq, D = A.q.shape
+        Hkv, Tcap = A.k_cache.shape[1], A.k_cache.shape[2]
+        x = dict(q=t(A.q, True), kc=torch.from_numpy(A.k_cache).to(dev), vc=torch.from_numpy(A.v_cache).to(dev),
+                 n_past=i32(A.n_past), parent=i32(A.parent), n_nodes=i32(A.n_nodes),
+                 out=torch.empty((B, N, Hq, D), dtype=torch.float32, device=dev),
+                 lse=torch.empty((B, N, Hq), dtype=torch.float32, device=dev),
+                 ws=torch.empty(max(tvl.attn_tree_workspace_bytes(B, N, Hq, Hkv, D, Tcap, window), 256),
+                                dtype=torch.uint8, device=dev))
+
+        def attn():
+            tvl.attn_tree_verify(x["q"], x["kc"], x["vc"], A.k_type, A.v_type, x["n_past"], x["parent"],
+                                 x["n_nodes"], A.window, A.scale, out=x["out"], lse=x["lse"], workspace=x["ws"])
+
+        us = graph_us(torch, attn)
+        n = int(A.n_nodes.sum())
+        nb = attn_bytes(A)
+        res[f"attention_27b_window{window}"] = {
+            "attn_tree_verify": {"us": round(us, 2), "nodes_per_s": round(n / (us * 1e-6), 1),
+                                 "algorithmic_MB": round(nb / 1e6, 3),
+                                 "GB_per_s": round(nb / (us * 1e-6) / 1e9, 1)},
+            "workload": f"1 sequence, {n}-node tree, Hq{Hq}/Hkv{Hkv} D{D}, {A.k_type} K and V, "
+                        f"{int(A.n_past[0])} committed slots, window {window}"}
+        del x
+    print("# timed the single-sequence layers", file=sys.stderr, flush=True)
+    return res
+
+
 def time_long_context(args, tvl, torch, dev):
     """One decoding step of a long-context model at one sequence: four groups of four linear
     layers (27B widths, fused commit + verify) followed by one attention layer over 131072
@@ -748,6 +860,7 @@ def main():
     unfused = None if args.no_workload2 else time_unfused_linear(args, tvl, torch, pool, sets)
     next_kernels = time_next_rows(args, tvl, torch, dev, pool[0], A0, B)
     workload2 = None if args.no_workload2 else time_workload2(args, tvl, torch, dev, B)
+    single = None if args.no_single_sequence else time_single_sequence(args, tvl, torch, dev)
     long_context = None if args.no_long_context else time_long_context(args, tvl, torch, dev)
 
     cpu = None
@@ -775,6 +888,7 @@ def main():
         "linear_unfused": unfused,
         "next_kernels": next_kernels,
         "workload2": workload2,
+        "single_sequence": single,
         "long_context": long_context,
         "roofline": roofline,
         "cpu_baseline": cpu,

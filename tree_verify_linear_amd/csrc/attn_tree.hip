@@ -633,9 +633,13 @@ __global__ __launch_bounds__(THREADS, 1) void attn_kernel(AttnLaunch L) {
     }
 }
 
-// Merges the splits of one row: O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
+// Merges the splits of one row: O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.  The max and
+// the sum run across the wave's lanes (split s on lane s mod 64); the output loop keeps eight
+// splits' loads in flight per lane, so the merge costs a few memory round trips, not one per
+// split.
 __global__ __launch_bounds__(64) void attn_combine_kernel(AttnLaunch L) {
     const AttnArgs& a = L.a;
+    const int t = threadIdx.x;
     int wg = blockIdx.x;
     const int r = wg % L.rows;
     wg /= L.rows;
@@ -645,28 +649,49 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(AttnLaunch L) {
     const int node = r / L.G, hh = r - node * L.G;
     if (node >= n) return;
     const size_t p0 = (static_cast<size_t>(b) * a.Hkv + kvh) * L.nsplit;
+    const int ns = L.nsplit;
     float M = -INFINITY;
-    for (int s = 0; s < L.nsplit; ++s) M = fmaxf(M, L.mpart[(p0 + s) * L.rows_pad + r]);
+    for (int s = t; s < ns; s += 64) M = fmaxf(M, L.mpart[(p0 + s) * L.rows_pad + r]);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
     float Lsum = 0.f;
+    if (M != -INFINITY) {
+        for (int s = t; s < ns; s += 64) {
+            const float ms = L.mpart[(p0 + s) * L.rows_pad + r];
+            if (ms != -INFINITY) Lsum += exp2f(ms - M) * L.lpart[(p0 + s) * L.rows_pad + r];
+        }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) Lsum += __shfl_xor(Lsum, o);
     float acc[D / 64];
 #pragma unroll
     for (int k = 0; k < D / 64; ++k) acc[k] = 0.f;
     if (M != -INFINITY) {
-        for (int s = 0; s < L.nsplit; ++s) {
-            const float ms = L.mpart[(p0 + s) * L.rows_pad + r];
-            if (ms == -INFINITY) continue;
-            const float w = exp2f(ms - M);
-            Lsum += w * L.lpart[(p0 + s) * L.rows_pad + r];
-            const float* op = L.opart + ((p0 + s) * L.rows_pad + r) * D;
+        constexpr int U = 8;
+        for (int s0 = 0; s0 < ns; s0 += U) {
+            float ms[U], ov[U][D / 64];
 #pragma unroll
-            for (int k = 0; k < D / 64; ++k) acc[k] += w * op[k * 64 + threadIdx.x];
+            for (int u = 0; u < U; ++u) {
+                const int s = s0 + u < ns ? s0 + u : ns - 1;
+                ms[u] = L.mpart[(p0 + s) * L.rows_pad + r];
+                const float* op = L.opart + ((p0 + s) * L.rows_pad + r) * D;
+#pragma unroll
+                for (int k = 0; k < D / 64; ++k) ov[u][k] = op[k * 64 + t];
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                if (s0 + u >= ns || ms[u] == -INFINITY) continue;
+                const float w = exp2f(ms[u] - M);
+#pragma unroll
+                for (int k = 0; k < D / 64; ++k) acc[k] += w * ov[u][k];
+            }
         }
     }
     const float inv = Lsum > 0.f ? 1.f / Lsum : 0.f;
     float* orow = a.out + ((static_cast<size_t>(b) * a.N + node) * a.Hq + kvh * L.G + hh) * D;
 #pragma unroll
-    for (int k = 0; k < D / 64; ++k) orow[k * 64 + threadIdx.x] = acc[k] * inv;
-    if (a.lse && threadIdx.x == 0)
+    for (int k = 0; k < D / 64; ++k) orow[k * 64 + t] = acc[k] * inv;
+    if (a.lse && t == 0)
         a.lse[(static_cast<size_t>(b) * a.N + node) * a.Hq + kvh * L.G + hh] = (M + log2f(Lsum)) * kLn2;
 }
 
@@ -683,7 +708,8 @@ int cu_count() {
 }
 
 // Split policy: about one workgroup per CU (the LDS footprint allows one), splits of at least
-// two tiles.  Depends only on host-known sizes (n_past lives on the device), using the
+// four tiles (below that the per-split set-up, partial writes and merge outweigh the extra
+// parallelism).  Depends only on host-known sizes (n_past lives on the device), using the
 // widest visible span.
 struct SplitPlan {
     int G, rows, rows_pad, rblocks, nsplit, chunk;
@@ -699,7 +725,7 @@ SplitPlan plan_splits(int B, int N, int Hq, int Hkv, int Tcap, int window, int c
     if (span < 1) span = 1;
     const long long units = static_cast<long long>(B) * Hkv * p.rblocks;
     long long ns = (cus + units - 1) / units;
-    const long long maxns = (span + 2 * TS - 1) / (2 * TS);
+    const long long maxns = (span + 4 * TS - 1) / (4 * TS);
     if (ns > maxns) ns = maxns;
     if (ns < 1) ns = 1;
     long long chunk = (span + ns - 1) / ns;
