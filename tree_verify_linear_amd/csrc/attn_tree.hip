@@ -695,18 +695,6 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(AttnLaunch L) {
         a.lse[(static_cast<size_t>(b) * a.N + node) * a.Hq + kvh * L.G + hh] = (M + log2f(Lsum)) * kLn2;
 }
 
-int cu_count() {
-    static int cached[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (!cached[dev]) {
-        int cus = 0;
-        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-        cached[dev] = cus;
-    }
-    return cached[dev];
-}
-
 // Split policy: about one workgroup per CU (the LDS footprint allows one), splits of at least
 // four tiles (below that the per-split set-up, partial writes and merge outweigh the extra
 // parallelism).  Depends only on host-known sizes (n_past lives on the device), using the
@@ -749,14 +737,26 @@ void launch_pair(const AttnLaunch& L, unsigned wgs, hipStream_t stream) {
 
 }  // namespace
 
+int device_cu_count() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (!cached[dev]) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+        cached[dev] = cus;
+    }
+    return cached[dev];
+}
+
 size_t attn_workspace_bytes(int B, int N, int Hq, int Hkv, int D_, int Tcap, int window) {
-    const SplitPlan p = plan_splits(B, N, Hq, Hkv, Tcap, window, cu_count());
+    const SplitPlan p = plan_splits(B, N, Hq, Hkv, Tcap, window, device_cu_count());
     return workspace_for(p, B, Hkv, D_);
 }
 
 int launch_attn(const AttnArgs& a, hipStream_t stream) {
     if (a.D != D) return set_error(TV_EUNSUPPORTED, "attn_tree_verify: D=%d not built", a.D);
-    const SplitPlan p = plan_splits(a.B, a.N, a.Hq, a.Hkv, a.Tcap, a.window, cu_count());
+    const SplitPlan p = plan_splits(a.B, a.N, a.Hq, a.Hkv, a.Tcap, a.window, device_cu_count());
     AttnLaunch L;
     L.a = a;
     L.G = p.G;

@@ -38,6 +38,8 @@
 namespace tv {
 namespace {
 
+constexpr int kMinChannels = 16;                // narrowest verify unit (one MFMA row tile)
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -574,7 +576,7 @@ __global__ __launch_bounds__(64, 2) void lin_verify_kernel(LinVerifyArgs a) {
     static_assert(NT <= 4, "register walk is for trees of up to 32 nodes");
     __shared__ VerifySmem<NT, BF16IN> sm;
     const int lane = threadIdx.x;
-    const int CW = a.dv < 64 ? a.dv : 64;
+    const int CW = a.cw;
     const int ctiles = a.dv / CW;
     const int u = xcd_remap(blockIdx.x, gridDim.x);
     UnitIn<DK, NT, BF16IN> in;
@@ -591,7 +593,7 @@ __global__ __launch_bounds__(64, 1) void lin_verify_wide_kernel(LinVerifyArgs a)
     static_assert(NT > 4 && NT <= 8, "wide register walk is for trees of 33..64 nodes");
     __shared__ VerifySmem<NT, BF16IN> sm;
     const int lane = threadIdx.x;
-    const int CW = a.dv < 64 ? a.dv : 64;
+    const int CW = a.cw;
     const int ctiles = a.dv / CW;
     const int u = xcd_remap(blockIdx.x, gridDim.x);
     UnitIn<DK, NT, BF16IN> in;
@@ -693,9 +695,22 @@ __global__ __launch_bounds__(256) void lin_commit_kernel(LinCommitArgs a, int ro
     if (t + 256 < nvec) update(s1, t + 256);
 }
 
+// Value channels per unit: 64 (one per lane of the walk), narrowed to 32 or 16 while the
+// launch would give fewer than two units per CU.  A narrower unit still walks the whole tree
+// (the walk's instruction count does not shrink) but loads, commits and contracts a
+// proportionally smaller state tile, which shortens the critical path of small batches.
+int verify_channels(int B, int Hv, int dv) {
+    int cw = dv < 64 ? dv : 64;
+    const long long target = 2LL * device_cu_count();
+    while (cw > kMinChannels && static_cast<long long>(B) * Hv * (dv / cw) < target) cw /= 2;
+    return cw;
+}
+
 template <int DK, int NT>
-int launch_verify_dk_nt(const LinVerifyArgs& a, bool bf16, hipStream_t stream) {
-    const int CW = a.dv < 64 ? a.dv : 64;
+int launch_verify_dk_nt(const LinVerifyArgs& args, bool bf16, hipStream_t stream) {
+    LinVerifyArgs a = args;
+    a.cw = verify_channels(a.B, a.Hv, a.dv);
+    const int CW = a.cw;
     const long long units = static_cast<long long>(a.B) * a.Hv * (a.dv / CW);
     if (units > 0x7fffffffLL) return set_error(TV_ERANGE, "lin_tree_verify: too many work units (%lld)", units);
     dim3 block(64);

@@ -13,6 +13,7 @@ namespace tv {
 int set_error(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 void clear_error();
 int launch_status(const char* what);   // TV_OK or TV_EDEVICE from hipGetLastError
+int device_cu_count();                // compute units of the current device (cached per device)
 
 // ---------------------------------------------------------------- launchers (host)
 struct LinVerifyArgs {
@@ -37,6 +38,7 @@ struct LinVerifyArgs {
     const void* pend_g;
     const float* pend_delta;
     float* state_out;                 // == state when a commit is pending
+    int cw;                           // value channels per work unit (set by the launcher)
 };
 int launch_lin_verify(const LinVerifyArgs& a, bool bf16, hipStream_t stream);
 
