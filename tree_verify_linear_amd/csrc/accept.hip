@@ -101,7 +101,13 @@ __global__ __launch_bounds__(ARG_THREADS) void argmax_chunk_kernel(ArgmaxArgs a)
 #pragma unroll
     for (int j = 0; j < ARG_VEC; ++j) {
         const int vi = j * ARG_THREADS + t;
-        r[j] = vi < nvec ? reinterpret_cast<const uint4*>(rowp)[vi] : make_uint4(F::kPad, F::kPad, F::kPad, F::kPad);
+        // the logits are read once: non-temporal loads keep them out of the caches
+        r[j] = make_uint4(F::kPad, F::kPad, F::kPad, F::kPad);
+        if (vi < nvec) {
+            typedef uint32_t u32v4 __attribute__((ext_vector_type(4)));
+            const u32v4 x = __builtin_nontemporal_load(reinterpret_cast<const u32v4*>(rowp) + vi);
+            r[j] = make_uint4(x[0], x[1], x[2], x[3]);
+        }
     }
 
     uint32_t best;
