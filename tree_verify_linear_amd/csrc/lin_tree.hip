@@ -445,8 +445,10 @@ __device__ __forceinline__ void store_unit(VerifySmem<NT, BF16IN>& sm, const Lin
         const bool isd = r < n;
         const int i = isd ? r : r - n;
         if (c4 < CW) {
+            // written once and read by a later call: streamed past the caches (whole lines)
             float* dst = (isd ? a.cap_delta : a.out) + rowbase + i * ostep + c4;
-            *reinterpret_cast<float4*>(dst) = *reinterpret_cast<const float4*>(cs_at(sm, isd ? i : N + i, c4));
+            const float4 x = *reinterpret_cast<const float4*>(cs_at(sm, isd ? i : N + i, c4));
+            __builtin_nontemporal_store(f32x4{x.x, x.y, x.z, x.w}, reinterpret_cast<f32x4*>(dst));
         }
     }
     __syncthreads();                                // LDS is reused by the next unit
