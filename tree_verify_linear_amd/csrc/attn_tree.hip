@@ -618,8 +618,10 @@ __global__ __launch_bounds__(THREADS, 1) void attn_kernel(AttnLaunch L) {
                     const float lsum = sm.lfin[rl];
                     const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
                     float* orow = a.out + ((static_cast<size_t>(b) * N + node) * a.Hq + kvh * L.G + hh) * D + 64 * wl;
-                    *reinterpret_cast<float4*>(orow + 4 * l16) =
-                        make_float4(oacc[r][0][e] * inv, oacc[r][1][e] * inv, oacc[r][2][e] * inv, oacc[r][3][e] * inv);
+                    // written once and read by a later call: streamed past the caches (whole lines)
+                    __builtin_nontemporal_store(f32x4{oacc[r][0][e] * inv, oacc[r][1][e] * inv, oacc[r][2][e] * inv,
+                                                      oacc[r][3][e] * inv},
+                                                reinterpret_cast<f32x4*>(orow + 4 * l16));
                     if (a.lse && wl == 0 && l16 == 0)
                         a.lse[(static_cast<size_t>(b) * N + node) * a.Hq + kvh * L.G + hh] =
                             (sm.mfin[rl] + log2f(lsum)) * kLn2;
