@@ -75,6 +75,14 @@ __device__ __forceinline__ void store8f(float* p, bool okb, const float (&u)[CPT
     if (okb) *reinterpret_cast<float4*>(p + HALF) = make_float4(u[4], u[5], u[6], u[7]);
 }
 
+// The same for outputs that are written once and read by a later call: streamed past the
+// caches (a wave's store covers whole lines).
+__device__ __forceinline__ void store8f_stream(float* p, bool okb, const float (&u)[CPT]) {
+    typedef float f32v4 __attribute__((ext_vector_type(4)));
+    __builtin_nontemporal_store(f32v4{u[0], u[1], u[2], u[3]}, reinterpret_cast<f32v4*>(p));
+    if (okb) __builtin_nontemporal_store(f32v4{u[4], u[5], u[6], u[7]}, reinterpret_cast<f32v4*>(p + HALF));
+}
+
 // SiLU with the hardware exp2 and reciprocal (each about 1 ulp).
 __device__ __forceinline__ float silu(float v) {
     return v * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-1.4426950408889634f * v));
@@ -138,7 +146,7 @@ __global__ __launch_bounds__(CONV_THREADS) void conv_tree_kernel(ConvArgs a) {
 #pragma unroll
             for (int e = 0; e < CPT; ++e) acc[e] = silu(acc[e]);
         }
-        if (i0 + q < n) store8f(a.y + (xrow + i) * a.C + c0, okb, acc);
+        if (i0 + q < n) store8f_stream(a.y + (xrow + i) * a.C + c0, okb, acc);
     }
 }
 
