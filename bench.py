@@ -12,8 +12,8 @@ of 128, fp32 state; attention 24 query / 4 KV heads of 256.
 value = node-layers per second = 2 * (tree nodes in the batch) / step time, i.e. the
 harmonic mean of the linear layer's and the attention layer's nodes/s.
 
-Inputs are seeded synthetic tensors (workloads.workload_batched); a pool of two distinct
-input sets (about 1.5 GB) rotates between steps so the 256 MB last-level cache cannot
+Inputs are seeded synthetic tensors (workloads.workload_batched); a pool of three distinct
+input sets (about 2 GB) rotates between steps so the 256 MB last-level cache cannot
 hold a step's working set.  Per-kernel durations come from HIP events recorded on the
 stream the kernels are launched on (torch's current stream) around every call in the
 timed region.
@@ -35,8 +35,9 @@ workload for about ten seconds.
 
 Warm-up runs at least --warmup steps and keeps going until --min-warmup-s (0.3 s) have
 passed: the clock ramps up over the first ~40 ms of sustained work, and timings taken
-inside the ramp read up to 15% slow.  ``warmup`` in the JSON line is the number of
-warm-up steps actually run.
+inside the ramp read up to 15% slow.  ``warmup`` in the JSON line is the requested minimum,
+``warmup_steps_run`` the number of warm-up steps actually run.  ``copy_ceiling`` is a
+device-to-device copy measured on the same GPU; every kernel also reports its fraction of it.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline]
 """
@@ -219,6 +220,31 @@ def counter_traffic(kernel: str):
         return None
 
 
+UTIL_FILE = os.path.join(ROOT, "profiles", "util_counters_batched64.txt")
+
+
+def counter_util(kernel: str):
+    """Matrix-core and vector-ALU utilisation of ``kernel`` from the committed counter summary
+    (rocprofv3 SQ_VALU_MFMA_BUSY_CYCLES etc.), if it was taken on the current source."""
+    if not os.path.exists(UTIL_FILE):
+        return None
+    fields = {}
+    with open(UTIL_FILE) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                key, val = line.split(":", 1)
+                fields[key.strip()] = val.strip()
+    if fields.get(f"{kernel}.source_sha256") != sha256_of(KERNEL_SOURCES[kernel]):
+        return None
+    out = {}
+    for key in ("mfma_util", "mfma_useful_frac", "valu_busy", "mfma_valu_coexec"):
+        try:
+            out[key] = float(fields[f"{kernel}.{key}"])
+        except (KeyError, ValueError):
+            pass
+    return out or None
+
+
 def to_device(L, A, dev):
     import numpy as np
     import torch
@@ -242,6 +268,26 @@ def to_device(L, A, dev):
     d["aout"] = torch.empty((Bq, Nq, Hq, D), dtype=torch.float32, device=dev)
     d["lse"] = torch.empty((Bq, Nq, Hq), dtype=torch.float32, device=dev)
     return d
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def _blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max((p.get("num_threads", 1) for p in threadpool_info()), default=None)
+    except Exception:
+        return None
 
 
 def cpu_baseline(L, A, budget_s: float):
@@ -269,12 +315,6 @@ def cpu_baseline(L, A, budget_s: float):
             break
     wall = time.perf_counter() - w0
     cpu = time.process_time() - c0
-    blas = None
-    try:
-        from threadpoolctl import threadpool_info
-        blas = max((p.get("num_threads", 1) for p in threadpool_info()), default=None)
-    except Exception:
-        pass
     return {
         "value": 2.0 * nodes / wall,
         "unit": "node-layers/s",
@@ -283,8 +323,60 @@ def cpu_baseline(L, A, budget_s: float):
         "sample": f"{seqs} of {B} sequences of the batched step (linear verify + commit + attention, "
                   f"{nodes} nodes), fp64 NumPy, {wall:.1f} s wall, {cpu:.1f} s CPU",
         "host_cpus": os.cpu_count(),
-        "blas_threads": blas,
+        "cpu_model": cpu_model(),
+        "blas_threads": _blas_threads(),
     }
+
+
+def cpu_baseline_configs(long_w):
+    """The same oracle on the other workloads, one call each (the long-context step from one
+    of its linear and one of its attention layers): wall seconds and nodes/s per layer call."""
+    import dataclasses
+    import oracle
+    from workloads import workload_tiny_linear, workload_linear_27b, workload_attention_27b
+
+    def timed(fn):
+        w0, c0 = time.perf_counter(), time.process_time()
+        fn()
+        return time.perf_counter() - w0, time.process_time() - c0
+
+    def lin(L):
+        oracle.lin_tree_verify(L.q, L.k, L.v, L.g, L.beta, L.state, L.parent, L.n_nodes, L.scale, L.dtype)
+        oracle.lin_commit_replay(L.state, L.path, L.path_len, L.k, L.v, L.g, L.beta, L.parent, L.n_nodes, L.dtype)
+
+    def attn(A, dense=False):
+        f = oracle.attn_tree_verify_dense if dense else oracle.attn_tree_verify
+        f(A.q, A.k_cache, A.v_cache, A.k_type, A.v_type, A.n_past, A.parent, A.n_nodes, A.window, A.scale, A.Hkv)
+
+    res = {}
+    L0 = workload_tiny_linear().lin[0]
+    reps = 20
+    w, c = timed(lambda: [lin(L0) for _ in range(reps)])
+    res["tiny_linear"] = {"wall_s_per_call": round(w / reps, 5), "nodes_per_s": round(reps * int(L0.n_nodes.sum()) / w, 1),
+                          "what": "verify + commit replay, 1 head, dk=dv=16, fp32, 8 nodes"}
+    L1 = workload_linear_27b(1).lin[0]
+    w, c = timed(lambda: lin(L1))
+    res["linear_27b"] = {"wall_s_per_call": round(w, 4), "nodes_per_s": round(int(L1.n_nodes.sum()) / w, 1),
+                         "what": "verify + commit replay, Hk16/Hv48 dk=dv=128, 22 nodes"}
+    A2 = workload_attention_27b(1).attn[0]
+    w, c = timed(lambda: attn(A2))
+    res["attention_27b"] = {"wall_s_per_call": round(w, 4), "nodes_per_s": round(int(A2.n_nodes.sum()) / w, 1),
+                            "what": "Hq24/Hkv4 D256, Q8_0, 4096 committed slots, window 2048, 22 nodes"}
+    if long_w is not None:
+        Ll, Al = long_w.lin[0], long_w.attn[0]
+        wl, _ = timed(lambda: lin(Ll))
+        out = {"linear_layer_wall_s": round(wl, 4)}
+        for window in (0, 2048):
+            Aw = dataclasses.replace(Al, window=window)
+            wa, _ = timed(lambda: attn(Aw, dense=True))
+            step = 16 * wl + 4 * wa
+            out[f"window{window}"] = {"attention_layer_wall_s": round(wa, 4), "step_wall_s": round(step, 3),
+                                      "node_layers_per_s": round(20 * int(Ll.n_nodes.sum()) / step, 1)}
+        out["what"] = ("one 22-node step of 16 linear + 4 attention layers (131072 Q4_0 slots), from one timed "
+                       "linear layer (verify + commit replay) and one attention layer (the oracle's dense masked "
+                       "softmax) per window")
+        res["long_context"] = out
+    return res
 
 
 def time_next_rows(args, tvl, torch, dev, d, A, B):
@@ -436,17 +528,21 @@ def time_next_rows(args, tvl, torch, dev, d, A, B):
 
 
 def time_unfused_linear(args, tvl, torch, pool, sets):
-    """The linear layer's separate calls (verify, then commit of the same step's path) on the
-    step's inputs, for comparison with the fused call."""
+    """The linear layer's separate calls (verify, then commit) on the step's inputs, for
+    comparison with the fused call.  Iteration i verifies input set i and commits the set
+    verified in iteration i - 1 (with that verify's deltas), so neither call finds its state
+    in the last-level cache from the call just before it (the sets rotate through about 2 GB)."""
     K = max(args.steps, 10)
+    n = len(pool)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
     for i in range(K):
-        d, L = pool[i % len(pool)], sets[i % len(sets)].lin[0]
+        d, L = pool[i % n], sets[i % n].lin[0]
+        c = pool[(i - 1) % n]
         ev[i][0].record()
         tvl.lin_tree_verify(d["q"], d["k"], d["v"], d["g"], d["beta"], d["state"], d["parent"], d["n_nodes"],
                             L.scale, out=d["out"], cap_delta=d["cap"])
         ev[i][1].record()
-        tvl.lin_tree_commit(d["state"], d["path"], d["path_len"], d["k"], d["g"], d["cap"])
+        tvl.lin_tree_commit(c["state"], c["path"], c["path_len"], c["k"], c["g"], c["cap"])
         ev[i][2].record()
     torch.cuda.synchronize()
     res = {}
@@ -523,6 +619,30 @@ def time_workload2(args, tvl, torch, dev, B):
 
 
 MFMA_F16_PEAK_TFLOPS = 2500.0   # MI355X dense fp16/bf16 matrix peak, vendor figure
+
+
+def measure_copy_ceiling(torch, dev, mib: int = 1024, reps: int = 10):
+    """A STREAM-style copy ceiling on this GPU: device-to-device copies of ``mib`` MiB (read
+    once, written once), timed with events; GB/s counts both directions."""
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    ms = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        ms.append(e0.elapsed_time(e1))
+    del src, dst
+    best = min(ms)
+    gbs = 2 * mib * (1 << 20) / (best * 1e-3) / 1e9
+    return {"GB_per_s": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "what": f"device-to-device copy of {mib} MiB (read + write), best of {reps}"}
 
 
 def graph_us(torch, fn, reps=20):
@@ -637,15 +757,16 @@ def time_long_context(args, tvl, torch, dev):
     """One decoding step of a long-context model at one sequence: four groups of four linear
     layers (27B widths, fused commit + verify) followed by one attention layer over 131072
     committed slots in Q4_0 (K and V), with one shared 22-node tree; full attention
-    (window 0) and window 2048.  Two distinct attention layers are generated (302 MB of
-    cache, above the 256 MB last-level cache) and alternate between the four attention
-    positions.  Not part of ``value``."""
+    (window 0) and window 2048.  Four distinct attention layers (604 MB of cache, over twice
+    the 256 MB last-level cache), so no attention layer is served from that cache at window 0.
+    At window 2048 a step touches about 60 MB, so it runs cache-resident; those figures are
+    latency-bound either way.  Not part of ``value``.  Returns (results, workload)."""
     import dataclasses
     import numpy as np
     from workloads import workload_long_context
 
     t0 = time.perf_counter()
-    W = workload_long_context(window=0, n_lin=16, n_attn=2)
+    W = workload_long_context(window=0, n_lin=16, n_attn=4)
     print(f"# generated the long-context layers in {time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
 
     def bits(a):
@@ -674,7 +795,7 @@ def time_long_context(args, tvl, torch, dev):
                           ws=torch.empty(ws_bytes, dtype=torch.uint8, device=dev)))
     order = []
     for a in range(4):
-        order += [("lin", 4 * a + j) for j in range(4)] + [("attn", a % 2)]
+        order += [("lin", 4 * a + j) for j in range(4)] + [("attn", a)]
     # the first visit of each linear layer has no previous path: a plain verify fills its deltas
     for i, d in enumerate(lins):
         L = W.lin[i]
@@ -740,7 +861,7 @@ def time_long_context(args, tvl, torch, dev):
         }
         print(f"# timed the long-context step, window {window}", file=sys.stderr, flush=True)
     del lins, attns
-    return res
+    return res, W
 
 
 # ----------------------------------------------------------------------------- main
@@ -766,7 +887,7 @@ def main():
 
     B = args.batch
     t_gen = time.perf_counter()
-    sets = [workload_batched(B), workload_batched(B, seq_ids=list(range(B, 2 * B)))]
+    sets = [workload_batched(B, seq_ids=list(range(k * B, (k + 1) * B))) for k in range(3)]
     print(f"# generated {len(sets)} input sets in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr, flush=True)
     pool = [to_device(W.lin[0], W.attn[0], dev) for W in sets]
     L0, A0 = sets[0].lin[0], sets[0].attn[0]
@@ -806,6 +927,7 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    copy_ceiling = measure_copy_ceiling(torch, dev)
 
     # Warm-up: at least --warmup steps, and untimed steps until --min-warmup-s have passed, so
     # the timed steps run at the clock the GPU holds under sustained load.
@@ -855,17 +977,25 @@ def main():
     achieved = kernels[dom]["GB_per_s"]
     roofline = {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": counter_traffic(dom),
-                "algorithmic_bytes_per_launch": int(byts[dom])}
+                "algorithmic_bytes_per_launch": int(byts[dom]),
+                "frac_copy_ceiling": round(achieved / copy_ceiling["GB_per_s"], 4)}
+    for n in names:
+        kernels[n]["frac_copy_ceiling"] = round(kernels[n]["GB_per_s"] / copy_ceiling["GB_per_s"], 4)
+    util = counter_util("attn_tree_verify")
+    if util:
+        kernels["attn_tree_verify"].update(util)
 
     unfused = None if args.no_workload2 else time_unfused_linear(args, tvl, torch, pool, sets)
     next_kernels = time_next_rows(args, tvl, torch, dev, pool[0], A0, B)
     workload2 = None if args.no_workload2 else time_workload2(args, tvl, torch, dev, B)
     single = None if args.no_single_sequence else time_single_sequence(args, tvl, torch, dev)
-    long_context = None if args.no_long_context else time_long_context(args, tvl, torch, dev)
+    long_context, long_w = (None, None) if args.no_long_context else time_long_context(args, tvl, torch, dev)
 
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(L0, A0, args.cpu_seconds)
+        cpu["per_config"] = cpu_baseline_configs(long_w)
+        print("# timed the CPU oracle", file=sys.stderr, flush=True)
 
     line = {
         "metric": "tree-verify nodes/s per layer (22-node tree) + achieved HBM GB/s vs peak",
@@ -873,7 +1003,8 @@ def main():
         "unit": "node-layers/s",
         "n_gpus": 1,
         "steps": K,
-        "warmup": warm,
+        "warmup": args.warmup,
+        "warmup_steps_run": warm,
         "ms_per_step": round(ms_step, 4),
         "host_ms_per_step": round(host_ms, 4),
         "higher_is_better": True,
@@ -891,6 +1022,7 @@ def main():
         "single_sequence": single,
         "long_context": long_context,
         "roofline": roofline,
+        "copy_ceiling": copy_ceiling,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

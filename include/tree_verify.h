@@ -160,6 +160,7 @@ int lin_tree_verify(int B, int N, int Hk, int Hv, int dk, int dv, int dtype, int
  *   g          device, [B][N][Hv]
  *   cap_delta  device, fp32 [B][N][Hv][dv], written by lin_tree_verify
  *   state      device, fp32 [B][Hv][dv][dk], updated in place
+ * state, k and cap_delta must be 16-byte aligned (TV_EINVAL otherwise).
  */
 int lin_tree_commit(int B, int N, int Hk, int Hv, int dk, int dv, int dtype, int head_group,
                     const int32_t* path, const int32_t* path_len, int Lmax,

@@ -146,3 +146,62 @@ def attn_tree_verify_rows(q, k_cache, v_cache, k_type: str, v_type: str, n_past,
         outs[r] = acc / l
         lses[r] = m + np.log(l)
     return outs, lses
+
+
+def visibility_mask(T: int, dep: np.ndarray, anc: np.ndarray, n: int, W: int, lo: int) -> np.ndarray:
+    """``M[i, s]`` is True iff query node i sees cache slot ``lo + s`` for slots lo .. T+n-1
+    (the window and ancestry rule of the module docstring, as a dense mask)."""
+    slots = np.arange(lo, T + n)
+    pos = np.where(slots < T, slots, 0).astype(np.int64)
+    M = np.zeros((n, len(slots)), dtype=bool)
+    for i in range(n):
+        pi = T + int(dep[i])
+        committed = slots < T
+        if W:
+            committed &= (pi - pos) < W
+        M[i] = committed
+        for j in range(n):
+            if anc[i, j] and (W == 0 or int(dep[i]) - int(dep[j]) < W):
+                M[i, T + j - lo] = True
+    return M
+
+
+def attn_tree_verify_dense(q, k_cache, v_cache, k_type: str, v_type: str, n_past, parent, n_nodes,
+                           window: int, scale: float, Hkv: int, chunk: int = 32768):
+    """The same outputs as ``attn_tree_verify``, computed as one masked softmax per KV head
+    over the union of the slots any node sees: scores of every (node, query head) row against
+    the union, invisible slots set to -inf, then softmax-weighted V.  Dequantised K and V are
+    taken in chunks of slots, so caches of 10^5 slots fit in memory; the softmax is exact
+    (scores of the whole union are kept, then one max, one exp, one weighted sum)."""
+    qf = bf16_bits_to_f64(q)
+    B, N, Hq, D = qf.shape
+    G = Hq // Hkv
+    out = np.zeros((B, N, Hq, D))
+    lse = np.zeros((B, N, Hq))
+    for b in range(B):
+        n, T = int(n_nodes[b]), int(n_past[b])
+        validate_tree(parent[b], n)
+        dep = depths(parent[b], n)
+        anc = ancestor_matrix(parent[b], n)
+        lo = 0 if window == 0 else max(0, T + int(dep.min()) - window + 1)
+        M = visibility_mask(T, dep, anc, n, window, lo)          # [n][slots]
+        S = T + n - lo
+        for kvh in range(Hkv):
+            heads = slice(kvh * G, (kvh + 1) * G)
+            Q = qf[b, :n, heads].reshape(n * G, D)                # row r = node r // G, head r % G
+            vis = np.repeat(M, G, axis=0)
+            s = np.empty((n * G, S))
+            for c0 in range(0, S, chunk):
+                K = dequant_rows(k_cache[b, kvh, lo + c0:lo + min(S, c0 + chunk)], k_type)
+                s[:, c0:c0 + K.shape[0]] = scale * (Q @ K.T)
+            s[~vis] = -np.inf
+            m = s.max(axis=1, keepdims=True)
+            p = np.exp(s - m)
+            acc = np.zeros((n * G, D))
+            for c0 in range(0, S, chunk):
+                V = dequant_rows(v_cache[b, kvh, lo + c0:lo + min(S, c0 + chunk)], v_type)
+                acc += p[:, c0:c0 + V.shape[0]] @ V
+            l = p.sum(axis=1, keepdims=True)
+            out[b, :n, heads] = (acc / l).reshape(n, G, D)
+            lse[b, :n, heads] = (m + np.log(l))[:, 0].reshape(n, G)
+    return out, lse

@@ -67,6 +67,12 @@ def test_commit_argument_errors():
     assert L.lin_tree_commit(1, 8, 1, 1, 16, 16, 0, 0, f, f, 9, f, f, f, f, f) == tvl.TV_ERANGE   # Lmax > N
     assert L.lin_tree_commit(1, 8, 1, 1, 16, 16, 0, 0, None, f, 4, f, f, f, f, f) == tvl.TV_EINVAL
     assert L.lin_tree_commit(1, 8, 1, 1, 12, 16, 0, 0, f, f, 4, f, f, f, f, f) == tvl.TV_EUNSUPPORTED
+    m = ctypes.c_void_p(4098)                                  # 2-byte aligned only
+    for i in range(3):                                         # k, cap_delta, state
+        args = [f, f, 4, f, f, f, f, None]
+        args[[3, 5, 6][i]] = m
+        assert L.lin_tree_commit(1, 8, 1, 1, 16, 16, 1, 0, *args) == tvl.TV_EINVAL
+        assert b"aligned" in L.tv_last_error()
 
 
 def test_attention_argument_errors():

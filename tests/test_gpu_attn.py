@@ -84,25 +84,21 @@ def test_ragged_history_and_other_grouping():
     check(A, "ragged")
 
 
-def test_long_context_sampled():
-    """131072 committed Q4_0 slots (window 0 and 2048): sampled rows against the oracle."""
-    for window in (0, 2048):
-        W = workload_long_context(window=window, n_lin=0, n_attn=1)
-        A = W.attn[0]
-        out, lse = run_gpu(A)
-        rng = np.random.default_rng(window)
-        n = int(A.n_nodes[0])
-        rows = [(0, int(i), int(h)) for i, h in zip(rng.integers(0, n, 12), rng.integers(0, A.Hq, 12))]
-        rows += [(0, 0, 0), (0, n - 1, A.Hq - 1)]
-        ro, rl = oracle.attn_tree_verify_rows(A.q, A.k_cache, A.v_cache, A.k_type, A.v_type, A.n_past, A.parent,
-                                              A.n_nodes, A.window, A.scale, A.Hkv, rows)
-        got = np.stack([out[b, i, h] for b, i, h in rows])
-        gl = np.array([lse[b, i, h] for b, i, h in rows])
-        e = rel_err(got, ro)
-        el = float(np.max(np.abs(gl - rl)))
-        print(f"[attn long w{window}] sampled out {e:.2e} x RMS, lse {el:.2e}")
-        assert e <= TOL and el <= TOL_LSE
-        assert np.isfinite(out[0, :n]).all()
+@pytest.mark.parametrize("window", [0, 2048])
+def test_long_context_all_rows(window):
+    """131072 committed Q4_0 slots (K and V), window 0 and 2048: every row of the layer (22
+    nodes x 24 query heads) against the oracle's dense masked softmax."""
+    W = workload_long_context(window=window, n_lin=0, n_attn=1)
+    A = W.attn[0]
+    out, lse = run_gpu(A)
+    ro, rl = oracle.attn_tree_verify_dense(A.q, A.k_cache, A.v_cache, A.k_type, A.v_type, A.n_past, A.parent,
+                                           A.n_nodes, A.window, A.scale, A.Hkv)
+    mask = valid_rows(A.n_nodes, A.parent.shape[1])
+    e = rel_err(out, ro, mask)
+    el = float(np.max(np.abs(lse[mask] - rl[mask])))
+    print(f"[attn long w{window}] all {int(mask.sum()) * A.Hq} rows: out {e:.2e} x RMS, lse {el:.2e}")
+    assert e <= TOL and el <= TOL_LSE
+    assert np.isnan(out[~mask]).all()
 
 
 def test_deterministic_and_batch_invariant():
@@ -115,6 +111,9 @@ def test_deterministic_and_batch_invariant():
     ob, lb = run_gpu(one)
     n = int(one.n_nodes[0])
     # The KV split plan depends on the batch size, so the two runs accumulate in different
-    # orders: each is within TOL of the exact result, hence within 2 TOL of each other.
-    assert rel_err(ob[0, :n], o1[1, :n]) <= 2 * TOL
-    assert np.max(np.abs(lb[0, :n] - l1[1, :n])) <= 2 * TOL_LSE
+    # orders; both are fp32 sums of the same exactly formed terms, so they agree to a few
+    # fp32 rounding steps, far inside the parity tolerance.
+    e = rel_err(ob[0, :n], o1[1, :n])
+    el = float(np.max(np.abs(lb[0, :n] - l1[1, :n])))
+    print(f"[attn batch invariance] out {e:.2e} x RMS, lse {el:.2e}")
+    assert e <= 1e-5 and el <= 1e-5

@@ -61,6 +61,70 @@ def test_fused_27b_width():
     check(*two_steps(16, 48, 128, 128, "bf16"), 2e-3, "27b")
 
 
+def _slice_lin(L, idx):
+    """The inputs of the sequences ``idx`` alone (every sequence is independent)."""
+    import dataclasses
+    idx = np.asarray(idx)
+    return dataclasses.replace(L, q=L.q[idx], k=L.k[idx], v=L.v[idx], g=L.g[idx], beta=L.beta[idx],
+                               state=L.state[idx], parent=L.parent[idx], n_nodes=L.n_nodes[idx],
+                               path=L.path[idx], path_len=L.path_len[idx])
+
+
+def _units_are_64_wide(B, Hv, dv):
+    """The launcher narrows units below 64 channels only while a launch would give fewer than
+    two units per compute unit; this returns whether this shape keeps 64-channel units."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    return B * Hv * (dv // 64) >= 2 * cus
+
+
+def test_fused_64_channel_units():
+    """27B width with enough sequences that the launcher keeps 64-channel units (the width the
+    batched step runs): every sequence of two steps compared with the oracle."""
+    B = 8
+    assert _units_are_64_wide(B, 48, 128), "this shape no longer exercises 64-channel units"
+    L1, L2 = two_steps(16, 48, 128, 128, "bf16", B=B, cfg=160)
+    check(L1, L2, 2e-3, "27b B8 cw64")
+
+
+def test_fused_batched_step_shape():
+    """The batched step itself: 64 sequences, 22-node trees, two steps through the fused call.
+    Every sequence is compared with the separate calls; eight sequences (first, last and six
+    spread between) with the oracle."""
+    B = 64
+    assert _units_are_64_wide(B, 48, 128)
+    # the batched step's linear layer (its trees and paths), and a second step of the same sequences
+    L1, L2 = (gen_lin(c, *trees_for(c, B, "ddtree"), 16, 48, 128, 128, "bf16") for c in (3, 203))
+    d1, d2 = lin_to_device(L1), lin_to_device(L2)
+    state = d1["state"].clone()
+    _, cap1 = tvl.lin_tree_verify(d1["q"], d1["k"], d1["v"], d1["g"], d1["beta"], state, d1["parent"],
+                                  d1["n_nodes"], L1.scale)
+    N = L2.parent.shape[1]
+    out = torch.full((B, N, L2.Hv, L2.dv), float("nan"), device="cuda")
+    cap = torch.full_like(out, float("nan"))
+    tvl.lin_tree_verify_commit(d2["q"], d2["k"], d2["v"], d2["g"], d2["beta"], state, d2["parent"], d2["n_nodes"],
+                               L2.scale, d1["path"], d1["path_len"], d1["k"], d1["g"], cap1, out=out, cap_delta=cap)
+    st_u = d1["state"].clone()
+    tvl.lin_tree_commit(st_u, d1["path"], d1["path_len"], d1["k"], d1["g"], cap1)
+    out_u, cap_u = tvl.lin_tree_verify(d2["q"], d2["k"], d2["v"], d2["g"], d2["beta"], st_u, d2["parent"],
+                                       d2["n_nodes"], L2.scale)
+    torch.cuda.synchronize()
+    mask = valid_rows(L2.n_nodes, N)
+    o, c, s = out.cpu().numpy(), cap.cpu().numpy(), state.cpu().numpy()
+    e_fu = max(rel_err(o, out_u.cpu().numpy(), mask), rel_err(c, cap_u.cpu().numpy(), mask),
+               rel_err(s, st_u.cpu().numpy()))
+    assert np.isnan(o[~mask]).all(), "padding rows were written"
+    pick = [0, 9, 18, 27, 36, 45, 54, 63]
+    A1, A2 = _slice_lin(L1, pick), _slice_lin(L2, pick)
+    prev = (A1.path, A1.path_len, A1.k, A1.v, A1.g, A1.beta, A1.parent, A1.n_nodes)
+    rs, ro, rd = oracle.lin_tree_verify_commit(A1.state, prev, A2.q, A2.k, A2.v, A2.g, A2.beta, A2.parent,
+                                               A2.n_nodes, A2.scale, A2.dtype)
+    m2 = valid_rows(A2.n_nodes, N)
+    e_o, e_d, e_s = rel_err(o[pick], ro, m2), rel_err(c[pick], rd, m2), rel_err(s[pick], rs)
+    print(f"[verify+commit b64] out {e_o:.2e} delta {e_d:.2e} state {e_s:.2e} (8 sequences); "
+          f"vs unfused {e_fu:.2e} (all 64)")
+    assert e_o <= 2e-3 and e_d <= 2e-3 and e_s <= 2e-3 and e_fu <= 2e-3
+
+
 def test_fused_tree_sizes_differ_and_empty_paths():
     """Previous step 40 nodes (the wide kernel's tree size), this step 8 (a chain); one
     sequence accepted nothing in the previous step: its state stays bit-identical."""

@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import (attn_tree_verify, attn_tree_verify_rows, dequant_q8_0, dequant_q4_0,
+from oracle import (attn_tree_verify, attn_tree_verify_rows, attn_tree_verify_dense, dequant_q8_0, dequant_q4_0,
                     dequant_rows, root_path, depths)
 from oracle.delta import bf16_bits_to_f64
 from workloads import (gen_attn, trees_for, tree_chain, tree_ddtree, quantize_q8_0, quantize_q4_0,
@@ -166,6 +166,23 @@ def test_rows_variant_matches_full():
     for r, (b, i, h) in enumerate(rows):
         np.testing.assert_allclose(o2[r], out[b, i, h], atol=1e-12)
         np.testing.assert_allclose(l2[r], lse[b, i, h], atol=1e-12)
+
+
+@pytest.mark.parametrize("window,kt,vt,chunk", [(0, "q8_0", "q8_0", 32768), (50, "q8_0", "q4_0", 7),
+                                                (1, "q4_0", "q8_0", 64), (3, "q4_0", "q4_0", 5)])
+def test_dense_variant_matches_per_node(window, kt, vt, chunk):
+    """The dense masked-softmax form (one score matrix per KV head over the union of visible
+    slots, taken in slot chunks) equals the per-node form on ragged histories, including a
+    sequence with no history and windows of 1 and 3."""
+    rng = np.random.default_rng(window + 11)
+    parents = [tree_ddtree(rng, budget=22), tree_chain(6), np.array([-1], np.int32)]
+    A = gen_attn(33, parents, 6, 2, 64, [300, 0, 17], kt, vt, window)
+    ref, rl = attn_tree_verify(A.q, A.k_cache, A.v_cache, kt, vt, A.n_past, A.parent, A.n_nodes, window,
+                               A.scale, A.Hkv)
+    out, lse = attn_tree_verify_dense(A.q, A.k_cache, A.v_cache, kt, vt, A.n_past, A.parent, A.n_nodes,
+                                      window, A.scale, A.Hkv, chunk=chunk)
+    np.testing.assert_allclose(out, ref, atol=1e-12)
+    np.testing.assert_allclose(lse, rl, atol=1e-12)
 
 
 def test_relabeling_invariance():

@@ -155,7 +155,8 @@ int lin_tree_commit(int B, int N, int Hk, int Hv, int dk, int dv, int dtype, int
     if (st != TV_OK) return st;
     if (Lmax < 1 || Lmax > N) return set_error(TV_ERANGE, "%s: Lmax=%d not in [1, N=%d]", fn, Lmax, N);
     if (!path || !path_len || !k || !g || !cap_delta || !state) return set_error(TV_EINVAL, "%s: null pointer argument", fn);
-    if (!aligned(state, 16)) return set_error(TV_EINVAL, "%s: state must be 16-byte aligned", fn);
+    if (!aligned(state, 16) || !aligned(k, 16) || !aligned(cap_delta, 16))
+        return set_error(TV_EINVAL, "%s: state, k and cap_delta must be 16-byte aligned", fn);
     LinCommitArgs a{B, N, Hk, Hv, dk, dv, Hv / Hk, head_group == TV_HEADS_TILED, Lmax, path, path_len, k, g,
                     cap_delta, state};
     return launch_lin_commit(a, dtype == TV_BF16, static_cast<hipStream_t>(stream));
@@ -168,12 +169,13 @@ size_t attn_tree_workspace_bytes(int B, int N, int Hq, int Hkv, int D, int Tcap,
     return attn_workspace_bytes(B, N, Hq, Hkv, D, Tcap, window);
 }
 
-int attn_tree_verify(int B, int N, int Hq, int Hkv, int D, int Tcap, int k_type, int v_type, int window, float scale,
-                     const int32_t* parent, const int32_t* n_nodes, const int32_t* n_past, const void* q,
-                     const void* k_cache, const void* v_cache, float* out, float* lse, void* workspace,
-                     size_t workspace_bytes, void* stream) {
-    clear_error();
-    const char* fn = "attn_tree_verify";
+}  // extern "C"
+
+// Host checks shared by attn_tree_verify and attn_tree_verify_noalloc (everything but the
+// workspace).
+static int check_attn(const char* fn, int B, int N, int Hq, int Hkv, int D, int Tcap, int k_type, int v_type,
+                      int window, float scale, const int32_t* parent, const int32_t* n_nodes, const int32_t* n_past,
+                      const void* q, const void* k_cache, const void* v_cache, const float* out) {
     if (B <= 0 || N <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || Tcap <= 0)
         return set_error(TV_EINVAL, "%s: sizes must be positive (B=%d N=%d Hq=%d Hkv=%d D=%d Tcap=%d)", fn, B, N, Hq,
                          Hkv, D, Tcap);
@@ -188,12 +190,26 @@ int attn_tree_verify(int B, int N, int Hq, int Hkv, int D, int Tcap, int k_type,
                          "(Q4_0, Q8_0), (Q4_0, Q4_0)", fn, k_type, v_type);
     if (window < 0) return set_error(TV_EINVAL, "%s: window=%d must be >= 0 (0 = full attention)", fn, window);
     if (!std::isfinite(scale)) return set_error(TV_EINVAL, "%s: scale is not finite", fn);
-    if (!parent || !n_nodes || !n_past || !q || !k_cache || !v_cache || !out || !workspace)
+    if (!parent || !n_nodes || !n_past || !q || !k_cache || !v_cache || !out)
         return set_error(TV_EINVAL, "%s: null pointer argument", fn);
-    if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
-        !aligned(workspace, 256))
-        return set_error(TV_EINVAL, "%s: q, the caches and out must be 16-byte aligned, workspace 256-byte aligned",
-                         fn);
+    if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16))
+        return set_error(TV_EINVAL, "%s: q, the caches and out must be 16-byte aligned", fn);
+    return TV_OK;
+}
+
+extern "C" {
+
+int attn_tree_verify(int B, int N, int Hq, int Hkv, int D, int Tcap, int k_type, int v_type, int window, float scale,
+                     const int32_t* parent, const int32_t* n_nodes, const int32_t* n_past, const void* q,
+                     const void* k_cache, const void* v_cache, float* out, float* lse, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+    clear_error();
+    const char* fn = "attn_tree_verify";
+    const int st = check_attn(fn, B, N, Hq, Hkv, D, Tcap, k_type, v_type, window, scale, parent, n_nodes, n_past, q,
+                              k_cache, v_cache, out);
+    if (st != TV_OK) return st;
+    if (!workspace) return set_error(TV_EINVAL, "%s: null pointer argument", fn);
+    if (!aligned(workspace, 256)) return set_error(TV_EINVAL, "%s: workspace must be 256-byte aligned", fn);
     const size_t need = attn_workspace_bytes(B, N, Hq, Hkv, D, Tcap, window);
     if (need == 0) return set_error(TV_ERANGE, "%s: sizes overflow", fn);
     if (workspace_bytes < need)
