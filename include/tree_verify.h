@@ -242,6 +242,24 @@ int attn_tree_verify(int B, int N, int Hq, int Hkv, int D, int Tcap, int k_type,
                      const void* v_cache, float* out, float* lse, void* workspace,
                      size_t workspace_bytes, void* stream);
 
+/*
+ * attn_tree_verify_noalloc -- attn_tree_verify for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same arguments, results and errors as attn_tree_verify, without the workspace:
+ * the split partials go to a scratch array the library holds on each device for the life of
+ * the process (64 MiB, reserved when the library's code is first loaded on a device).  The
+ * call allocates nothing.
+ *   - Sizes whose partials need more than the scratch (attn_tree_workspace_bytes(...) above
+ *     64 MiB) are rejected with TV_ERANGE before anything is enqueued.
+ *   - Every call on a device shares that device's scratch, so calls that can overlap on one
+ *     GPU (different streams, or different threads without ordering) race: serialise them.
+ *     Nothing in the scratch needs to start at zero; its contents are garbage afterwards.
+ */
+int attn_tree_verify_noalloc(int B, int N, int Hq, int Hkv, int D, int Tcap, int k_type, int v_type,
+                             int window, float scale, const int32_t* parent, const int32_t* n_nodes,
+                             const int32_t* n_past, const void* q, const void* k_cache,
+                             const void* v_cache, float* out, float* lse, void* stream);
+
 /* Bytes of workspace tree_accept_greedy needs (0 for invalid sizes or dtype). */
 size_t tree_accept_workspace_bytes(int B, int N, int V, int dtype);
 

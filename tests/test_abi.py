@@ -105,6 +105,32 @@ def test_attention_argument_errors():
     assert tvl.attn_tree_workspace_bytes(1, 22, 24, 5, 256, 4200, 2048) == 0
 
 
+def test_noalloc_attention_argument_errors():
+    """The no-allocation variant runs the same host checks and rejects sizes whose split
+    partials exceed its built-in scratch, before touching the device."""
+    L = tvl.lib()
+    f = _fake()
+
+    def call(B=1, N=22, Hq=24, Hkv=4, D=256, Tcap=4200, kt=0, vt=0, W=2048, ptr=f):
+        return L.attn_tree_verify_noalloc(B, N, Hq, Hkv, D, Tcap, kt, vt, W, 0.0625, *([ptr] * 8), None)
+
+    assert call(Hq=25) == tvl.TV_EINVAL
+    assert call(D=128) == tvl.TV_EUNSUPPORTED
+    assert call(kt=3) == tvl.TV_EUNSUPPORTED and b"supported pairs" in L.tv_last_error()
+    assert call(W=-1) == tvl.TV_EINVAL
+    assert call(ptr=None) == tvl.TV_EINVAL
+    # a shape whose split partials exceed the 64 MiB scratch (the split plan decides which)
+    big = None
+    for B in range(1, 160):
+        for Hkv in (1, 2, 3, 4):
+            for N, G in ((22, 6), (64, 8)):
+                if big is None and tvl.attn_tree_workspace_bytes(B, N, G * Hkv, Hkv, 256, 131136, 0) > 64 << 20:
+                    big = (B, N, G * Hkv, Hkv)
+    assert big is not None
+    assert call(B=big[0], N=big[1], Hq=big[2], Hkv=big[3], Tcap=131136, W=0) == tvl.TV_ERANGE
+    assert b"scratch" in L.tv_last_error()
+
+
 def test_validate_tree_and_path():
     parents, paths = trees_for(1, 3, "ddtree")
     parent, n = pad_trees(parents)

@@ -15,7 +15,7 @@ import os
 import torch
 
 __all__ = ["TreeVerifyError", "lib", "lib_path", "lin_tree_verify", "lin_tree_commit", "lin_tree_verify_commit",
-           "attn_tree_verify", "attn_tree_workspace_bytes", "tree_accept_greedy",
+           "attn_tree_verify", "attn_tree_verify_noalloc", "attn_tree_workspace_bytes", "tree_accept_greedy",
            "tree_accept_workspace_bytes", "kv_tree_compact", "conv_tree_verify", "conv_tree_commit",
            "validate_tree", "validate_path",
            "abi_version", "KV_TYPES", "EXPORTS"]
@@ -38,6 +38,7 @@ EXPORTS = {
                                     _i, _p, _p, _i, _p, _p, _p, _p]),
     "attn_tree_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
     "attn_tree_verify": (_i, [_i, _i, _i, _i, _i, _i, _i, _i, _i, _f, _p, _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
+    "attn_tree_verify_noalloc": (_i, [_i, _i, _i, _i, _i, _i, _i, _i, _i, _f, _p, _p, _p, _p, _p, _p, _p, _p, _p]),
     "tree_accept_workspace_bytes": (_sz, [_i, _i, _i, _i]),
     "tree_accept_greedy": (_i, [_i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
     "kv_tree_compact": (_i, [_i, _i, _i, _i, _i, _i, _p, _p, _p, _i, _p, _p, _p]),
@@ -209,6 +210,27 @@ def attn_tree_verify(q, k_cache, v_cache, k_type: str, v_type: str, n_past, pare
                                   float(scale), _ptr(parent), _ptr(n_nodes), _ptr(n_past), _ptr(q), _ptr(k_cache),
                                   _ptr(v_cache), _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
                                   _stream(q.device)))
+    return out, lse
+
+
+def attn_tree_verify_noalloc(q, k_cache, v_cache, k_type: str, v_type: str, n_past, parent, n_nodes, window: int,
+                             scale: float, out, lse=None):
+    """``attn_tree_verify`` without a workspace argument: the library's built-in scratch holds
+    the split partials, so the call allocates nothing on the device.  ``out`` (and ``lse``, if
+    wanted) must be passed in.  Calls that can overlap on one GPU race on the scratch."""
+    B, N, Hq, D = q.shape
+    Hkv, Tcap = k_cache.shape[1], k_cache.shape[2]
+    _dev(q, "q", torch.bfloat16)
+    _dev(k_cache, "k_cache", torch.uint8, (B, Hkv, Tcap, D // 32 * KV_BLOCK_BYTES[k_type]))
+    _dev(v_cache, "v_cache", torch.uint8, (B, Hkv, Tcap, D // 32 * KV_BLOCK_BYTES[v_type]))
+    _dev(n_past, "n_past", torch.int32, (B,))
+    _dev(parent, "parent", torch.int32, (B, N)); _dev(n_nodes, "n_nodes", torch.int32, (B,))
+    _dev(out, "out", torch.float32, (B, N, Hq, D))
+    if lse is not None:
+        _dev(lse, "lse", torch.float32, (B, N, Hq))
+    _check(lib().attn_tree_verify_noalloc(B, N, Hq, Hkv, D, Tcap, KV_TYPES[k_type], KV_TYPES[v_type], int(window),
+                                          float(scale), _ptr(parent), _ptr(n_nodes), _ptr(n_past), _ptr(q),
+                                          _ptr(k_cache), _ptr(v_cache), _ptr(out), _ptr(lse), _stream(q.device)))
     return out, lse
 
 

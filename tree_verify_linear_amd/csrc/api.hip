@@ -219,6 +219,27 @@ int attn_tree_verify(int B, int N, int Hq, int Hkv, int D, int Tcap, int k_type,
     return launch_attn(a, static_cast<hipStream_t>(stream));
 }
 
+int attn_tree_verify_noalloc(int B, int N, int Hq, int Hkv, int D, int Tcap, int k_type, int v_type, int window,
+                             float scale, const int32_t* parent, const int32_t* n_nodes, const int32_t* n_past,
+                             const void* q, const void* k_cache, const void* v_cache, float* out, float* lse,
+                             void* stream) {
+    clear_error();
+    const char* fn = "attn_tree_verify_noalloc";
+    const int st = check_attn(fn, B, N, Hq, Hkv, D, Tcap, k_type, v_type, window, scale, parent, n_nodes, n_past, q,
+                              k_cache, v_cache, out);
+    if (st != TV_OK) return st;
+    const size_t need = attn_workspace_bytes(B, N, Hq, Hkv, D, Tcap, window);
+    if (need == 0) return set_error(TV_ERANGE, "%s: sizes overflow", fn);
+    if (need > attn_scratch_capacity())
+        return set_error(TV_ERANGE, "%s: these sizes need %zu bytes of split partials, more than the %zu bytes of "
+                         "built-in scratch; use attn_tree_verify with a workspace", fn, need, attn_scratch_capacity());
+    void* ws = attn_scratch_device_ptr();
+    if (!ws) return TV_EDEVICE;                     // message set by the lookup
+    AttnArgs a{B, N, Hq, Hkv, D, Tcap, k_type, v_type, window, scale, parent, n_nodes, n_past, q,
+               static_cast<const uint8_t*>(k_cache), static_cast<const uint8_t*>(v_cache), out, lse, ws};
+    return launch_attn(a, static_cast<hipStream_t>(stream));
+}
+
 size_t tree_accept_workspace_bytes(int B, int N, int V, int dtype) {
     clear_error();
     if (B <= 0 || N <= 0 || N > TV_MAX_NODES || V <= 0 || (dtype != TV_F32 && dtype != TV_BF16)) return 0;

@@ -36,9 +36,16 @@
 //     sums the splits.  With a single split the kernel normalises and writes the output.
 #include <cfloat>
 #include <cmath>
+#include <mutex>
 #include <type_traits>
 
 #include "tv_internal.h"
+
+// Split partials for callers that cannot allocate (attn_tree_verify_noalloc): one array per
+// device, held for the life of the process.  Host code never passes this name to a kernel
+// (on the host it is only a stand-in); it uses the device address looked up once per device.
+static constexpr size_t kAttnScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kAttnScratchBytes];
 
 namespace tv {
 namespace {
@@ -749,6 +756,30 @@ int device_cu_count() {
         cached[dev] = cus;
     }
     return cached[dev];
+}
+
+size_t attn_scratch_capacity() { return kAttnScratchBytes; }
+
+void* attn_scratch_device_ptr() {
+    static std::mutex mu;
+    static void* ptrs[64] = {nullptr};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+        set_error(TV_EDEVICE, "attn_tree_verify_noalloc: no current HIP device");
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(mu);
+    if (!ptrs[dev]) {
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) {
+            set_error(TV_EDEVICE, "attn_tree_verify_noalloc: scratch lookup failed on device %d: %s", dev,
+                      hipGetErrorString(e));
+            return nullptr;
+        }
+        ptrs[dev] = p;
+    }
+    return ptrs[dev];
 }
 
 size_t attn_workspace_bytes(int B, int N, int Hq, int Hkv, int D_, int Tcap, int window) {

@@ -68,6 +68,8 @@ struct AttnArgs {
 };
 size_t attn_workspace_bytes(int B, int N, int Hq, int Hkv, int D, int Tcap, int window);
 int launch_attn(const AttnArgs& a, hipStream_t stream);
+size_t attn_scratch_capacity();       // bytes of the library's own split-partial scratch
+void* attn_scratch_device_ptr();      // its address on the current device (nullptr + error on failure)
 
 struct AcceptArgs {
     int B, N, V;
