@@ -228,7 +228,9 @@ int lin_tree_verify_commit(int B, int N, int Hk, int Hv, int dk, int dv, int dty
  *   scale      score scale (usually 1/sqrt(D)); finite
  *   parent, n_nodes  device, see "Tree representation"
  *   n_past     device, int32 [B]
- *   q          device, bf16 [B][N][Hq][D]; |q| must stay below 65504 (converted to fp16)
+ *   q          device, bf16 [B][N][Hq][D], any finite values (each row is rescaled by a power
+ *              of two before entering the matrix cores, so its range is not limited to fp16's);
+ *              the scores scale * <q, k> must stay within fp32 range
  *   k_cache    device, bytes [B][Hkv][Tcap][D/32 blocks of k_type]
  *   v_cache    device, bytes [B][Hkv][Tcap][D/32 blocks of v_type]
  *   out        device, fp32 [B][N][Hq][D], 16-byte aligned

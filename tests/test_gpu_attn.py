@@ -117,3 +117,46 @@ def test_deterministic_and_batch_invariant():
     el = float(np.max(np.abs(lb[0, :n] - l1[1, :n])))
     print(f"[attn batch invariance] out {e:.2e} x RMS, lse {el:.2e}")
     assert e <= 1e-5 and el <= 1e-5
+
+
+def _scaled_queries(A, factor_rows):
+    """A copy of A whose query rows (node, head) are multiplied by powers of two (exact in
+    bf16): factor_rows maps node -> factor."""
+    import dataclasses
+    from workloads import f32_to_bf16_bits
+    from oracle.delta import bf16_bits_to_f64
+    q = bf16_bits_to_f64(A.q)
+    for node, f in factor_rows.items():
+        q[:, node] *= f
+    return dataclasses.replace(A, q=f32_to_bf16_bits(q.astype(np.float32)))
+
+
+def test_query_range_beyond_fp16():
+    """Queries far outside fp16's range.  Each query row enters the matrix cores pre-scaled by
+    a power of two, so (1) every query times 2^20 with the scale times 2^-20, and (2) times
+    2^-30 with the scale times 2^30, give the unscaled call's outputs bit for bit; (3) single
+    nodes whose queries reach 10^5 .. 10^6 (beyond fp16's 65504) or 10^-9 match the oracle."""
+    import dataclasses
+    rng = np.random.default_rng(5)
+    parents = [tree_ddtree(rng, budget=22), tree_chain(7)]
+    A = gen_attn(83, parents, 24, 4, 256, [300, 120], "q8_0", "q4_0", 0)
+    o0, l0 = run_gpu(A)
+    for f in (2.0 ** 20, 2.0 ** -30):
+        Af = dataclasses.replace(_scaled_queries(A, {i: f for i in range(A.parent.shape[1])}), scale=A.scale / f)
+        of, lf = run_gpu(Af)
+        assert np.array_equal(of, o0, equal_nan=True) and np.array_equal(lf, l0, equal_nan=True), f
+    Am = _scaled_queries(A, {1: 2.0 ** 17, 3: 2.0 ** 18, 5: 2.0 ** -30})
+    out, lse = run_gpu(Am)
+    assert np.abs(bf16_max(Am.q)) > 65504.0
+    ro, rl = oracle.attn_tree_verify(Am.q, Am.k_cache, Am.v_cache, Am.k_type, Am.v_type, Am.n_past, Am.parent,
+                                     Am.n_nodes, Am.window, Am.scale, Am.Hkv)
+    mask = valid_rows(Am.n_nodes, Am.parent.shape[1])
+    e = rel_err(out, ro, mask)
+    el = float(np.max(np.abs(lse[mask] - rl[mask]) / np.maximum(1.0, np.abs(rl[mask]))))
+    print(f"[attn large queries] out {e:.2e} x RMS, lse rel {el:.2e}")
+    assert e <= TOL and el <= TOL_LSE
+
+
+def bf16_max(q):
+    from oracle.delta import bf16_bits_to_f64
+    return np.abs(bf16_bits_to_f64(q)).max()

@@ -17,9 +17,13 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libtreeverify.so")
 ARCH = "gfx950"
 
-# Packed-fp32 VALU ops are disabled for all device code; the rest is a plain -O3 build.
+# Packed-fp32 VALU ops are disabled for all device code.  Per-thread arrays are never moved
+# into LDS by the compiler: the kernels size their LDS themselves, and an array moved there
+# turns every register staging load into a load, wait and LDS store.  The rest is a plain
+# -O3 build.
 HIPFLAGS = ["-std=c++17", "-O3", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-mllvm", "-disable-promote-alloca-to-lds",
             "-Wall", "-Wno-unused-function", "-Wno-unknown-pragmas"]
 
 

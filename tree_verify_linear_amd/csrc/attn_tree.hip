@@ -12,26 +12,32 @@
 // 16 -- so every K/V byte is read from HBM once per split and reused by all of them.
 //
 // Layout of the work inside a workgroup (8 waves, two per SIMD, in two roles):
-//   * K/V slot tiles (32 slots) are copied raw into LDS with 16-byte loads issued one tile
-//     ahead.  Dequantisation is exact: d*q has at most 19 significant bits (fp16 d, <= 8-bit
-//     q), so it splits exactly into fp16 hi = RN(d*q) and lo = d*q - hi.
-//   * Scoring waves (4): the head dimension (256 = 8 quantisation blocks) is split in four
-//     quarters; scoring wave w owns blocks 2w, 2w+1 and computes S^T = K Q^T over those 64
-//     dimensions for all 9 row tiles on v_mfma_f32_16x16x32_f16 (K hi and lo as the A
-//     operand, Q in registers as the B operand, fp32 accumulate).  The partial scores of a row
-//     tile meet in LDS at the scoring wave that owns the tile's softmax.  The owner
-//     masks, runs an online softmax in the exp2 domain (the reference max moves only when a
-//     row max grows by more than 2^8; O is then rescaled) and writes P as an fp16 pair hi +
-//     lo (P to about 2^-22) to LDS in the PV A-operand layout (the score layout of S^T
-//     already is that layout, so no transpose).
+//   * K/V slot tiles (32 slots, one contiguous run of rows each) are copied raw from HBM into
+//     rings of LDS slots by direct global-to-LDS loads, K three tiles and V two tiles ahead of
+//     their first use, so several tiles per CU are in flight without holding registers.
+//   * Queries are pre-scaled per row by a power of two 2^-e (the row's largest magnitude lands
+//     in [2^14, 2^15)), so every bf16 query converts to fp16 exactly whatever its range; 2^e
+//     is folded into the row's score scale.
+//   * K enters the matrix cores as exact integers: one tile step ahead, the scoring waves
+//     convert the raw Q8_0 / Q4_0 codes into fp16 integers in the QK operand layout (plus
+//     each block's fp16 scale as fp32).  The QK^T product of each 32-element block is one
+//     v_mfma_f32_16x16x32_f16 (K integers x Q), and the block's per-slot scale is applied to
+//     the fp32 result: scores are exact products summed in fp32.
+//   * Scoring waves (4): wave w owns row tiles w and w + 4 over the whole head dimension, so
+//     no partial score leaves the wave.  Row tile 8 (more than 128 rows) is the exception:
+//     waves 1..3 compute its partial scores over blocks {0,1,2}, {3,4,5}, {6,7} and wave 0
+//     adds them and runs its softmax.  Each wave masks its rows, runs an online softmax in
+//     the exp2 domain (the reference max moves only when a row max grows by more than 2^8; O
+//     is then rescaled) and writes P as an fp16 pair hi + lo (P to about 2^-22) to LDS in the
+//     PV A-operand layout (the score layout of S^T already is that layout).
 //   * PV waves (4): PV wave w owns output columns 64w .. 64w+63 of all rows.  It dequantises
-//     its columns of V into fp16 hi/lo registers (the PV B operand) and accumulates
+//     its columns of V exactly into fp16 hi/lo registers (d*q has at most 19 significant
+//     bits, so hi = RN(d*q) and lo = d*q - hi) and accumulates
 //     O += P_hi V_hi + P_hi V_lo + P_lo V_hi (the dropped P_lo V_lo is ~2^-22 relative), one
 //     tile behind the scores.
-//   * Each SIMD carries one wave of each role, and the phases pair them up: while the scoring
-//     wave issues the QK^T matrix instructions the PV wave dequantises V and issues the first
-//     PV_EARLY row tiles of PV, and while the scoring wave runs the softmax the PV wave issues
-//     the remaining row tiles.
+//   * Two phases per tile step, one wave of each role per SIMD: the scoring waves' QK^T and K
+//     conversion beside the PV waves' V dequantisation and first PV row tiles, then the
+//     softmax beside the remaining PV row tiles.
 //   * Each split writes unnormalised O, its running max and sum; a combine pass rescales and
 //     sums the splits.  With a single split the kernel normalises and writes the output.
 #include <cfloat>
@@ -54,6 +60,7 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int D = 256;
 constexpr int TS = 32;                       // slots per tile
@@ -62,13 +69,59 @@ constexpr int THREADS = 64 * WAVES;
 constexpr int RTMAX = 9;                     // row tiles per row block
 constexpr int OWNMAX = (RTMAX + 3) / 4;      // softmax tiles owned per scoring wave
 constexpr int ROWS_PER_BLOCK = RTMAX * 16;   // 144
-constexpr int PV_EARLY = 2;                  // PV row tiles issued in phase 1 (the rest in phase 2)
+#ifndef TV_PV_EARLY
+#define TV_PV_EARLY 2
+#endif
+constexpr int PV_EARLY = TV_PV_EARLY;        // PV row tiles issued in phase 1 (the rest in phase 2)
 constexpr int MAXROW = 8 * 34;               // bytes of one slot's row (Q8_0, the larger)
+// Raw K/V tiles are copied straight from HBM into rings of LDS slots by direct global-to-LDS
+// loads (1 KiB per wave instruction), DK (K) and DV (V) tiles ahead of their first use.
+#ifndef TV_DK
+#define TV_DK 3
+#endif
+#ifndef TV_DV
+#define TV_DV 2
+#endif
+constexpr int DK = TV_DK, DV = TV_DV;
+constexpr int RK = DK + 2, RV = DV + 1;      // ring slots (see the schedule in attn_kernel)
+constexpr int SLOT = (TS * MAXROW + 1023) / 1024 * 1024;   // 9 KiB: whole wave instructions
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
 __device__ __forceinline__ f32x4 mfma_f16(const f16x8& a, const f16x8& b, const f32x4& c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// Wait until at most N of this wave's vector-memory operations are outstanding (loads return
+// in issue order, so the older ones are then complete).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+// Workgroup barrier for LDS traffic only: this wave's LDS operations are complete, then the
+// barrier.  Unlike __syncthreads it does not wait for outstanding global-to-LDS copies, which
+// must stay in flight across barriers; each copy is waited for explicitly before the barrier
+// that publishes it.  The signal fences keep the compiler from moving LDS accesses across.
+__device__ __forceinline__ void lds_barrier() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0xC07F);                  // lgkmcnt(0), other counters unchanged
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// One direct global-to-LDS copy instruction: lane l moves the 16 bytes at its `src` to LDS
+// byte address lds + 16 l (lds is wave-uniform, passed in M0).  Written as a statement of its
+// own so that the compiler neither reorders LDS accesses across it ("memory") nor inserts
+// waits for it: the copy has no result register, and every wait for it is an explicit
+// wait_vm.  (With the builtin, the compiler would wait for all copies before any later LDS
+// access, since it cannot tell the copy's destination from the other LDS arrays.)
+__device__ __forceinline__ void copy16_to_lds(const void* src, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" : : "s"(lds), "v"(src) : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)p));
 }
 
 template <int TYPE>
@@ -172,10 +225,9 @@ struct AttnLaunch {
 };
 
 struct AttnSmem {
-    __align__(16) uint8_t rawk[TS * MAXROW + 16];           // K rows of the tile being scored
-    __align__(16) uint8_t rawv[2][TS * MAXROW + 16];        // V rows, two tiles in flight
-    __align__(16) f32x4 spart[RTMAX][3][2][64];             // partial scores from non-owners
-    __align__(16) f32x4 sdump[2][64];                       // wave 0's copy of row tile 8 (not read)
+    __align__(16) f16x8 kop[2][2][8][64];                   // K integers in the QK operand layout
+    __align__(16) float kd[2][8][TS];                       // K block scales [block][slot]
+    __align__(16) f32x4 spart8[3][2][64];                   // row tile 8: partial scores of waves 1..3
     __align__(16) f16x8 pbuf[2][RTMAX][64];                 // P hi in the PV operand layout
     __align__(16) f16x8 pbuf_lo[2][RTMAX][64];              // P lo = P - P hi, same layout
     __align__(16) float alpha[2][RTMAX][16];                // O rescale factor per row
@@ -191,19 +243,66 @@ struct RowState {
     int node, dep, rlo;         // rlo: first committed slot the row sees
     uint64_t anc;
     float m, l;                 // running max (log2 domain, lane-group uniform), lane's sum
+    float sl2;                  // log2(e) * |scale| * 2^e of the row's query pre-scale
     bool on;                    // the row exists
 };
+
+// Blocks of row tile 8 whose partial scores scoring wave w (1..3) computes: [first, first+count).
+__device__ __forceinline__ int t8_first(int w) { return w == 1 ? 0 : (w == 2 ? 3 : 6); }
+__device__ __forceinline__ int t8_count(int w) { return w == 0 ? 0 : (w == 3 ? 2 : 3); }
+
+// One query row (bf16) as this lane's QK operand pieces: elements kb*32 + 8*g4 .. +7 for the 8
+// blocks.  The row is pre-scaled by 2^-e, e chosen per row so that its largest magnitude lands
+// in [2^14, 2^15): every bf16 value then converts to fp16 exactly (down to 2^-32 of the row's
+// maximum), whatever the query's range, and 2^e is folded into the row's score scale.  The
+// scale's sign is folded in too (exact), so the scores see a positive factor.
+// (The row address is always valid -- rows past the tree read node 0's row -- so the loads are
+// unconditional and absent rows are zeroed after them.)
+__device__ __forceinline__ int load_qrow(const uint16_t* qrow, bool ok, int g4, uint4 (&w)[8]) {
+    uint32_t mx = 0;
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb) {
+        const uint4 x = *reinterpret_cast<const uint4*>(qrow + kb * 32 + 8 * g4);
+        w[kb] = ok ? x : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb) {
+        const uint32_t u[4] = {w[kb].x, w[kb].y, w[kb].z, w[kb].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t lo = (u[e] << 16) & 0x7fff0000u, hi = u[e] & 0x7fff0000u;
+            mx = lo > mx ? lo : mx;
+            mx = hi > mx ? hi : mx;
+        }
+    }
+    // the row's maximum magnitude as fp32 bits (order of non-negative floats = order of bits)
+    uint32_t t = __shfl_xor(mx, 16);
+    mx = t > mx ? t : mx;
+    t = __shfl_xor(mx, 32);
+    mx = t > mx ? t : mx;
+    const int E = static_cast<int>(mx >> 23) - 127;          // exponent of the maximum
+    return (mx == 0u || E > 126) ? 0 : clampi(E - 14, -100, 100);
+}
+__device__ __forceinline__ f16x8 qrow_op(const uint4& w, int e, uint32_t qflip) {
+    const float s = __uint_as_float(static_cast<uint32_t>(127 - e) << 23);   // 2^-e
+    const uint32_t u[4] = {w.x ^ qflip, w.y ^ qflip, w.z ^ qflip, w.w ^ qflip};
+    f16x8 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        o[2 * i] = static_cast<_Float16>(__uint_as_float(u[i] << 16) * s);
+        o[2 * i + 1] = static_cast<_Float16>(__uint_as_float(u[i] & 0xffff0000u) * s);
+    }
+    return o;
+}
 
 template <int KT, int VT>
 __global__ __launch_bounds__(THREADS, 1) void attn_kernel(AttnLaunch L) {
     using KF = Fmt<KT>;
     using VF = Fmt<VT>;
     constexpr int KCH = TS * KF::ROW / 16, VCH = TS * VF::ROW / 16;    // 16-byte pieces per tile
-    // Staging threads: every wave but scoring wave 0, which owns a third softmax row tile
-    // (9 row tiles over 4 scoring waves) and would otherwise set the pace of phase 2.
-    constexpr int STG = THREADS - 64;
-    constexpr int KPT = (KCH + STG - 1) / STG, VPT = (VCH + STG - 1) / STG;
     __shared__ AttnSmem sm;
+    __shared__ __align__(1024) uint8_t ringk[RK][SLOT];     // raw K tiles (see dma_tile)
+    __shared__ __align__(1024) uint8_t ringv[RV][SLOT];     // raw V tiles
     const AttnArgs& a = L.a;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6) & (WAVES - 1);   // wave-uniform
@@ -245,112 +344,158 @@ __global__ __launch_bounds__(THREADS, 1) void attn_kernel(AttnLaunch L) {
 
     const uint8_t* kbase = a.k_cache + (static_cast<size_t>(b) * a.Hkv + kvh) * a.Tcap * KF::ROW;
     const uint8_t* vbase = a.v_cache + (static_cast<size_t>(b) * a.Hkv + kvh) * a.Tcap * VF::ROW;
-    // raw tile staging: 16-byte pieces, rows past the cache end read as zero
-    uint4 rk[KPT], rv[VPT];
-    auto gload = [&](int tile) {
+    // Raw tiles in LDS rings, copied by direct global-to-LDS loads.  Instruction i of a tile
+    // moves bytes 1024 i .. 1024 i + 1023 of the tile's contiguous run of rows (lane l: 16 bytes
+    // at 1024 i + 16 l).  Pieces past the tile (the last instruction's upper half) or past the
+    // cache end re-read the tile's last piece inside the cache: they land in the slot's padding
+    // or in rows that are never visible (masked scores, zeroed V scales).  The PV waves copy K,
+    // the scoring waves copy V, so no wave reads a ring it has copies in flight for: waits are
+    // explicit (wait_vm before the barrier that publishes a tile), never implied by a read.
+    constexpr int NIK = (TS * KF::ROW + 1023) / 1024, NIV = (TS * VF::ROW + 1023) / 1024;
+    // instructions per tile issued by this wave (i = wl, wl + 4, ...): the same count for every
+    // tile, so a fixed number of tiles still in flight is a fixed vmcnt
+    const int cntk = (NIK - wl + 3) / 4, cntv = (NIV - wl + 3) / 4;
+    auto dma_tile = [&](const uint8_t* base, int rowbytes, int nch, uint8_t* slot, int tile) {
         const int t0 = s0 + tile * TS;
-        const int slots_ok = a.Tcap - t0 < TS ? a.Tcap - t0 : TS;
-#pragma unroll
-        for (int x = 0; x < KPT; ++x) {
-            const int c = (tid - 64) + x * STG;
-            rk[x] = make_uint4(0, 0, 0, 0);
-            if (c < KCH && c * 16 < slots_ok * KF::ROW)
-                rk[x] = *reinterpret_cast<const uint4*>(kbase + static_cast<size_t>(t0) * KF::ROW + c * 16);
-        }
-#pragma unroll
-        for (int x = 0; x < VPT; ++x) {
-            const int c = (tid - 64) + x * STG;
-            rv[x] = make_uint4(0, 0, 0, 0);
-            if (c < VCH && c * 16 < slots_ok * VF::ROW)
-                rv[x] = *reinterpret_cast<const uint4*>(vbase + static_cast<size_t>(t0) * VF::ROW + c * 16);
+        const int last = (a.Tcap - t0 < TS ? a.Tcap - t0 : TS) * rowbytes / 16 - 1;   // t0 < Tcap
+        const uint8_t* src = base + static_cast<size_t>(t0) * rowbytes;
+        const int ni = (TS * rowbytes + 1023) / 1024;
+        for (int i = wl; i < ni; i += 4) {
+            int c = i * 64 + lane;
+            c = c < nch ? c : nch - 1;
+            c = c < last ? c : last;
+            copy16_to_lds(src + c * 16, __builtin_amdgcn_readfirstlane(lds_address(slot + i * 1024)));
         }
     };
-    auto lstore = [&](int tile) {
-#pragma unroll
-        for (int x = 0; x < KPT; ++x) {
-            const int c = (tid - 64) + x * STG;
-            if (c < KCH) *reinterpret_cast<uint4*>(&sm.rawk[c * 16]) = rk[x];
-        }
-#pragma unroll
-        for (int x = 0; x < VPT; ++x) {
-            const int c = (tid - 64) + x * STG;
-            if (c < VCH) *reinterpret_cast<uint4*>(&sm.rawv[tile & 1][c * 16]) = rv[x];
+    auto dma_k = [&](int tile) { dma_tile(kbase, KF::ROW, KCH, &ringk[tile % RK][0], tile); };
+    auto dma_v = [&](int tile) { dma_tile(vbase, VF::ROW, VCH, &ringv[tile % RV][0], tile); };
+    // Wait for a copied tile: `after` tiles copied since by this wave may stay in flight; a
+    // count short of the steady state (the last tiles) waits for everything.
+    auto wait_k = [&](int after) {
+        if (after == DK) {
+            if (cntk == 1) wait_vm<DK>();
+            else if (cntk == 2) wait_vm<2 * DK>();
+            else if (cntk == 3) wait_vm<3 * DK>();
+            else wait_vm<0>();
+        } else if (after == DK + 1) {
+            if (cntk == 1) wait_vm<DK + 1>();
+            else if (cntk == 2) wait_vm<2 * (DK + 1)>();
+            else if (cntk == 3) wait_vm<3 * (DK + 1)>();
+            else wait_vm<0>();
+        } else {
+            wait_vm<0>();
         }
     };
-    // Raw tile k+1 into LDS (rawk was last read by the scores of tile k, rawv[(k+1)&1] by the
-    // dequantisation of tile k-1, both before the phase barrier), then loads of tile k+2.
-    const bool stager = tid >= 64;
-    auto stage = [&](int k) {
-        if (stager && k + 1 < ntiles) {
-            lstore(k + 1);
-            if (k + 2 < ntiles) gload(k + 2);
+    auto wait_v = [&](int after) {
+        if (after == DV) {
+            if (cntv == 1) wait_vm<DV>();
+            else if (cntv == 2) wait_vm<2 * DV>();
+            else if (cntv == 3) wait_vm<3 * DV>();
+            else wait_vm<0>();
+        } else {
+            wait_vm<0>();
+        }
+    };
+    // K integers of tile `tile` (raw rows in its ring slot) into the QK operand buffer
+    // kop[tile&1] and their block scales into kd[tile&1]: scoring wave w converts blocks 2w, 2w+1.
+    // Lane (g4, l16) of slot half st holds slot 16 st + l16, elements 8 g4 .. 8 g4 + 7 of the
+    // block: exactly the MFMA A operand of that (half, block), so the scoring waves read it
+    // back with one conflict-free 16-byte load per lane.
+    auto convert_k = [&](int tile) {
+        const int buf = tile & 1;
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+            const uint8_t* krow = &ringk[tile % RK][(16 * st + l16) * KF::ROW];
+            sm.kop[buf][st][2 * wl][lane] = block_ints8<KT, false>(krow, 2 * wl, g4);
+            sm.kop[buf][st][2 * wl + 1][lane] = block_ints8<KT, true>(krow, 2 * wl + 1, g4);
+            if (g4 < 2) {
+                const int kb = 2 * wl + g4;
+                sm.kd[buf][kb][16 * st + l16] = static_cast<float>(block_scale(krow + kb * KF::BLK));
+            }
         }
     };
 
-    if (stager && ntiles > 0) {
-        gload(0);
-        lstore(0);
-        if (ntiles > 1) gload(1);
+    // Prologue: K tiles 0 .. DK+1 and V tiles 0 .. DV-1 in flight; K tile 0 converted.
+    const int nk0 = ntiles < DK + 2 ? ntiles : DK + 2, nv0 = ntiles < DV ? ntiles : DV;
+    if (!scorer) {
+        for (int t = 0; t < nk0; ++t) dma_k(t);
+        wait_k(nk0 - 1);                                     // tile 0
+    } else {
+        for (int t = 0; t < nv0; ++t) dma_v(t);
     }
-    __syncthreads();
+    lds_barrier();
+    if (scorer && ntiles > 0) convert_k(0);
+    if (!scorer) wait_k(nk0 - 2);                           // tile 1 (converted in step 0)
+    lds_barrier();
 
-    // Barrier sequence, identical in both roles: one above, two per tile step k = 0..ntiles
+    // Barrier sequence, identical in both roles: two above, two per tile step k = 0..ntiles
     // (after phase 1 and after phase 2), one before the epilogue's output writes.
     if (scorer) {
         // ------------------------------------------------------------ scoring waves
-        // Q of all row tiles, this wave's two blocks, as the QK B operand
-        // Row tiles in this wave's own order: its softmax tiles wl and wl + 4 first, then tile 8
-        // (wave 0's third softmax tile), then the other six.  With the order fixed per wave,
-        // the partial scores the wave keeps sit at compile-time register positions.
-        auto rtile = [&](int i) -> int {
-            if (i == 0) return wl;
-            if (i == 1) return wl + 4;
-            if (i == 2) return 8;
-            const int x = (i - 3) % 3, half = (i - 3) / 3;
-            return 4 * half + (x < wl ? x : x + 1);
-        };
-        // The sign of the scale is folded into Q (exact), so the scores are scaled by a positive
-        // factor and the row maximum can be taken before scaling.
+        // Wave w scores row tiles w and w + 4 over the whole head dimension, so no partial
+        // score leaves the wave.  Row tile 8 (present only for more than 128 rows) is the
+        // exception: waves 1..3 compute its partial scores over blocks {0,1,2}, {3,4,5}, {6,7}
+        // and wave 0 adds them up and runs its softmax (wave 0 owns three softmax tiles and
+        // no staging, waves 1..3 two softmax tiles, the extra matrix work and staging).
         const uint32_t qflip = a.scale < 0.f ? 0x80008000u : 0u;
-        f16x8 qop[RTMAX][2];
-#pragma unroll
-        for (int i = 0; i < RTMAX; ++i) {
-            const int r = rtile(i);
-            const int row = rowbase + r * 16 + l16;
-            const int node = row / L.G, hh = row - node * L.G;
-            const bool ok = r < RT && row < L.rows && node < n;
-            const uint16_t* qrow = static_cast<const uint16_t*>(a.q) +
-                                   ((static_cast<size_t>(b) * N + (ok ? node : 0)) * a.Hq + kvh * L.G + hh) * D;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                uint4 w = make_uint4(0, 0, 0, 0);
-                if (ok) w = *reinterpret_cast<const uint4*>(qrow + (2 * wl + kb) * 32 + 8 * g4);
-                const uint32_t u[4] = {w.x ^ qflip, w.y ^ qflip, w.z ^ qflip, w.w ^ qflip};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    qop[i][kb][2 * e] = static_cast<_Float16>(__uint_as_float(u[e] << 16));
-                    qop[i][kb][2 * e + 1] = static_cast<_Float16>(__uint_as_float(u[e] & 0xffff0000u));
-                }
-            }
-        }
-        // softmax rows this wave owns: row tiles wl, wl + 4, wl + 8
+        const float sl2b = fabsf(a.scale) * kLog2e;
+        const int n8 = t8_count(wl), f8 = t8_first(wl);
+        f16x8 qop[2][8], q8op[3];
         RowState rs[OWNMAX];
         int rlo_max[OWNMAX];
-        f32x4 own[OWNMAX][2];
 #pragma unroll
         for (int j = 0; j < OWNMAX; ++j) {
-            const int r = wl + 4 * j;
-            const int row = rowbase + r * 16 + l16;
-            const int node = row / L.G;
-            rs[j].on = r < RT && row < L.rows && node < n;
-            rs[j].node = rs[j].on ? node : 0;
-            rs[j].dep = rs[j].on ? sm.dep[node] : 0;
-            rs[j].anc = rs[j].on ? sm.anc[node] : 0ull;
-            rs[j].rlo = W ? T + rs[j].dep - W + 1 : 0;
+            rs[j].on = false;
+            rs[j].node = rs[j].dep = rs[j].rlo = 0;
+            rs[j].anc = 0ull;
             rs[j].m = -INFINITY;
             rs[j].l = 0.f;
-            // a committed tile is unmasked for this row tile when every row sees all its
-            // slots (rows that do not exist are cleared separately)
+            rs[j].sl2 = FLT_MIN;
+        }
+        q8op[0] = q8op[1] = q8op[2] = f16x8{};
+        auto setup_row = [&](auto jc) {
+            constexpr int j = decltype(jc)::value;
+            const int r = j < 2 ? wl + 4 * j : 8;
+            const int row = rowbase + r * 16 + l16;
+            const int node = row / L.G, hh = row - node * L.G;
+            const bool on = r < RT && row < L.rows && node < n;
+            const uint16_t* qrow = static_cast<const uint16_t*>(a.q) +
+                                   ((static_cast<size_t>(b) * N + (on ? node : 0)) * a.Hq + kvh * L.G + hh) * D;
+            uint4 qw[8];
+            const int qe = load_qrow(qrow, on, g4, qw);
+            if constexpr (j < 2) {
+#pragma unroll
+                for (int kb = 0; kb < 8; ++kb) qop[j][kb] = qrow_op(qw[kb], qe, qflip);
+            } else {
+                // blocks {0,1,2}, {3,4,5}, {6,7} for waves 1, 2, 3 (static indices, uniform branches)
+                if (wl == 1) {
+                    q8op[0] = qrow_op(qw[0], qe, qflip); q8op[1] = qrow_op(qw[1], qe, qflip);
+                    q8op[2] = qrow_op(qw[2], qe, qflip);
+                } else if (wl == 2) {
+                    q8op[0] = qrow_op(qw[3], qe, qflip); q8op[1] = qrow_op(qw[4], qe, qflip);
+                    q8op[2] = qrow_op(qw[5], qe, qflip);
+                } else if (wl == 3) {
+                    q8op[0] = qrow_op(qw[6], qe, qflip); q8op[1] = qrow_op(qw[7], qe, qflip);
+                }
+            }
+            rs[j].on = on;
+            rs[j].node = on ? node : 0;
+            rs[j].dep = on ? sm.dep[node] : 0;
+            rs[j].anc = on ? sm.anc[node] : 0ull;
+            rs[j].rlo = W ? T + rs[j].dep - W + 1 : 0;
+            // |scale| * log2(e) * 2^e, kept positive (a zero scale becomes the smallest normal
+            // float: the scores then vanish and the weights are uniform, as for scale 0)
+            rs[j].sl2 = fmaxf(ldexpf(sl2b, qe), FLT_MIN);
+        };
+        setup_row(std::integral_constant<int, 0>{});
+        setup_row(std::integral_constant<int, 1>{});
+        // row tile 8 is loaded by every scoring wave (wave 0 for its softmax scale, waves 1..3
+        // for their blocks of its scores)
+        if (RT > 8) setup_row(std::integral_constant<int, 2>{});
+#pragma unroll
+        for (int j = 0; j < OWNMAX; ++j) {
+            // a committed tile is unmasked for this row tile when every row sees all its slots
+            // (rows that do not exist are cleared separately)
             int rm = rs[j].on ? rs[j].rlo : -0x7fffffff;
 #pragma unroll
             for (int o = 1; o < 16; o <<= 1) {
@@ -358,130 +503,143 @@ __global__ __launch_bounds__(THREADS, 1) void attn_kernel(AttnLaunch L) {
                 rm = t > rm ? t : rm;
             }
             rlo_max[j] = __builtin_amdgcn_readfirstlane(rm);
-            own[j][0] = own[j][1] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
-        // |scale| * log2(e), kept positive (a zero scale becomes the smallest normal float: the
-        // scores then vanish and the weights are uniform, as they are for scale 0)
-        const float sl2 = fmaxf(fabsf(a.scale) * kLog2e, FLT_MIN);
+        const bool own0 = wl < RT, own1 = wl + 4 < RT;       // wave-uniform
+        const bool has8 = RT > 8;
 
-        for (int k = 0; k <= ntiles; ++k) {
-            // phase 1: partial scores of tile k
-            if (k < ntiles) {
-                // both slot halves' K operands first, so the second half's LDS reads and
-                // dequantisation overlap the first half's matrix work
-                f16x8 kh[2][2], kl[2][2];
+        // The tile loop of one scoring wave, specialised on what the wave holds so that the
+        // inner loop has no branches: NJ own row tiles (0..2), the blocks of row tile 8 whose
+        // partial scores it computes (W8 = 1, 2, 3: blocks {0,1,2}, {3,4,5}, {6,7}; 0: none)
+        // and whether it runs row tile 8's softmax (S8, wave 0).
+        auto scoring_loop = [&](auto njc, auto w8c, auto s8c) {
+            constexpr int NJ = decltype(njc)::value;
+            constexpr int W8 = decltype(w8c)::value;
+            constexpr bool S8 = decltype(s8c)::value;
+            constexpr int F8 = W8 == 1 ? 0 : (W8 == 2 ? 3 : 6);
+            constexpr int C8 = W8 == 0 ? 0 : (W8 == 3 ? 2 : 3);
+            constexpr int NS = NJ + (S8 ? 1 : 0);          // softmax row tiles
+            f32x4 own[OWNMAX][2];
+            for (int k = 0; k <= ntiles; ++k) {
+                // phase 1: scores of tile k.  Per slot half: the K integers of all 8 blocks
+                // against Q on the matrix cores (independent products, issued back to back),
+                // then each block's per-slot scale applied and summed in fp32.
+                if (k < ntiles) {
+                    const int buf = k & 1;
 #pragma unroll
-                for (int st = 0; st < 2; ++st) {
-                    const uint8_t* krow = &sm.rawk[(16 * st + l16) * KF::ROW];
-                    const f16x8 d0 = block_scale(krow + 2 * wl * KF::BLK);
-                    const f16x8 d1 = block_scale(krow + (2 * wl + 1) * KF::BLK);
-                    split_exact(block_ints8<KT, false>(krow, 2 * wl, g4), d0, kh[st][0], kl[st][0]);
-                    split_exact(block_ints8<KT, true>(krow, 2 * wl + 1, g4), d1, kh[st][1], kl[st][1]);
-                }
+                    for (int st = 0; st < 2; ++st) {
+                        f32x4 sa[NJ > 0 ? NJ : 1], s8 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int st = 0; st < 2; ++st) {
-                    const f16x8 (&ah)[2] = kh[st];
-                    const f16x8 (&al)[2] = kl[st];
+                        for (int h = 0; h < 4; ++h) {                // blocks 2h, 2h+1
+                            f16x8 ka[2];
+                            f32x4 d4[2];
 #pragma unroll
-                    for (int i = 0; i < RTMAX; ++i) {
-                        const int r = rtile(i);
-                        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                            for (int x = 0; x < 2; ++x) {
+                                ka[x] = sm.kop[buf][st][2 * h + x][lane];
+                                d4[x] = *reinterpret_cast<const f32x4*>(&sm.kd[buf][2 * h + x][16 * st + 4 * g4]);
+                            }
+                            const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+                            f32x4 acc[NJ > 0 ? NJ : 1][2], acc8[2];
 #pragma unroll
-                        for (int kb = 0; kb < 2; ++kb) {
-                            acc = mfma_f16(ah[kb], qop[i][kb], acc);
-                            acc = mfma_f16(al[kb], qop[i][kb], acc);
+                            for (int x = 0; x < 2; ++x) {
+#pragma unroll
+                                for (int jj = 0; jj < NJ; ++jj) acc[jj][x] = mfma_f16(ka[x], qop[jj][2 * h + x], z);
+                            }
+#pragma unroll
+                            for (int x = 0; x < 2; ++x) {
+                                const int kb = 2 * h + x;
+                                if (kb >= F8 && kb < F8 + C8) acc8[x] = mfma_f16(ka[x], q8op[kb - F8 < 3 ? kb - F8 : 0], z);
+                            }
+#pragma unroll
+                            for (int jj = 0; jj < NJ; ++jj) {
+#pragma unroll
+                                for (int x = 0; x < 2; ++x) {
+                                    if (h == 0 && x == 0) sa[jj] = d4[0] * acc[jj][0];
+                                    else sa[jj] += d4[x] * acc[jj][x];
+                                }
+                            }
+#pragma unroll
+                            for (int x = 0; x < 2; ++x) {
+                                const int kb = 2 * h + x;
+                                if (kb >= F8 && kb < F8 + C8) s8 += d4[x] * acc8[x];
+                            }
                         }
-                        if (i < 2) {
-                            own[i][st] = acc;
-                        } else if (i == 2) {
-                            // row tile 8: wave 0 keeps it; the other waves' copies are what it
-                            // reads (wave 0's store goes to a dump slot, so there is no branch)
-                            own[2][st] = acc;
-                            f32x4* dst = wl == 0 ? &sm.sdump[st][lane] : &sm.spart[8][(wl - 1) & 3][st][lane];
-                            *dst = acc;
-                        } else {
-                            sm.spart[r][(wl - (r & 3) - 1) & 3][st][lane] = acc;
-                        }
+#pragma unroll
+                        for (int jj = 0; jj < NJ; ++jj) own[jj][st] = sa[jj];
+                        if constexpr (C8 > 0) sm.spart8[W8 - 1][st][lane] = s8;
                     }
                 }
-            }
-            __syncthreads();
-            // phase 2: stage the next tile; softmax of tile k for the owned row tiles
-            stage(k);
-            if (k < ntiles) {
-                const int t0 = s0 + k * TS;
-                const int bufk = k & 1;
-                // The owned row tiles (two, three for wave 0) go through each step together, so
-                // their independent chains interleave.
-                auto softmax = [&](auto njc) {
-                    constexpr int NJ = decltype(njc)::value;
-                    float x[NJ][8];        // unscaled scores
+                // K of tile k+1 into the other operand buffer (read by the scores of step k+1)
+                if (k + 1 < ntiles) convert_k(k + 1);
+                lds_barrier();
+                // phase 2: softmax of tile k for the owned row tiles
+                if (k < ntiles && NS > 0) {
+                    const int t0 = s0 + k * TS;
+                    const int bufk = k & 1;
+                    if constexpr (S8) {
 #pragma unroll
-                    for (int j = 0; j < NJ; ++j) {
-                        const int r = wl + 4 * j;
-                        f32x4 pa_[3], pb_[3];
+                        for (int st = 0; st < 2; ++st)
+                            own[2][st] = (sm.spart8[0][st][lane] + sm.spart8[1][st][lane]) + sm.spart8[2][st][lane];
+                    }
+                    // The owned row tiles (two, three for wave 0) go through each step together,
+                    // so their independent chains interleave.
+                    float x[NS > 0 ? NS : 1][8];        // unscaled scores
 #pragma unroll
-                        for (int src = 0; src < 3; ++src) {
-                            pa_[src] = sm.spart[r][src][0][lane];
-                            pb_[src] = sm.spart[r][src][1][lane];
-                        }
-                        const f32x4 sa = (own[j][0] + pa_[0]) + (pa_[1] + pa_[2]);
-                        const f32x4 sb = (own[j][1] + pb_[0]) + (pb_[1] + pb_[2]);
+                    for (int jj = 0; jj < NS; ++jj) {
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
-                            x[j][e] = sa[e];
-                            x[j][4 + e] = sb[e];
+                            x[jj][e] = own[jj][0][e];
+                            x[jj][4 + e] = own[jj][1][e];
                         }
                     }
 #pragma unroll
-                    for (int j = 0; j < NJ; ++j) {
-                        const bool fast = t0 + TS <= (T < s1 ? T : s1) && t0 >= rlo_max[j];
+                    for (int jj = 0; jj < NS; ++jj) {
+                        const bool fast = t0 + TS <= (T < s1 ? T : s1) && t0 >= rlo_max[jj];
                         if (!fast) {
 #pragma unroll
                             for (int e = 0; e < 8; ++e) {
                                 const int slot = t0 + (e < 4 ? 4 * g4 + e : 16 + 4 * g4 + (e - 4));
-                                bool vis = rs[j].on && slot < s1;
+                                bool vis = rs[jj].on && slot < s1;
                                 if (slot < T) {
-                                    vis = vis && slot >= rs[j].rlo;
+                                    vis = vis && slot >= rs[jj].rlo;
                                 } else {
                                     const int jn = slot - T;     // < n <= 64 whenever slot < s1
-                                    vis = vis && jn < TV_MAX_NODES && ((rs[j].anc >> (jn & 63)) & 1ull) &&
-                                          (W == 0 || rs[j].dep - sm.dep[jn & 63] < W);
+                                    vis = vis && jn < TV_MAX_NODES && ((rs[jj].anc >> (jn & 63)) & 1ull) &&
+                                          (W == 0 || rs[jj].dep - sm.dep[jn & 63] < W);
                                 }
-                                x[j][e] = vis ? x[j][e] : -INFINITY;
+                                x[jj][e] = vis ? x[jj][e] : -INFINITY;
                             }
                         }
                     }
-                    // (rows past the tree are not masked on unmasked tiles: their Q is zero,
-                    // so their weights stay finite, and nothing reads their results)
-                    float mt[NJ];
+                    // (rows past the tree are not masked on unmasked tiles: their Q is zero, so
+                    // their weights stay finite, and nothing reads their results)
+                    float mt[NS > 0 ? NS : 1];
 #pragma unroll
-                    for (int j = 0; j < NJ; ++j) {
-                        mt[j] = x[j][0];
+                    for (int jj = 0; jj < NS; ++jj) {
+                        mt[jj] = x[jj][0];
 #pragma unroll
-                        for (int e = 1; e < 8; ++e) mt[j] = fmaxf(mt[j], x[j][e]);
+                        for (int e = 1; e < 8; ++e) mt[jj] = fmaxf(mt[jj], x[jj][e]);
                     }
                     // the row's 32 slots sit in the four lane groups: max over l, l^16, l^32
 #pragma unroll
-                    for (int j = 0; j < NJ; ++j) {
-                        const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(mt[j]), __float_as_uint(mt[j]), false, false);
-                        mt[j] = fmaxf(__uint_as_float(s16[0]), __uint_as_float(s16[1]));
+                    for (int jj = 0; jj < NS; ++jj) {
+                        const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(mt[jj]), __float_as_uint(mt[jj]), false, false);
+                        mt[jj] = fmaxf(__uint_as_float(s16[0]), __uint_as_float(s16[1]));
                     }
 #pragma unroll
-                    for (int j = 0; j < NJ; ++j) {
-                        const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt[j]), __float_as_uint(mt[j]), false, false);
-                        mt[j] = fmaxf(__uint_as_float(s32[0]), __uint_as_float(s32[1])) * sl2;
+                    for (int jj = 0; jj < NS; ++jj) {
+                        const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt[jj]), __float_as_uint(mt[jj]), false, false);
+                        mt[jj] = fmaxf(__uint_as_float(s32[0]), __uint_as_float(s32[1])) * rs[jj].sl2;
                     }
 #pragma unroll
-                    for (int j = 0; j < NJ; ++j) {
-                        const int r = wl + 4 * j;
+                    for (int jj = 0; jj < NS; ++jj) {
+                        const int r = jj < 2 ? wl + 4 * jj : 8;
                         // Lazy rescaling: P is taken against a reference max that moves only when
                         // the row max grows by more than 2^8 (so P <= 256); alpha is 1 otherwise.
-                        const bool grow = mt[j] > rs[j].m + 8.f;
+                        const bool grow = mt[jj] > rs[jj].m + 8.f;
                         const bool anyg = __builtin_amdgcn_ballot_w64(grow) != 0;
-                        const float mnew = grow ? mt[j] : rs[j].m;
-                        const float al = rs[j].m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(rs[j].m - mnew);
-                        rs[j].m = mnew;
+                        const float mnew = grow ? mt[jj] : rs[jj].m;
+                        const float al = rs[jj].m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(rs[jj].m - mnew);
+                        rs[jj].m = mnew;
                         const float m = mnew == -INFINITY ? 0.f : mnew;      // then every x is -inf
                         // P = hi + lo in fp16 (lo is the rounding residual of hi), so P enters
                         // the PV products to about 2^-22 relative
@@ -489,28 +647,49 @@ __global__ __launch_bounds__(THREADS, 1) void attn_kernel(AttnLaunch L) {
                         float ps = 0.f;
 #pragma unroll
                         for (int e = 0; e < 8; ++e) {
-                            pe[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[j][e], sl2, -m));
+                            pe[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[jj][e], rs[jj].sl2, -m));
                             ps += pe[e];
                         }
                         uint32_t ph[4], pl[4];
 #pragma unroll
                         for (int e = 0; e < 4; ++e) split_p2(pe[2 * e], pe[2 * e + 1], ph[e], pl[e]);
-                        rs[j].l = rs[j].l * al + ps;
+                        rs[jj].l = rs[jj].l * al + ps;
                         *reinterpret_cast<uint4*>(&sm.pbuf[bufk][r][lane]) = make_uint4(ph[0], ph[1], ph[2], ph[3]);
                         *reinterpret_cast<uint4*>(&sm.pbuf_lo[bufk][r][lane]) = make_uint4(pl[0], pl[1], pl[2], pl[3]);
                         if (g4 == 0) sm.alpha[bufk][r][l16] = al;          // row l16's factor
                         if (lane == 0) sm.grow[bufk][r] = anyg;
                     }
-                };
-                if (wl == 0) softmax(std::integral_constant<int, OWNMAX>{});    // row tile 8 too
-                else softmax(std::integral_constant<int, 2>{});
+                }
+                // copy V tile k+DV (its slot's tile k-1 was dequantised in phase 1); V tile k is
+                // dequantised in phase 1 of the next step
+                if (k + DV < ntiles) dma_v(k + DV);
+                wait_v(ntiles - 1 - k < DV ? ntiles - 1 - k : DV);
+                lds_barrier();
             }
-            __syncthreads();
+        };
+        using I0 = std::integral_constant<int, 0>;
+        using I1 = std::integral_constant<int, 1>;
+        using I2 = std::integral_constant<int, 2>;
+        using I3 = std::integral_constant<int, 3>;
+        using BF = std::integral_constant<bool, false>;
+        using BT = std::integral_constant<bool, true>;
+        if (has8) {
+            if (wl == 0) scoring_loop(I2{}, I0{}, BT{});
+            else if (wl == 1) scoring_loop(I2{}, I1{}, BF{});
+            else if (wl == 2) scoring_loop(I2{}, I2{}, BF{});
+            else scoring_loop(I2{}, I3{}, BF{});
+        } else if (own1) {
+            scoring_loop(I2{}, I0{}, BF{});
+        } else if (own0) {
+            scoring_loop(I1{}, I0{}, BF{});        // small trees: one row tile
+        } else {
+            scoring_loop(I0{}, I0{}, BF{});        // no row tile: staging and barriers only
         }
         // epilogue: row maxima and sums for the PV waves (and the split partials)
 #pragma unroll
         for (int j = 0; j < OWNMAX; ++j) {
-            const int r = wl + 4 * j;
+            const int r = j < 2 ? wl + 4 * j : 8;
+            if (j == 2 && wl != 0) continue;
             float l = rs[j].l;
             l += __shfl_xor(l, 16);
             l += __shfl_xor(l, 32);
@@ -534,7 +713,9 @@ __global__ __launch_bounds__(THREADS, 1) void attn_kernel(AttnLaunch L) {
             for (int jj = 0; jj < 4; ++jj) oacc[r][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
 
         // O += P V for one row tile of tile k-1 (P hi/lo from LDS, V operands in registers)
-        auto pv_rowtile = [&](int r, int bufp, const f16x8 (&bh)[4], const f16x8 (&bl)[4]) {
+        auto pv_rowtile = [&](auto rc, int bufp, const f16x8 (&bh)[4], const f16x8 (&bl)[4]) {
+            constexpr int r = decltype(rc)::value;
+            if (r >= RT) return;
             const f16x8 pa = sm.pbuf[bufp][r][lane];
             const f16x8 pl = sm.pbuf_lo[bufp][r][lane];
 #pragma unroll
@@ -544,14 +725,24 @@ __global__ __launch_bounds__(THREADS, 1) void attn_kernel(AttnLaunch L) {
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) oacc[r][jj] = mfma_f16(pl, bh[jj], oacc[r][jj]);
         };
+        using R0 = std::integral_constant<int, 0>;
+        using R1 = std::integral_constant<int, 1>;
+        using R2 = std::integral_constant<int, 2>;
+        using R3 = std::integral_constant<int, 3>;
+        using R4 = std::integral_constant<int, 4>;
+        using R5 = std::integral_constant<int, 5>;
+        using R6 = std::integral_constant<int, 6>;
+        using R7 = std::integral_constant<int, 7>;
+        using R8 = std::integral_constant<int, 8>;
         for (int k = 0; k <= ntiles; ++k) {
-            // phase 1: this wave's 64 columns of V for tile k-1 as the PV B operands, fp16 hi/lo,
-            // straight from the raw rows into registers.  Column tile jj, lane (g4, l16) holds
-            // column 4*l16 + jj of the wave's 64 (four adjacent columns = one dword per slot)
-            // at the slots of the P operand's lane group: 4g4 .. 4g4+3 and 16+4g4 .. 16+4g4+3.
+            // phase 1: this wave's 64 columns of V for tile k-1 as the PV B operands, fp16
+            // hi/lo, straight from the raw rows into registers.  Column tile jj, lane (g4, l16)
+            // holds column 4*l16 + jj of the wave's 64 (four adjacent columns = one dword per
+            // slot) at the slots of the P operand's lane
+            // group: 4g4 .. 4g4+3 and 16+4g4 .. 16+4g4+3.
             f16x8 bh[4], bl[4];
             if (k >= 1) {
-                const uint8_t* raw = sm.rawv[(k - 1) & 1];
+                const uint8_t* raw = &ringv[(k - 1) % RV][0];
                 const int kb = 2 * wl + (l16 >> 3), c4 = 4 * (l16 & 7);
                 const int o = VT == TV_Q8_0 ? 34 * kb + 2 + c4 : 18 * kb + 2 + (c4 & 15);
                 const int sh = c4 >= 16 ? 4 : 0;
@@ -563,6 +754,16 @@ __global__ __launch_bounds__(THREADS, 1) void attn_kernel(AttnLaunch L) {
                     const uint8_t* row = raw + (t < 4 ? 4 * g4 + t : 12 + 4 * g4 + t) * VF::ROW;
                     w[t] = to_biased<VT>(bytes4_rt(row, o), sh);
                     dd[t] = block_scale(row + kb * VF::BLK);
+                }
+                // slots past the split's end hold bytes of no concern here (possibly not even
+                // finite scales): their weights are zero, and a zero scale keeps 0 * V exact
+                const int tv0 = s0 + (k - 1) * TS;
+                if (tv0 + TS > s1) {
+#pragma unroll
+                    for (int t = 0; t < 8; ++t) {
+                        const int slot = tv0 + (t < 4 ? 4 * g4 + t : 12 + 4 * g4 + t);
+                        dd[t] = slot < s1 ? dd[t] : static_cast<_Float16>(0.f);
+                    }
                 }
 #pragma unroll
                 for (int pp = 0; pp < 4; ++pp) {
@@ -587,28 +788,38 @@ __global__ __launch_bounds__(THREADS, 1) void attn_kernel(AttnLaunch L) {
                 const int bufp = (k - 1) & 1;
                 int anyg = 0;
 #pragma unroll
-                for (int r = 0; r < RTMAX; ++r) anyg |= sm.grow[bufp][r];
+                for (int r = 0; r < RTMAX; ++r) anyg |= r < RT ? sm.grow[bufp][r] : 0;
                 if (anyg) {
 #pragma unroll
                     for (int r = 0; r < RTMAX; ++r) {
-                        if (!sm.grow[bufp][r]) continue;
+                        if (r >= RT || !sm.grow[bufp][r]) continue;
                         const f32x4 al = *reinterpret_cast<const f32x4*>(&sm.alpha[bufp][r][4 * g4]);
 #pragma unroll
                         for (int jj = 0; jj < 4; ++jj) oacc[r][jj] *= al;
                     }
                 }
-#pragma unroll
-                for (int r = 0; r < PV_EARLY; ++r) pv_rowtile(r, bufp, bh, bl);
+                if constexpr (PV_EARLY > 0) pv_rowtile(R0{}, bufp, bh, bl);
+                if constexpr (PV_EARLY > 1) pv_rowtile(R1{}, bufp, bh, bl);
             }
-            __syncthreads();
-            // phase 2: stage the next tile; O += P V for tile k-1
-            stage(k);
+            lds_barrier();
+            // phase 2: O += P V for tile k-1
             if (k >= 1) {
                 const int bufp = (k - 1) & 1;
-#pragma unroll
-                for (int r = PV_EARLY; r < RTMAX; ++r) pv_rowtile(r, bufp, bh, bl);
+                if constexpr (PV_EARLY < 1) pv_rowtile(R0{}, bufp, bh, bl);
+                if constexpr (PV_EARLY < 2) pv_rowtile(R1{}, bufp, bh, bl);
+                pv_rowtile(R2{}, bufp, bh, bl);
+                pv_rowtile(R3{}, bufp, bh, bl);
+                pv_rowtile(R4{}, bufp, bh, bl);
+                pv_rowtile(R5{}, bufp, bh, bl);
+                pv_rowtile(R6{}, bufp, bh, bl);
+                pv_rowtile(R7{}, bufp, bh, bl);
+                pv_rowtile(R8{}, bufp, bh, bl);
             }
-            __syncthreads();
+            // copy K tile k+2+DK (its slot's tile k was converted in phase 1 of step k-1); K
+            // tile k+2 is converted in phase 1 of the next step
+            if (k + 2 + DK < ntiles) dma_k(k + 2 + DK);
+            wait_k(ntiles - 3 - k < DK ? ntiles - 3 - k : DK);
+            lds_barrier();
         }
         __syncthreads();
         // epilogue: this wave's 64 columns of every row
