@@ -6,7 +6,9 @@ gated delta-rule layer -- ``lin_tree_verify_commit``: the commit of the path the
 sequences accepted in their previous step, then the verify of this step's tree, in one
 pass over the state -- and one tree-masked attention layer (``attn_tree_verify``, Q8_0
 cache of 4096 committed slots, window 2048).  ``linear_unfused`` times the separate
-``lin_tree_verify`` and ``lin_tree_commit`` calls on the same inputs.  Widths: linear 16 key / 48 value heads
+``lin_tree_verify`` and ``lin_tree_commit`` calls on the same inputs; ``linear_bank`` the
+pending bank (``lin_tree_verify_bank``, a 32-entry bank per sequence: the state is written
+only when the bank fills).  Widths: linear 16 key / 48 value heads
 of 128, fp32 state; attention 24 query / 4 KV heads of 256.
 
 value = node-layers per second = 2 * (tree nodes in the batch) / step time, i.e. the
@@ -60,6 +62,7 @@ KERNEL_SOURCES = {
     "lin_tree_verify": "tree_verify_linear_amd/csrc/lin_tree.hip",
     "lin_tree_commit": "tree_verify_linear_amd/csrc/lin_tree.hip",
     "lin_tree_verify_commit": "tree_verify_linear_amd/csrc/lin_tree.hip",
+    "lin_tree_verify_bank": "tree_verify_linear_amd/csrc/lin_tree.hip",
     "attn_tree_verify": "tree_verify_linear_amd/csrc/attn_tree.hip",
     "tree_accept_greedy": "tree_verify_linear_amd/csrc/accept.hip",
     "kv_tree_compact": "tree_verify_linear_amd/csrc/accept.hip",
@@ -555,6 +558,84 @@ def time_unfused_linear(args, tvl, torch, pool, sets):
     return res
 
 
+def lin_bank_entry_bytes(L) -> int:
+    """HBM bytes of one pending-bank entry per sequence: its key row per key head, its
+    captured delta row and decay per value head."""
+    Hv, dv = L.state.shape[1], L.state.shape[2]
+    Hk, dk = L.k.shape[2], L.k.shape[3]
+    eb = 2 if L.dtype == "bf16" else 4
+    return Hk * dk * eb + Hv * (dv * 4 + 4)
+
+
+def time_bank_linear(args, tvl, torch, pool, sets, Emax: int = 32):
+    """The linear layer with the pending bank (``lin_tree_verify_bank``): each step verifies
+    from the stored state plus the bank plus the previous step's path, then appends that
+    path to the bank, or -- for the sequences whose bank it would overflow -- stores the
+    committed state and empties the bank.  The state is read every step and written once
+    per bank fill.  The three input sets rotate as in the step, each with its own state and
+    bank; after enough untimed steps for the banks to reach their steady cycle, K steps are
+    timed.  Bytes per step follow each sequence's bank length (simulated on the host with
+    the same rule)."""
+    import numpy as np
+    n = len(pool)
+    L0 = sets[0].lin[0]
+    B, Hk, dk = L0.k.shape[0], L0.k.shape[2], L0.k.shape[3]
+    Hv, dv = L0.state.shape[1], L0.state.shape[2]
+    eb = 2 if L0.dtype == "bf16" else 4
+    banks = [tvl.lin_bank_empty(B, Hk, Hv, dk, dv, Emax, torch.bfloat16, "cuda") for _ in range(n)]
+    E = [np.zeros(B, np.int64) for _ in range(n)]
+    entry = lin_bank_entry_bytes(L0)
+    tile = Hv * dv * dk * 4
+
+    def one(i, ev=None):
+        d, L = pool[i % n], sets[i % n].lin[0]
+        v = i // n
+        cap, prev_cap = d["caps"][v % 2], d["caps"][(v + 1) % 2]
+        plen = d["path_len"] if v > 0 else d["zero_len"]
+        if ev:
+            ev[0].record()
+        tvl.lin_tree_verify_bank(d["q"], d["k"], d["v"], d["g"], d["beta"], d["state"], d["parent"], d["n_nodes"],
+                                 L.scale, d["path"], plen, d["k"], d["g"], prev_cap, banks[i % n], out=d["out"],
+                                 cap_delta=cap)
+        if ev:
+            ev[1].record()
+        # host model of the same step: bytes beyond the plain verify's
+        Lp = L.path_len.astype(np.int64) if v > 0 else np.zeros(B, np.int64)
+        e = E[i % n]
+        flushed = Lp > Emax - e
+        extra = (int(e.sum()) * entry                     # the bank's entries read
+                 + int(Lp.sum()) * (Hk * dk * eb + Hv * dv * 4 + Hv * eb)   # the previous path read
+                 + int(Lp[~flushed].sum()) * entry          # appended
+                 + int((flushed & (e + Lp > 0)).sum()) * tile)   # committed tiles stored
+        E[i % n] = np.where(flushed, 0, e + Lp)
+        return extra, int(flushed.sum()), float(e.mean())
+
+    for p in pool:
+        p["zero_len"] = torch.zeros_like(p["path_len"])
+    warm = n * (Emax + 2)                            # every bank past its first fill
+    for i in range(warm):
+        one(i)
+    torch.cuda.synchronize()
+    K = max(args.steps, 4 * n)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
+    extra, flushes, emean = 0, 0, 0.0
+    for i in range(K):
+        x, f, e = one(warm + i, ev[i])
+        extra += x
+        flushes += f
+        emean += e
+    torch.cuda.synchronize()
+    ms = sum(e[0].elapsed_time(e[1]) for e in ev) / K
+    nb = sum(lin_verify_bytes(W.lin[0]) for W in sets) / n + extra / K
+    nodes = sum(int(W.lin[0].n_nodes.sum()) for W in sets) / n
+    gbs = nb / (ms * 1e-3) / 1e9
+    return {"Emax": Emax, "steps_timed": K, "mean_us": round(ms * 1e3, 2),
+            "algorithmic_MB": round(nb / 1e6, 2), "GB_per_s": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "nodes_per_s": round(nodes / (ms * 1e-3), 1),
+            "flushed_fraction": round(flushes / (K * B), 4), "bank_entries_mean": round(emean / K, 2),
+            "counter_traffic_bytes": counter_traffic("lin_tree_verify_bank")}
+
+
 def time_workload2(args, tvl, torch, dev, B):
     """The second workload: budgets 8 (a chain), 16 and 40, with a Q8_0 K cache and a Q4_0 V
     cache, through the same three calls as the step.  One input set per variant (each is
@@ -986,6 +1067,7 @@ def main():
         kernels["attn_tree_verify"].update(util)
 
     unfused = None if args.no_workload2 else time_unfused_linear(args, tvl, torch, pool, sets)
+    bank = None if args.no_workload2 else time_bank_linear(args, tvl, torch, pool, sets)
     next_kernels = time_next_rows(args, tvl, torch, dev, pool[0], A0, B)
     workload2 = None if args.no_workload2 else time_workload2(args, tvl, torch, dev, B)
     single = None if args.no_single_sequence else time_single_sequence(args, tvl, torch, dev)
@@ -1017,6 +1099,7 @@ def main():
                    "global_batch": B, "tree_nodes": 22, "kv_type": "q8_0", "window": 2048, "n_past": 4096},
         "kernels": kernels,
         "linear_unfused": unfused,
+        "linear_bank": bank,
         "next_kernels": next_kernels,
         "workload2": workload2,
         "single_sequence": single,

@@ -10,7 +10,9 @@
  *                     per-node factors needed to commit later;
  *   lin_tree_commit   after acceptance, moves the committed state in place to the end of
  *                     the accepted root path, using the captured factors (or, fused,
- *                     lin_tree_verify_commit applies it inside the next step's verify);
+ *                     lin_tree_verify_commit applies it inside the next step's verify,
+ *                     and lin_tree_verify_bank keeps several steps pending in a bank and
+ *                     writes the state only when the bank fills);
  *   attn_tree_verify  full-attention layer: tree-masked softmax attention over a Q8_0 /
  *                     Q4_0 quantised KV cache with an optional sliding window.
  *
@@ -79,6 +81,7 @@ extern "C" {
 
 #define TV_ABI_VERSION 1
 #define TV_MAX_NODES 64
+#define TV_BANK_MAX_ENTRIES 256   /* largest pending-bank capacity (lin_tree_verify_bank) */
 
 typedef enum {
     TV_OK = 0,
@@ -205,6 +208,64 @@ int lin_tree_verify_commit(int B, int N, int Hk, int Hv, int dk, int dv, int dty
                            int prev_N, const int32_t* prev_path, const int32_t* prev_path_len,
                            int prev_Lmax, const void* prev_k, const void* prev_g,
                            const float* prev_cap_delta, void* stream);
+
+/*
+ * Pending bank -- several steps' commits kept pending, flushed when the bank fills.
+ * (PR #606 "SpecLA factor-capture speculative decoding": "CLI", the fused-commit option that
+ * is on by default, and the review comment on the pending bank, its pending count and the
+ * fused flush of the pending factors into the raw state.)
+ *
+ * A bank holds, per sequence, accepted entries (key, decay, captured delta) of earlier steps
+ * that are not yet in the stored state, in acceptance order: E = bank_len[b] entries.  The
+ * committed state is the stored state, then the bank's entries, then the accepted path of
+ * the step verified last (pending until the next call, as with lin_tree_verify_commit):
+ *     S = G S_stored + sum_e c_e k_e delta_e^T,  G = prod_e g_e,  c_e = prod_{e' > e} g_e'
+ * over all of those entries in order -- exactly where committing each step's path in turn
+ * with lin_tree_commit would have moved the state.  lin_tree_verify_bank verifies this step's
+ * tree from S and then either appends the previous path to the bank, leaving `state` alone,
+ * or stores S into `state` and empties the bank: when the path does not fit (E + L > Emax) or
+ * a flush is asked for.  So the state is written once per bank fill instead of every step.
+ * lin_bank_flush stores S without a verify (e.g. before the state is read elsewhere).
+ *
+ * Bank buffers (caller-owned, device; Emax a multiple of 32 in [32, TV_BANK_MAX_ENTRIES]):
+ *   bank_k      [B][Hk][dk][Emax] of dtype (each key channel's entries contiguous)
+ *   bank_g      fp32 [B][Hv][Emax]
+ *   bank_delta  fp32 [B][Hv][dv][Emax] (each value channel's entries contiguous)
+ *   bank_len    int32 [B]: E per sequence, in [0, Emax] (clamped into it); 0 for an empty
+ *               bank (set it to 0 whenever `state` is replaced by the caller).
+ * Entries at or beyond E are never used and need no initialisation.  The bank, the state and
+ * the previous step's buffers belong together: calls that use one bank must not overlap.
+ *
+ * lin_tree_verify_bank -- lin_tree_verify from the committed state S above.
+ *   B .. cap_delta         as for lin_tree_verify (this step); state is in/out
+ *   prev_N .. prev_cap_delta   the previous step's accepted path and its k, g and captured
+ *                          deltas, as for lin_tree_verify_commit (prev_path_len[b] = 0 when
+ *                          nothing is pending, e.g. at the first step)
+ *   Emax, bank_k, bank_g, bank_delta, bank_len   the bank (updated)
+ *   flush                  0 or 1: 1 stores S and empties every sequence's bank
+ * Alignment as for lin_tree_verify_commit, plus bank_k and bank_delta 16-byte, bank_g and
+ * bank_len 4-byte.  Accuracy: bank keys enter exactly (bf16) or as bf16 hi + lo (fp32),
+ * c_e delta_e as bf16 hi + lo, accumulated in fp32 (about 2^-16 relative per term).
+ */
+int lin_tree_verify_bank(int B, int N, int Hk, int Hv, int dk, int dv, int dtype, int head_group,
+                         float scale, const int32_t* parent, const int32_t* n_nodes,
+                         const void* q, const void* k, const void* v, const void* g,
+                         const void* beta, float* state, float* out, float* cap_delta,
+                         int prev_N, const int32_t* prev_path, const int32_t* prev_path_len,
+                         int prev_Lmax, const void* prev_k, const void* prev_g,
+                         const float* prev_cap_delta, int Emax, int flush, void* bank_k,
+                         float* bank_g, float* bank_delta, int32_t* bank_len, void* stream);
+
+/*
+ * lin_bank_flush -- store the committed state S (stored state + bank + previous step's
+ * path) into `state` and empty the bank.  Arguments as for lin_tree_verify_bank; no tree is
+ * verified and no node input is read.
+ */
+int lin_bank_flush(int B, int Hk, int Hv, int dk, int dv, int dtype, int head_group, float* state,
+                   int prev_N, const int32_t* prev_path, const int32_t* prev_path_len,
+                   int prev_Lmax, const void* prev_k, const void* prev_g,
+                   const float* prev_cap_delta, int Emax, void* bank_k, float* bank_g,
+                   float* bank_delta, int32_t* bank_len, void* stream);
 
 /*
  * attn_tree_verify -- one full-attention layer over the draft tree.

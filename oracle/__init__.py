@@ -30,7 +30,7 @@ convention, not to the pages (which only name the formats).
 """
 from .tree import depths, root_path, ancestor_matrix, validate_tree, validate_path  # noqa: F401
 from .delta import (bf16_bits_to_f64, lin_tree_verify, lin_commit_replay,  # noqa: F401
-                    lin_chain_recurrence, lin_tree_verify_commit)
+                    lin_chain_recurrence, lin_tree_verify_commit, lin_tree_verify_bank)
 from .attention import (dequant_q8_0, dequant_q4_0, dequant_rows, attn_tree_verify,  # noqa: F401
                         attn_tree_verify_rows, attn_tree_verify_dense, visible_slots)
 from .accept import (logits_f64, argmax_rows, greedy_walk, tree_accept_greedy,  # noqa: F401

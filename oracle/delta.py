@@ -152,3 +152,27 @@ def lin_tree_verify_commit(state, prev, q, k, v, g, beta, parent, n_nodes, scale
     stored = committed.astype(np.float32)
     out, delta = lin_tree_verify(q, k, v, g, beta, stored, parent, n_nodes, scale, dtype, head_group)
     return stored.astype(np.float64), out, delta
+
+
+def lin_tree_verify_bank(state, pending, q, k, v, g, beta, parent, n_nodes, scale: float, dtype: str = "f32",
+                         head_group: str = "contiguous"):
+    """One verify step with several accepted steps still pending.
+
+    PR #606 "SpecLA factor-capture speculative decoding": "CLI" (the fused commit is on by
+    default) and the review comment on the pending bank (a pending count of accepted
+    factors, flushed into the raw state).  Reading taken: the pending steps are committed in
+    acceptance order, each exactly as a separate commit of its accepted path would
+    (``lin_commit_replay``, its result stored as fp32), and this step's verify starts from
+    the state they reach.  How many steps stay pending before a flush does not change any
+    value: it only decides when the state is written.
+
+    ``pending`` = the steps accepted since the state was last stored, oldest first, each
+    (path, path_len, k, v, g, beta, parent, n_nodes) of that step.  Returns
+    ``(committed_state, out, delta)`` as ``lin_tree_verify_commit`` does."""
+    S = np.asarray(state, dtype=np.float32).astype(np.float64)
+    for prev in pending:
+        path, path_len, pk, pv, pg, pbeta, pparent, pn = prev
+        S = lin_commit_replay(S, path, path_len, pk, pv, pg, pbeta, pparent, pn, dtype, head_group)
+        S = S.astype(np.float32).astype(np.float64)
+    out, delta = lin_tree_verify(q, k, v, g, beta, S.astype(np.float32), parent, n_nodes, scale, dtype, head_group)
+    return S, out, delta

@@ -75,6 +75,38 @@ def test_commit_argument_errors():
         assert b"aligned" in L.tv_last_error()
 
 
+def test_bank_argument_errors():
+    L = tvl.lib()
+    f = _fake()
+
+    def vb(Emax=32, flush=0, ptr=f, bank_k=None, prev_Lmax=4, **kw):
+        a = dict(B=1, N=8, Hk=1, Hv=1, dk=16, dv=16, dtype=1, head_group=0)
+        a.update(kw)
+        return L.lin_tree_verify_bank(a["B"], a["N"], a["Hk"], a["Hv"], a["dk"], a["dv"], a["dtype"],
+                                      a["head_group"], 0.25, *([ptr] * 9), ctypes.c_void_p(8192), 8, ptr, ptr,
+                                      prev_Lmax, ptr, ptr, ptr, Emax, flush,
+                                      bank_k if bank_k is not None else ptr, ptr, ptr, ptr, None)
+
+    assert vb(Emax=48) == tvl.TV_ERANGE and b"multiple of 32" in L.tv_last_error()
+    assert vb(Emax=288) == tvl.TV_ERANGE
+    assert vb(Emax=0) == tvl.TV_ERANGE
+    assert vb(flush=2) == tvl.TV_EINVAL
+    assert vb(prev_Lmax=9) == tvl.TV_ERANGE                        # prev_Lmax > prev_N
+    assert vb(ptr=None) == tvl.TV_EINVAL and b"null" in L.tv_last_error()
+    assert vb(bank_k=ctypes.c_void_p(4104)) == tvl.TV_EINVAL and b"aligned" in L.tv_last_error()
+    assert vb(dk=48) == tvl.TV_EUNSUPPORTED
+
+    def fl(Emax=32, ptr=f, bank_delta=None, prev_Lmax=4, state=f):
+        return L.lin_bank_flush(1, 1, 1, 16, 16, 1, 0, state, 8, ptr, ptr, prev_Lmax, ptr, ptr, ptr, Emax, ptr, ptr,
+                                bank_delta if bank_delta is not None else ptr, ptr, None)
+
+    assert fl(Emax=40) == tvl.TV_ERANGE
+    assert fl(prev_Lmax=0) == tvl.TV_ERANGE
+    assert fl(ptr=None) == tvl.TV_EINVAL
+    assert fl(state=ctypes.c_void_p(4100)) == tvl.TV_EINVAL and b"aligned" in L.tv_last_error()
+    assert fl(bank_delta=ctypes.c_void_p(4100)) == tvl.TV_EINVAL and b"aligned" in L.tv_last_error()
+
+
 def test_attention_argument_errors():
     L = tvl.lib()
     f = _fake()

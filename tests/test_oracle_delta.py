@@ -291,3 +291,87 @@ def test_verify_commit_is_commit_then_verify_and_matches_a_chain_replay():
     ref0, _ = oracle.lin_tree_verify(L2.q, L2.k, L2.v, L2.g, L2.beta, L1.state, L2.parent, L2.n_nodes, L2.scale, "f32")
     assert np.array_equal(st0, L1.state.astype(np.float64))
     np.testing.assert_allclose(out0, ref0, rtol=1e-15, atol=1e-15)
+
+
+def _chain_step(cfg, n, L, Hk=1, Hv=2, dk=16, dv=16, dtype="f32"):
+    from workloads import gen_lin, tree_chain
+    return gen_lin(cfg, [tree_chain(n)], [np.arange(L, dtype=np.int32)], Hk, Hv, dk, dv, dtype)
+
+
+def _prev(L):
+    return (L.path, L.path_len, L.k, L.v, L.g, L.beta, L.parent, L.n_nodes)
+
+
+def test_bank_of_chain_steps_is_one_chain():
+    """Three accepted chain steps pending (4, 0 and 6 tokens accepted), then a fourth chain
+    verified: one sequential recurrence over the accepted tokens followed by the new chain
+    (a chain is a degenerate tree, PR #606 "Paper mapping")."""
+    steps = [_chain_step(80, 6, 4), _chain_step(81, 5, 1), _chain_step(82, 7, 6)]
+    steps[1].path_len[:] = 0                         # the middle step accepted nothing
+    last = _chain_step(83, 5, 5)
+    S0 = steps[0].state
+    st, out, delta = oracle.lin_tree_verify_bank(S0, [_prev(s) for s in steps], last.q, last.k, last.v, last.g,
+                                                 last.beta, last.parent, last.n_nodes, last.scale, "f32")
+    acc = [(s, int(s.path_len[0])) for s in steps]
+    for h in range(last.Hv):
+        cat = lambda f, hh: np.concatenate([f(s)[0, :L, hh] for s, L in acc] + [f(last)[0, :, hh]]).astype(np.float64)
+        q, k = cat(lambda s: s.q, 0), cat(lambda s: s.k, 0)
+        v, g, bt = cat(lambda s: s.v, h), cat(lambda s: s.g, h), cat(lambda s: s.beta, h)
+        o_ref, _ = oracle.lin_chain_recurrence(q, k, v, g, bt, S0[0, h].T.astype(np.float64), last.scale)
+        n_acc = sum(L for _, L in acc)
+        np.testing.assert_allclose(out[0, :, h], o_ref[n_acc:], rtol=1e-6, atol=1e-6)   # fp32 stored states
+        # the committed state is the chain's state after the accepted tokens
+        _, S_acc = oracle.lin_chain_recurrence(q[:n_acc], k[:n_acc], v[:n_acc], g[:n_acc], bt[:n_acc],
+                                               S0[0, h].T.astype(np.float64), last.scale)
+        np.testing.assert_allclose(st[0, h].T, S_acc, rtol=1e-6, atol=1e-6)
+
+
+def test_bank_factor_form():
+    """The pending bank's closed form: with the entries e of every pending step's accepted
+    path in acceptance order, each carrying the key k_e, decay g_e and the delta delta_e that
+    step's verify captured,  S = (prod_e g_e) S0 + sum_e (prod_{e' > e} g_e') k_e delta_e^T.
+    Built here entry by entry with explicit products; the steps are 22-node trees."""
+    from workloads import gen_lin, trees_for
+    Hk, Hv, dk, dv = 2, 4, 16, 8
+    steps = [gen_lin(90 + t, *trees_for(90 + t, 1, "ddtree"), Hk, Hv, dk, dv, "f32") for t in range(3)]
+    S0 = steps[0].state
+    # every step's captured deltas, from the state the bank oracle commits before it
+    entries = []                                     # per value head: (k_e, g_e, delta_e)
+    for t, s in enumerate(steps):
+        st, _, delta = oracle.lin_tree_verify_bank(S0, [_prev(x) for x in steps[:t]], s.q, s.k, s.v, s.g, s.beta,
+                                                   s.parent, s.n_nodes, s.scale, "f32")
+        for a in s.path[0, :int(s.path_len[0])]:
+            entries.append((s.k[0, a], s.g[0, a], delta[0, a]))
+    last = gen_lin(99, *trees_for(99, 1, "ddtree"), Hk, Hv, dk, dv, "f32")
+    st, _, _ = oracle.lin_tree_verify_bank(S0, [_prev(x) for x in steps], last.q, last.k, last.v, last.g,
+                                           last.beta, last.parent, last.n_nodes, last.scale, "f32")
+    assert len(entries) > 6
+    for h in range(Hv):
+        kh = h // (Hv // Hk)
+        G = np.prod([float(g[h]) for _, g, _ in entries])
+        S = G * S0[0, h].T.astype(np.float64)
+        for e, (ke, _, de) in enumerate(entries):
+            c = np.prod([float(g[h]) for _, g, _ in entries[e + 1:]])
+            S += c * np.outer(ke[kh].astype(np.float64), de[h])
+        np.testing.assert_allclose(st[0, h].T, S, rtol=1e-5, atol=1e-6)
+
+
+def test_bank_degenerate_cases():
+    """Nothing pending: the plain verify.  Only empty paths pending: the state is unchanged
+    bit for bit."""
+    from workloads import gen_lin, trees_for
+    s1 = gen_lin(95, *trees_for(95, 2, "ddtree"), 2, 4, 16, 16, "bf16")
+    s2 = gen_lin(96, *trees_for(96, 2, "ddtree"), 2, 4, 16, 16, "bf16")
+    st, out, delta = oracle.lin_tree_verify_bank(s1.state, [], s2.q, s2.k, s2.v, s2.g, s2.beta, s2.parent,
+                                                 s2.n_nodes, s2.scale, "bf16")
+    ref_o, ref_d = oracle.lin_tree_verify(s2.q, s2.k, s2.v, s2.g, s2.beta, s1.state, s2.parent, s2.n_nodes,
+                                          s2.scale, "bf16")
+    assert np.array_equal(st, s1.state.astype(np.float64))
+    np.testing.assert_array_equal(out, ref_o)
+    np.testing.assert_array_equal(delta, ref_d)
+    p = _prev(s1)
+    empty = (p[0], np.zeros_like(p[1])) + p[2:]
+    st2, out2, _ = oracle.lin_tree_verify_bank(s1.state, [empty, empty], s2.q, s2.k, s2.v, s2.g, s2.beta, s2.parent,
+                                               s2.n_nodes, s2.scale, "bf16")
+    assert np.array_equal(st2, s1.state.astype(np.float64))
+    np.testing.assert_array_equal(out2, ref_o)

@@ -15,7 +15,7 @@ import os
 import torch
 
 __all__ = ["TreeVerifyError", "lib", "lib_path", "lin_tree_verify", "lin_tree_commit", "lin_tree_verify_commit",
-           "attn_tree_verify", "attn_tree_verify_noalloc", "attn_tree_workspace_bytes", "tree_accept_greedy",
+           "LinBank", "lin_bank_empty", "lin_tree_verify_bank", "lin_bank_flush", "attn_tree_verify", "attn_tree_verify_noalloc", "attn_tree_workspace_bytes", "tree_accept_greedy",
            "tree_accept_workspace_bytes", "kv_tree_compact", "conv_tree_verify", "conv_tree_commit",
            "validate_tree", "validate_path",
            "abi_version", "KV_TYPES", "EXPORTS"]
@@ -36,6 +36,9 @@ EXPORTS = {
     "lin_tree_commit": (_i, [_i, _i, _i, _i, _i, _i, _i, _i, _p, _p, _i, _p, _p, _p, _p, _p]),
     "lin_tree_verify_commit": (_i, [_i, _i, _i, _i, _i, _i, _i, _i, _f, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p,
                                     _i, _p, _p, _i, _p, _p, _p, _p]),
+    "lin_tree_verify_bank": (_i, [_i, _i, _i, _i, _i, _i, _i, _i, _f, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p,
+                                  _i, _p, _p, _i, _p, _p, _p, _i, _i, _p, _p, _p, _p, _p]),
+    "lin_bank_flush": (_i, [_i, _i, _i, _i, _i, _i, _i, _p, _i, _p, _p, _i, _p, _p, _p, _i, _p, _p, _p, _p, _p]),
     "attn_tree_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
     "attn_tree_verify": (_i, [_i, _i, _i, _i, _i, _i, _i, _i, _i, _f, _p, _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
     "attn_tree_verify_noalloc": (_i, [_i, _i, _i, _i, _i, _i, _i, _i, _i, _f, _p, _p, _p, _p, _p, _p, _p, _p, _p]),
@@ -178,6 +181,87 @@ def lin_tree_verify_commit(q, k, v, g, beta, state, parent, n_nodes, scale: floa
                                         _ptr(prev_path_len), prev_path.shape[1], _ptr(prev_k), _ptr(prev_g),
                                         _ptr(prev_cap_delta), _stream(q.device)))
     return out, cap_delta
+
+
+class LinBank:
+    """A pending bank: ``k`` [B][Hk][dk][Emax] (input dtype), ``g`` fp32 [B][Hv][Emax],
+    ``delta`` fp32 [B][Hv][dv][Emax] and ``length`` int32 [B] (entries pending per sequence,
+    besides the previous step's path)."""
+
+    def __init__(self, k, g, delta, length):
+        self.k, self.g, self.delta, self.length = k, g, delta, length
+        self.Emax = k.shape[3]
+
+
+def lin_bank_empty(B: int, Hk: int, Hv: int, dk: int, dv: int, Emax: int, dtype, device) -> LinBank:
+    """An empty bank of capacity ``Emax`` (a multiple of 32, at most 256)."""
+    return LinBank(torch.zeros((B, Hk, dk, Emax), dtype=dtype, device=device),
+                   torch.zeros((B, Hv, Emax), dtype=torch.float32, device=device),
+                   torch.zeros((B, Hv, dv, Emax), dtype=torch.float32, device=device),
+                   torch.zeros((B,), dtype=torch.int32, device=device))
+
+
+def _dev_bank(bank: LinBank, B, Hk, Hv, dk, dv, dt):
+    E = bank.Emax
+    _dev(bank.k, "bank.k", dt, (B, Hk, dk, E)); _dev(bank.g, "bank.g", torch.float32, (B, Hv, E))
+    _dev(bank.delta, "bank.delta", torch.float32, (B, Hv, dv, E)); _dev(bank.length, "bank.length", torch.int32, (B,))
+
+
+def _dev_prev(prev_path, prev_path_len, prev_k, prev_g, prev_cap_delta, B, Hk, Hv, dk, dv, dt):
+    PN = prev_k.shape[1]
+    _dev(prev_k, "prev_k", dt, (B, PN, Hk, dk)); _dev(prev_g, "prev_g", dt, (B, PN, Hv))
+    _dev(prev_cap_delta, "prev_cap_delta", torch.float32, (B, PN, Hv, dv))
+    _dev(prev_path, "prev_path", torch.int32); _dev(prev_path_len, "prev_path_len", torch.int32, (B,))
+    if prev_path.dim() != 2 or prev_path.shape[0] != B:
+        raise ValueError(f"prev_path has shape {tuple(prev_path.shape)}, expected ({B}, Lmax)")
+    return PN
+
+
+def lin_tree_verify_bank(q, k, v, g, beta, state, parent, n_nodes, scale: float, prev_path, prev_path_len,
+                         prev_k, prev_g, prev_cap_delta, bank: LinBank, flush: bool = False,
+                         head_group: str = "contiguous", out=None, cap_delta=None):
+    """Verify from the committed state (``state`` + ``bank`` + the previous step's accepted
+    path), then append that path to the bank -- or, when it does not fit or ``flush`` is set,
+    store the committed state and empty the bank.  Returns ``(out, cap_delta)``."""
+    B, N, Hk, dk = q.shape
+    Hv, dv = v.shape[2], v.shape[3]
+    dt = q.dtype
+    _dev(q, "q", dt); _dev(k, "k", dt, (B, N, Hk, dk)); _dev(v, "v", dt, (B, N, Hv, dv))
+    _dev(g, "g", dt, (B, N, Hv)); _dev(beta, "beta", dt, (B, N, Hv))
+    _dev(state, "state", torch.float32, (B, Hv, dv, dk))
+    _dev(parent, "parent", torch.int32, (B, N)); _dev(n_nodes, "n_nodes", torch.int32, (B,))
+    PN = _dev_prev(prev_path, prev_path_len, prev_k, prev_g, prev_cap_delta, B, Hk, Hv, dk, dv, dt)
+    _dev_bank(bank, B, Hk, Hv, dk, dv, dt)
+    if out is None:
+        out = torch.empty((B, N, Hv, dv), dtype=torch.float32, device=q.device)
+    if cap_delta is None:
+        cap_delta = torch.empty((B, N, Hv, dv), dtype=torch.float32, device=q.device)
+    _dev(out, "out", torch.float32, (B, N, Hv, dv)); _dev(cap_delta, "cap_delta", torch.float32, (B, N, Hv, dv))
+    _check(lib().lin_tree_verify_bank(B, N, Hk, Hv, dk, dv, _in_dtype(q), HEAD_GROUPS[head_group], float(scale),
+                                      _ptr(parent), _ptr(n_nodes), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                      _ptr(state), _ptr(out), _ptr(cap_delta), PN, _ptr(prev_path),
+                                      _ptr(prev_path_len), prev_path.shape[1], _ptr(prev_k), _ptr(prev_g),
+                                      _ptr(prev_cap_delta), bank.Emax, int(bool(flush)), _ptr(bank.k), _ptr(bank.g),
+                                      _ptr(bank.delta), _ptr(bank.length), _stream(q.device)))
+    return out, cap_delta
+
+
+def lin_bank_flush(state, prev_path, prev_path_len, prev_k, prev_g, prev_cap_delta, bank: LinBank,
+                   head_group: str = "contiguous"):
+    """Store the committed state (``state`` + ``bank`` + the previous step's accepted path)
+    into ``state`` and empty the bank."""
+    B, Hv, dv, dk = state.shape
+    Hk = prev_k.shape[2]
+    dt = prev_k.dtype
+    _dev(state, "state", torch.float32)
+    _dev(prev_k, "prev_k", (torch.bfloat16, torch.float32))
+    PN = _dev_prev(prev_path, prev_path_len, prev_k, prev_g, prev_cap_delta, B, Hk, Hv, dk, dv, dt)
+    _dev_bank(bank, B, Hk, Hv, dk, dv, dt)
+    _check(lib().lin_bank_flush(B, Hk, Hv, dk, dv, _in_dtype(prev_k), HEAD_GROUPS[head_group], _ptr(state), PN,
+                                _ptr(prev_path), _ptr(prev_path_len), prev_path.shape[1], _ptr(prev_k),
+                                _ptr(prev_g), _ptr(prev_cap_delta), bank.Emax, _ptr(bank.k), _ptr(bank.g),
+                                _ptr(bank.delta), _ptr(bank.length), _stream(state.device)))
+    return state
 
 
 def attn_tree_workspace_bytes(B: int, N: int, Hq: int, Hkv: int, D: int, Tcap: int, window: int) -> int:

@@ -146,6 +146,97 @@ int lin_tree_verify_commit(int B, int N, int Hk, int Hv, int dk, int dv, int dty
     return launch_lin_verify(a, dtype == TV_BF16, static_cast<hipStream_t>(stream));
 }
 
+static int check_bank(const char* fn, int Emax) {
+    if (Emax < 32 || Emax > TV_BANK_MAX_ENTRIES || Emax % 32 != 0)
+        return set_error(TV_ERANGE, "%s: Emax=%d must be a multiple of 32 in [32, %d]", fn, Emax, TV_BANK_MAX_ENTRIES);
+    return TV_OK;
+}
+
+static int check_prev(const char* fn, int prev_N, int prev_Lmax) {
+    if (prev_N < 1 || prev_N > TV_MAX_NODES) return set_error(TV_ERANGE, "%s: prev_N=%d not in [1, %d]", fn, prev_N, TV_MAX_NODES);
+    if (prev_Lmax < 1 || prev_Lmax > prev_N)
+        return set_error(TV_ERANGE, "%s: prev_Lmax=%d not in [1, prev_N=%d]", fn, prev_Lmax, prev_N);
+    return TV_OK;
+}
+
+static int check_bank_buffers(const char* fn, const void* bank_k, const float* bank_g, const float* bank_delta,
+                              const int32_t* bank_len) {
+    if (!bank_k || !bank_g || !bank_delta || !bank_len) return set_error(TV_EINVAL, "%s: null pointer argument", fn);
+    if (!aligned(bank_k, 16) || !aligned(bank_delta, 16) || !aligned(bank_g, 4) || !aligned(bank_len, 4))
+        return set_error(TV_EINVAL, "%s: bank_k and bank_delta must be 16-byte aligned (bank_g and bank_len 4-byte)",
+                         fn);
+    return TV_OK;
+}
+
+int lin_tree_verify_bank(int B, int N, int Hk, int Hv, int dk, int dv, int dtype, int head_group, float scale,
+                         const int32_t* parent, const int32_t* n_nodes, const void* q, const void* k, const void* v,
+                         const void* g, const void* beta, float* state, float* out, float* cap_delta, int prev_N,
+                         const int32_t* prev_path, const int32_t* prev_path_len, int prev_Lmax, const void* prev_k,
+                         const void* prev_g, const float* prev_cap_delta, int Emax, int flush, void* bank_k,
+                         float* bank_g, float* bank_delta, int32_t* bank_len, void* stream) {
+    clear_error();
+    const char* fn = "lin_tree_verify_bank";
+    int st = check_common_lin(fn, B, N, Hk, Hv, dk, dv, dtype, head_group);
+    if (st != TV_OK) return st;
+    if ((st = check_prev(fn, prev_N, prev_Lmax)) != TV_OK) return st;
+    if ((st = check_bank(fn, Emax)) != TV_OK) return st;
+    if (flush != 0 && flush != 1) return set_error(TV_EINVAL, "%s: flush=%d is not 0 or 1", fn, flush);
+    if (!std::isfinite(scale)) return set_error(TV_EINVAL, "%s: scale is not finite", fn);
+    if (!parent || !n_nodes || !q || !k || !v || !g || !beta || !state || !out || !cap_delta || !prev_path ||
+        !prev_path_len || !prev_k || !prev_g || !prev_cap_delta)
+        return set_error(TV_EINVAL, "%s: null pointer argument", fn);
+    if ((st = check_bank_buffers(fn, bank_k, bank_g, bank_delta, bank_len)) != TV_OK) return st;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(state, 16) || !aligned(out, 16) ||
+        !aligned(cap_delta, 16) || !aligned(prev_k, 16) || !aligned(prev_cap_delta, 16))
+        return set_error(TV_EINVAL, "%s: q, k, v, state, out, cap_delta, prev_k and prev_cap_delta must be 16-byte "
+                         "aligned", fn);
+    if (static_cast<const void*>(cap_delta) == static_cast<const void*>(prev_cap_delta))
+        return set_error(TV_EINVAL, "%s: cap_delta and prev_cap_delta must be different buffers", fn);
+    LinVerifyArgs a{B, N, Hk, Hv, dk, dv, Hv / Hk, head_group == TV_HEADS_TILED, scale, parent, n_nodes,
+                    q, k, v, g, beta, state, out, cap_delta, prev_N, prev_Lmax, prev_path, prev_path_len, prev_k,
+                    prev_g, prev_cap_delta, state};
+    a.bank_Emax = Emax;
+    a.bank_len = bank_len;
+    a.bank_k = bank_k;
+    a.bank_g = bank_g;
+    a.bank_delta = bank_delta;
+    a.bank_flush = flush;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if ((st = launch_lin_verify(a, dtype == TV_BF16, s)) != TV_OK) return st;
+    return launch_lin_bank_len(bank_len, prev_path_len, prev_Lmax, B, Emax, flush, s);
+}
+
+int lin_bank_flush(int B, int Hk, int Hv, int dk, int dv, int dtype, int head_group, float* state, int prev_N,
+                   const int32_t* prev_path, const int32_t* prev_path_len, int prev_Lmax, const void* prev_k,
+                   const void* prev_g, const float* prev_cap_delta, int Emax, void* bank_k, float* bank_g,
+                   float* bank_delta, int32_t* bank_len, void* stream) {
+    clear_error();
+    const char* fn = "lin_bank_flush";
+    int st = check_common_lin(fn, B, 1, Hk, Hv, dk, dv, dtype, head_group);
+    if (st != TV_OK) return st;
+    if ((st = check_prev(fn, prev_N, prev_Lmax)) != TV_OK) return st;
+    if ((st = check_bank(fn, Emax)) != TV_OK) return st;
+    if (!state || !prev_path || !prev_path_len || !prev_k || !prev_g || !prev_cap_delta)
+        return set_error(TV_EINVAL, "%s: null pointer argument", fn);
+    if ((st = check_bank_buffers(fn, bank_k, bank_g, bank_delta, bank_len)) != TV_OK) return st;
+    if (!aligned(state, 16) || !aligned(prev_k, 16) || !aligned(prev_cap_delta, 16))
+        return set_error(TV_EINVAL, "%s: state, prev_k and prev_cap_delta must be 16-byte aligned", fn);
+    // the bank verify with an empty tree (N = 0): no node input is read and nothing is written
+    // but the committed state
+    LinVerifyArgs a{B, 0, Hk, Hv, dk, dv, Hv / Hk, head_group == TV_HEADS_TILED, 1.f, nullptr, nullptr,
+                    nullptr, nullptr, nullptr, nullptr, nullptr, state, nullptr, nullptr, prev_N, prev_Lmax, prev_path,
+                    prev_path_len, prev_k, prev_g, prev_cap_delta, state};
+    a.bank_Emax = Emax;
+    a.bank_len = bank_len;
+    a.bank_k = bank_k;
+    a.bank_g = bank_g;
+    a.bank_delta = bank_delta;
+    a.bank_flush = 1;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if ((st = launch_lin_verify(a, dtype == TV_BF16, s)) != TV_OK) return st;
+    return launch_lin_bank_len(bank_len, prev_path_len, prev_Lmax, B, Emax, 1, s);
+}
+
 int lin_tree_commit(int B, int N, int Hk, int Hv, int dk, int dv, int dtype, int head_group, const int32_t* path,
                     const int32_t* path_len, int Lmax, const void* k, const void* g, const float* cap_delta,
                     float* state, void* stream) {

@@ -92,13 +92,6 @@ __device__ __forceinline__ f32x4 mfma_f16(const f16x8& a, const f16x8& b, const 
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
-// Wait until at most N of this wave's vector-memory operations are outstanding (loads return
-// in issue order, so the older ones are then complete).
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
 // Workgroup barrier for LDS traffic only: this wave's LDS operations are complete, then the
 // barrier.  Unlike __syncthreads it does not wait for outstanding global-to-LDS copies, which
 // must stay in flight across barriers; each copy is waited for explicitly before the barrier
@@ -108,20 +101,6 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_s_waitcnt(0xC07F);                  // lgkmcnt(0), other counters unchanged
     __builtin_amdgcn_s_barrier();
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
-
-// One direct global-to-LDS copy instruction: lane l moves the 16 bytes at its `src` to LDS
-// byte address lds + 16 l (lds is wave-uniform, passed in M0).  Written as a statement of its
-// own so that the compiler neither reorders LDS accesses across it ("memory") nor inserts
-// waits for it: the copy has no result register, and every wait for it is an explicit
-// wait_vm.  (With the builtin, the compiler would wait for all copies before any later LDS
-// access, since it cannot tell the copy's destination from the other LDS arrays.)
-__device__ __forceinline__ void copy16_to_lds(const void* src, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" : : "s"(lds), "v"(src) : "memory", "m0");
-}
-
-__device__ __forceinline__ uint32_t lds_address(const void* p) {
-    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)p));
 }
 
 template <int TYPE>

@@ -33,12 +33,20 @@
 //   a streaming rank-L update (HBM bound).  Fused variant: the next step's verify applies
 //   the same update to the state tile it has just loaded, stores the committed tile and
 //   verifies from it, so the state is read once per step instead of twice.
+#include <type_traits>
+
 #include "tv_internal.h"
 
 namespace tv {
 namespace {
 
 constexpr int kMinChannels = 16;                // narrowest verify unit (one MFMA row tile)
+// Units of the bank verify hold at most 32 value channels: the bank's operands then fit beside
+// the state tile and the unit's inputs without spilling registers.
+constexpr int kBankTiles = 4;
+// bf16 units copy their key / query rows and value rows straight from memory into LDS
+// (global-to-LDS copies) instead of holding them in registers while the state tile streams in.
+constexpr bool kStageBf16 = true;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -63,10 +71,14 @@ __device__ __forceinline__ void split_bf16(const float4& x0, const float4& x1, b
     }
 }
 
-// Contraction order shared by both MFMA operands: lane group g (lane / 16) of K-step ks
-// holds elements ks*32 + 8g .. ks*32 + 8g + 7 of its row (zero past dk).
+// Contraction order shared by every MFMA operand over the keys: lane group g (lane / 16) of
+// K-step ks holds keys ks*32 + 4g .. 4g+3 (half 0) and ks*32 + 16 + 4g .. 16 + 4g + 3 (half 1)
+// of its row, zero past dk.  (Any order gives the same dot products; this one is also the
+// accumulator layout of a 16 x 16 matrix-core tile over 16 keys, so a state tile held this way
+// can be updated by matrix instructions in place.)
 template <int DK>
-__device__ __forceinline__ bool kvalid(int ks, int g4) { return ks * 32 + 8 * g4 < DK; }
+__device__ __forceinline__ bool kvalid(int ks, int g4, int half) { return ks * 32 + 16 * half + 4 * g4 < DK; }
+__device__ __forceinline__ int kfirst(int ks, int g4, int half) { return ks * 32 + 16 * half + 4 * g4; }
 
 template <bool BF16IN>
 __device__ __forceinline__ float load_scalar(const void* base, size_t idx) {
@@ -78,39 +90,37 @@ __device__ __forceinline__ float load_scalar(const void* base, size_t idx) {
 template <int DK, bool BF16IN>
 __device__ __forceinline__ void load_row_operand(const void* row, int ks, int g4, bool valid, bf16x8& hi,
                                                  bf16x8& lo) {
-    const int r0 = ks * 32 + 8 * g4;
-    const bool ok = valid && kvalid<DK>(ks, g4);
+    const int r0 = kfirst(ks, g4, 0), r1 = kfirst(ks, g4, 1);
+    const bool ok0 = valid && kvalid<DK>(ks, g4, 0), ok1 = valid && kvalid<DK>(ks, g4, 1);
     if constexpr (BF16IN) {
-        uint4 w = make_uint4(0, 0, 0, 0);
-        if (ok) w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(row) + r0);
-        u32x4 u = {w.x, w.y, w.z, w.w};
+        uint2 w0 = make_uint2(0, 0), w1 = w0;
+        if (ok0) w0 = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(row) + r0);
+        if (ok1) w1 = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(row) + r1);
+        u32x4 u = {w0.x, w0.y, w1.x, w1.y};
         hi = __builtin_bit_cast(bf16x8, u);
         lo = bf16x8{};
     } else {
         float4 x0 = make_float4(0.f, 0.f, 0.f, 0.f), x1 = x0;
-        if (ok) {
-            const float* p = static_cast<const float*>(row) + r0;
-            x0 = *reinterpret_cast<const float4*>(p);
-            x1 = *reinterpret_cast<const float4*>(p + 4);
-        }
+        if (ok0) x0 = *reinterpret_cast<const float4*>(static_cast<const float*>(row) + r0);
+        if (ok1) x1 = *reinterpret_cast<const float4*>(static_cast<const float*>(row) + r1);
         split_bf16(x0, x1, hi, lo);
     }
 }
 
 // A unit's S0 tile (MT x 16 value channels x dk) in MFMA A-operand order.
-template <int DK>
-__device__ __forceinline__ void load_state_tile(float4 (&sa)[4][(DK + 31) / 32][2], const float* tile, int MT,
+template <int DK, int MTX>
+__device__ __forceinline__ void load_state_tile(float4 (&sa)[MTX][(DK + 31) / 32][2], const float* tile, int MT,
                                                 int l16, int g4) {
     constexpr int KS = (DK + 31) / 32;
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int mt = 0; mt < MTX; ++mt)
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            sa[mt][ks][0] = sa[mt][ks][1] = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (mt < MT && kvalid<DK>(ks, g4)) {
-                const float* p = tile + (mt * 16 + l16) * DK + ks * 32 + 8 * g4;
-                sa[mt][ks][0] = *reinterpret_cast<const float4*>(p);
-                sa[mt][ks][1] = *reinterpret_cast<const float4*>(p + 4);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                sa[mt][ks][h] = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (mt < MT && kvalid<DK>(ks, g4, h))
+                    sa[mt][ks][h] = *reinterpret_cast<const float4*>(tile + (mt * 16 + l16) * DK + kfirst(ks, g4, h));
             }
         }
 }
@@ -127,118 +137,6 @@ __device__ __forceinline__ UnitIds unit_ids(const LinVerifyArgs& a, int unit, in
     u.kh = a.tiled ? u.h % a.Hk : u.h / a.group_div;
     u.j0 = u.ct * CW;
     return u;
-}
-
-// Everything one unit reads from global memory, held in registers while in flight.
-template <int DK, int NT, bool BF16IN>
-struct UnitIn {
-    static constexpr int KS = (DK + 31) / 32;
-    static constexpr int NMAX = NT * 8;
-    static constexpr int ESZ = BF16IN ? 2 : 4;
-    static constexpr int VL = (NMAX * 64 * ESZ + 1023) / 1024;   // 16-byte v loads per lane
-    float4 sa[4][KS][2];
-    bf16x8 bh[NT][KS], bo[NT][KS];
-    uint4 vraw[VL];
-    uint32_t graw, braw;                             // lane i: node i's g and beta, raw input bits
-    int praw, nraw;                                  // lane i: parent[i]; n_nodes[b] (unclamped)
-    // a pending commit (previous step's path): its length, lane l's entry (node, decay) and
-    // the first four entries' key / delta segments (lane -> entry lane / 16, segment lane % 16)
-    int pL, pnode;
-    float pgv;
-    float pkv[8];
-    float4 pdv;
-};
-
-// Issues every load of a unit.  No address depends on loaded data (the tree size n is
-// only applied at compute time; rows up to N are loaded), so a wave can issue the next
-// unit's loads without waiting for anything.
-template <int DK, int NT, bool BF16IN>
-__device__ __forceinline__ void load_unit(UnitIn<DK, NT, BF16IN>& in, const LinVerifyArgs& a, int unit, int ctiles,
-                                          int CW, int lane) {
-    using U = UnitIn<DK, NT, BF16IN>;
-    const int g4 = lane >> 4, l16 = lane & 15;
-    const UnitIds id = unit_ids(a, unit, ctiles, CW);
-    const int N = a.N;                              // <= NMAX by dispatch
-    // wave-uniform: read through the constant address space (a scalar load, counted apart
-    // from the vector loads and stores, so nothing waits on them for it)
-    in.nraw = ((const __attribute__((address_space(4))) int32_t*)(a.n_nodes))[id.b];
-    in.praw = -1;
-    in.graw = in.braw = 0u;
-    if (lane < N) {
-        in.praw = a.parent[static_cast<size_t>(id.b) * N + lane];
-        const size_t gi = (static_cast<size_t>(id.b) * N + lane) * a.Hv + id.h;
-        if constexpr (BF16IN) {
-            in.graw = static_cast<const uint16_t*>(a.g)[gi];
-            in.braw = static_cast<const uint16_t*>(a.beta)[gi];
-        } else {
-            in.graw = static_cast<const uint32_t*>(a.g)[gi];
-            in.braw = static_cast<const uint32_t*>(a.beta)[gi];
-        }
-    }
-    // B operand columns: c < N -> k_c, N <= c < 2N -> q_{c-N}, beyond -> zero.
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-        const int c = nt * 16 + l16;
-        const bool isk = c < N;
-        const bool valid = c < 2 * N;
-        const int node = valid ? (isk ? c : c - N) : 0;
-        const size_t rowoff = ((static_cast<size_t>(id.b) * N + node) * a.Hk + id.kh) * DK;
-        const void* row = static_cast<const char*>(isk ? a.k : a.q) + rowoff * U::ESZ;
-#pragma unroll
-        for (int ks = 0; ks < U::KS; ++ks) load_row_operand<DK, BF16IN>(row, ks, g4, valid, in.bh[nt][ks], in.bo[nt][ks]);
-    }
-    // v rows of this unit's channels: 16 bytes per lane, several nodes per instruction.
-    const int epl = 16 / U::ESZ;                    // elements per lane
-    const int lpr = CW / epl;                       // lanes per node row
-    const int rpi = 64 / lpr;                       // node rows per instruction
-#pragma unroll
-    for (int t = 0; t < U::VL; ++t) {
-        const int row = t * rpi + lane / lpr, col = (lane % lpr) * epl;
-        in.vraw[t] = make_uint4(0, 0, 0, 0);
-        if (row < N)
-            in.vraw[t] = *reinterpret_cast<const uint4*>(
-                static_cast<const char*>(a.v) +
-                (((static_cast<size_t>(id.b) * N + row) * a.Hv + id.h) * a.dv + id.j0 + col) * U::ESZ);
-    }
-    const float* tile = a.state + (static_cast<size_t>(id.b) * a.Hv + id.h) * a.dv * DK + static_cast<size_t>(id.j0) * DK;
-    load_state_tile<DK>(in.sa, tile, CW >> 4, l16, g4);
-    in.pL = 0;
-    if (a.pend_path_len) {
-        // Issued last: the path entries, then (dependent on them) the decays and the first
-        // four entries' key and delta segments, so the other loads are already in flight.
-        const int PN = a.pend_N;
-        in.pL = clampi(((const __attribute__((address_space(4))) int32_t*)(a.pend_path_len))[id.b], 0, a.pend_Lmax);
-        int node = 0;
-        if (lane < a.pend_Lmax) node = clampi(a.pend_path[static_cast<size_t>(id.b) * a.pend_Lmax + lane], 0, PN - 1);
-        in.pnode = node;
-        in.pgv = lane < a.pend_Lmax ? load_scalar<BF16IN>(a.pend_g, (static_cast<size_t>(id.b) * PN + node) * a.Hv + id.h)
-                                    : 0.f;
-        const int q = lane >> 4, sg = lane & 15;
-        const int nq = __shfl(node, q);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) in.pkv[e] = 0.f;
-        in.pdv = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (sg * 8 < DK) {
-            const size_t ko = ((static_cast<size_t>(id.b) * PN + nq) * a.Hk + id.kh) * DK + sg * 8;
-            if constexpr (BF16IN) {
-                const uint4 w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.pend_k) + ko);
-                const uint32_t u[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    in.pkv[2 * e] = __uint_as_float(u[e] << 16);
-                    in.pkv[2 * e + 1] = __uint_as_float(u[e] & 0xffff0000u);
-                }
-            } else {
-                const float4 x0 = *reinterpret_cast<const float4*>(static_cast<const float*>(a.pend_k) + ko);
-                const float4 x1 = *reinterpret_cast<const float4*>(static_cast<const float*>(a.pend_k) + ko + 4);
-                in.pkv[0] = x0.x; in.pkv[1] = x0.y; in.pkv[2] = x0.z; in.pkv[3] = x0.w;
-                in.pkv[4] = x1.x; in.pkv[5] = x1.y; in.pkv[6] = x1.z; in.pkv[7] = x1.w;
-            }
-        }
-        if (sg * 4 < CW)
-            in.pdv = *reinterpret_cast<const float4*>(
-                a.pend_delta + ((static_cast<size_t>(id.b) * PN + nq) * a.Hv + id.h) * a.dv + id.j0 + sg * 4);
-    }
 }
 
 // Shared memory of one verify wave, kept at or under 20 KiB for trees of up to 24 nodes so
@@ -279,16 +177,196 @@ __device__ __forceinline__ float* cs_at(SM& sm, int row, int col) {
     return &sm.Cs[row][col ^ ((row & 15) << 2)];
 }
 
-template <int DK, int NT, bool BF16IN>
-__device__ __forceinline__ int compute_unit(const UnitIn<DK, NT, BF16IN>& in, VerifySmem<NT, BF16IN>& sm,
+// Everything one unit reads from global memory, held in registers while in flight.  MTX: the
+// most 16-channel pieces a unit holds (4: up to 64 channels).
+template <int DK, int NT, bool BF16IN, int MTX = 4>
+struct UnitIn {
+    static constexpr int KS = (DK + 31) / 32;
+    static constexpr int NMAX = NT * 8;
+    static constexpr int ESZ = BF16IN ? 2 : 4;
+    static constexpr int VL = (NMAX * 64 * ESZ + 1023) / 1024;   // 16-byte v loads per lane
+    float4 sa[MTX][KS][2];
+    bf16x8 bh[NT][KS], bo[NT][KS];
+    uint4 vraw[VL];
+    uint32_t graw, braw;                             // lane i: node i's g and beta, raw input bits
+    int praw, nraw;                                  // lane i: parent[i]; n_nodes[b] (unclamped)
+    // a pending commit (previous step's path): its length, lane l's entry (node, decay) and
+    // the first four entries' key / delta segments (lane -> entry lane / 16, segment lane % 16)
+    int pL, pnode;
+    int bE;                                          // bank mode: entries already in the bank
+    float pgv;
+    float pkv[8];
+    float4 pdv;
+};
+
+// Issues every load of a unit.  No address depends on loaded data (the tree size n is
+// only applied at compute time; rows up to N are loaded), so a wave can issue the next
+// unit's loads without waiting for anything.
+template <int DK, int NT, bool BF16IN, bool STAGE, bool PRELOAD = true, int MTX = 4>
+__device__ __forceinline__ void load_unit(UnitIn<DK, NT, BF16IN, MTX>& in, VerifySmem<NT, BF16IN>& sm,
+                                          const LinVerifyArgs& a, int unit, int ctiles, int CW, int lane) {
+    using U = UnitIn<DK, NT, BF16IN, MTX>;
+    const int g4 = lane >> 4, l16 = lane & 15;
+    const UnitIds id = unit_ids(a, unit, ctiles, CW);
+    const int N = a.N;                              // <= NMAX by dispatch
+    // wave-uniform: read through the constant address space (a scalar load, counted apart
+    // from the vector loads and stores, so nothing waits on them for it)
+    in.nraw = N > 0 ? ((const __attribute__((address_space(4))) int32_t*)(a.n_nodes))[id.b] : 0;
+    in.praw = -1;
+    in.graw = in.braw = 0u;
+    if (lane < N) {
+        in.praw = a.parent[static_cast<size_t>(id.b) * N + lane];
+        const size_t gi = (static_cast<size_t>(id.b) * N + lane) * a.Hv + id.h;
+        if constexpr (BF16IN) {
+            in.graw = static_cast<const uint16_t*>(a.g)[gi];
+            in.braw = static_cast<const uint16_t*>(a.beta)[gi];
+        } else {
+            in.graw = static_cast<const uint32_t*>(a.g)[gi];
+            in.braw = static_cast<const uint32_t*>(a.beta)[gi];
+        }
+    }
+    if constexpr (STAGE) {
+        static_assert(BF16IN, "staged rows are bf16");
+        if (N > 0) {                                // (N = 0: a flush without a tree)
+            // B operand columns c (< N: k_c; < 2N: q_{c-N}; beyond: k_0, never used) as LDS rows of
+            // Cs, row c at byte 2 DK c; its 16-byte pieces are stored XOR-rotated by the row index
+            // (piece p at slot p ^ (c mod LPR)), so the 16 rows a matrix-core operand read touches
+            // fall in different banks.  One copy instruction moves 1 KiB: RPI whole rows.
+            constexpr int LPR = DK / 8, RPI = 64 / LPR, NI = (NT * 16 + RPI - 1) / RPI;   // <= Cs
+            const uint32_t cs = lds_address(&sm.Cs[0][0]);
+            const int rr = lane / LPR, ck = lane % LPR;
+#pragma unroll
+            for (int j = 0; j < NI; ++j) {
+                const int c = j * RPI + rr;
+                const bool isq = c >= N && c < 2 * N;
+                const int node = c < N ? c : (isq ? c - N : 0);
+                const uint16_t* row = static_cast<const uint16_t*>(isq ? a.q : a.k) +
+                                      ((static_cast<size_t>(id.b) * N + node) * a.Hk + id.kh) * DK;
+                copy16_to_lds(row + (ck ^ (c & (LPR - 1))) * 8, __builtin_amdgcn_readfirstlane(cs + j * 1024));
+            }
+            // v rows of the unit's channels into Vs, row i at byte 2 CW i (rows past N repeat N - 1)
+            const int lprv = CW / 8, rpiv = 64 / lprv, niv = (U::NMAX + rpiv - 1) / rpiv;
+            const uint32_t vs = lds_address(&sm.Vs[0]);
+            for (int j = 0; j < niv; ++j) {
+                const int row = j * rpiv + lane / lprv;
+                const int node = row < N ? row : N - 1;
+                const uint16_t* src = static_cast<const uint16_t*>(a.v) +
+                                      ((static_cast<size_t>(id.b) * N + node) * a.Hv + id.h) * a.dv + id.j0 + (lane % lprv) * 8;
+                copy16_to_lds(src, __builtin_amdgcn_readfirstlane(vs + j * 1024));
+            }
+        }
+    } else {
+        // B operand columns: c < N -> k_c, N <= c < 2N -> q_{c-N}, beyond -> zero.
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            const int c = nt * 16 + l16;
+            const bool isk = c < N;
+            const bool valid = c < 2 * N;
+            const int node = valid ? (isk ? c : c - N) : 0;
+            const size_t rowoff = ((static_cast<size_t>(id.b) * N + node) * a.Hk + id.kh) * DK;
+            const void* row = static_cast<const char*>(isk ? a.k : a.q) + rowoff * U::ESZ;
+#pragma unroll
+            for (int ks = 0; ks < U::KS; ++ks) load_row_operand<DK, BF16IN>(row, ks, g4, valid, in.bh[nt][ks], in.bo[nt][ks]);
+        }
+        // v rows of this unit's channels: 16 bytes per lane, several nodes per instruction.
+        const int epl = 16 / U::ESZ;                    // elements per lane
+        const int lpr = CW / epl;                       // lanes per node row
+        const int rpi = 64 / lpr;                       // node rows per instruction
+#pragma unroll
+        for (int t = 0; t < U::VL; ++t) {
+            const int row = t * rpi + lane / lpr, col = (lane % lpr) * epl;
+            in.vraw[t] = make_uint4(0, 0, 0, 0);
+            if (row < N)
+                in.vraw[t] = *reinterpret_cast<const uint4*>(
+                    static_cast<const char*>(a.v) +
+                    (((static_cast<size_t>(id.b) * N + row) * a.Hv + id.h) * a.dv + id.j0 + col) * U::ESZ);
+        }
+    }
+    const float* tile = a.state + (static_cast<size_t>(id.b) * a.Hv + id.h) * a.dv * DK + static_cast<size_t>(id.j0) * DK;
+    load_state_tile<DK, MTX>(in.sa, tile, CW >> 4, l16, g4);
+    in.pL = 0;
+    if (a.pend_path_len) {
+        // Issued last: the path entries, then (dependent on them) the decays and the first
+        // four entries' key and delta segments, so the other loads are already in flight.
+        const int PN = a.pend_N;
+        in.pL = clampi(((const __attribute__((address_space(4))) int32_t*)(a.pend_path_len))[id.b], 0, a.pend_Lmax);
+        int node = 0;
+        if (lane < a.pend_Lmax) node = clampi(a.pend_path[static_cast<size_t>(id.b) * a.pend_Lmax + lane], 0, PN - 1);
+        in.pnode = node;
+        in.pgv = lane < a.pend_Lmax ? load_scalar<BF16IN>(a.pend_g, (static_cast<size_t>(id.b) * PN + node) * a.Hv + id.h)
+                                    : 0.f;
+        if constexpr (!PRELOAD) return;             // apply_pending loads every entry itself
+        const int q = lane >> 4, sg = lane & 15;
+        const int nq = __shfl(node, q);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) in.pkv[e] = 0.f;
+        in.pdv = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (sg * 8 < DK) {
+            const size_t ko = ((static_cast<size_t>(id.b) * PN + nq) * a.Hk + id.kh) * DK + sg * 8;
+            if constexpr (BF16IN) {
+                const uint4 w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.pend_k) + ko);
+                const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    in.pkv[2 * e] = __uint_as_float(u[e] << 16);
+                    in.pkv[2 * e + 1] = __uint_as_float(u[e] & 0xffff0000u);
+                }
+            } else {
+                const float4 x0 = *reinterpret_cast<const float4*>(static_cast<const float*>(a.pend_k) + ko);
+                const float4 x1 = *reinterpret_cast<const float4*>(static_cast<const float*>(a.pend_k) + ko + 4);
+                in.pkv[0] = x0.x; in.pkv[1] = x0.y; in.pkv[2] = x0.z; in.pkv[3] = x0.w;
+                in.pkv[4] = x1.x; in.pkv[5] = x1.y; in.pkv[6] = x1.z; in.pkv[7] = x1.w;
+            }
+        }
+        if (sg * 4 < CW)
+            in.pdv = *reinterpret_cast<const float4*>(
+                a.pend_delta + ((static_cast<size_t>(id.b) * PN + nq) * a.Hv + id.h) * a.dv + id.j0 + sg * 4);
+    }
+}
+
+// This lane's matrix-core operand (K-step ks) of column c from the staged LDS rows: keys
+// kfirst(ks, g4, 0..1) .. +3, i.e. 16-byte piece ks*4 + 2h + g4/2 of row c, half g4 & 1 of it,
+// at its XOR-rotated slot.
+template <int DK>
+__device__ __forceinline__ bf16x8 staged_operand(const float* rows, int c, int ks, int g4) {
+    constexpr int LPR = DK / 8;
+    const uint8_t* row = reinterpret_cast<const uint8_t*>(rows) + c * DK * 2;
+    uint2 w[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int slot = ((ks * 4 + 2 * h + (g4 >> 1)) ^ (c & (LPR - 1))) & (LPR - 1);
+        w[h] = make_uint2(0, 0);
+        if (kvalid<DK>(ks, g4, h)) w[h] = *reinterpret_cast<const uint2*>(row + slot * 16 + (g4 & 1) * 8);
+    }
+    u32x4 u = {w[0].x, w[0].y, w[1].x, w[1].y};
+    return __builtin_bit_cast(bf16x8, u);
+}
+
+template <int DK, int NT, bool BF16IN, bool STAGE, int MTX>
+__device__ __forceinline__ int compute_unit(const UnitIn<DK, NT, BF16IN, MTX>& in, VerifySmem<NT, BF16IN>& sm,
                                             const LinVerifyArgs& a, int unit, int ctiles, int CW, int lane) {
-    using U = UnitIn<DK, NT, BF16IN>;
+    using U = UnitIn<DK, NT, BF16IN, MTX>;
     constexpr int KS = U::KS, NMAX = U::NMAX, GT = (NMAX + 15) / 16;
     const int g4 = lane >> 4, l16 = lane & 15;
     const int N = a.N;
+    // staged rows: every copy of this wave has landed (also before an early exit, so that none
+    // is still writing LDS when the workgroup ends)
+    if constexpr (STAGE) asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
     const int n = clampi(in.nraw, 0, N);
     if (n <= 0) return 0;
     const int MT = CW >> 4;
+    // the B operands: from the staged LDS rows, or loaded into registers with the unit's inputs
+    bf16x8 opnd[STAGE ? NT : 1][KS];
+    if constexpr (STAGE) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) opnd[nt][ks] = staged_operand<DK>(&sm.Cs[0][0], nt * 16 + l16, ks, g4);
+    }
+    auto bop = [&](int nt, int ks) -> const bf16x8& {
+        if constexpr (STAGE) return opnd[nt][ks];
+        else return in.bh[nt][ks];
+    };
     // this lane's node (lane < n): parent, decay and write strength; zero beyond the tree
     const bool real = lane < n;
     const int pme = real && lane > 0 ? clampi(in.praw, 0, lane - 1) : -1;
@@ -307,7 +385,7 @@ __device__ __forceinline__ int compute_unit(const UnitIn<DK, NT, BF16IN>& in, Ve
         sm.Gm[lane][GC] = gme;
         sm.Gm[lane][GC + 1] = __int_as_float(pme);
     }
-    {
+    if constexpr (!STAGE) {
         const int epl = 16 / U::ESZ, lpr = CW / epl, rpi = 64 / lpr;
 #pragma unroll
         for (int t = 0; t < U::VL; ++t) {
@@ -323,7 +401,7 @@ __device__ __forceinline__ int compute_unit(const UnitIn<DK, NT, BF16IN>& in, Ve
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                acc = mfma16x16x32(in.bh[gt][ks], in.bh[nt][ks], acc);
+                acc = mfma16x16x32(bop(gt, ks), bop(nt, ks), acc);
                 if constexpr (!BF16IN) {
                     acc = mfma16x16x32(in.bh[gt][ks], in.bo[nt][ks], acc);
                     acc = mfma16x16x32(in.bo[gt][ks], in.bh[nt][ks], acc);
@@ -338,7 +416,7 @@ __device__ __forceinline__ int compute_unit(const UnitIn<DK, NT, BF16IN>& in, Ve
 
     // 2. S0^T x_c for the unit's channels.
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
+    for (int mt = 0; mt < MTX; ++mt) {
         if (mt >= MT) continue;
         bf16x8 ah[KS], al[KS];
 #pragma unroll
@@ -348,8 +426,8 @@ __device__ __forceinline__ int compute_unit(const UnitIn<DK, NT, BF16IN>& in, Ve
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                acc = mfma16x16x32(ah[ks], in.bh[nt][ks], acc);
-                acc = mfma16x16x32(al[ks], in.bh[nt][ks], acc);
+                acc = mfma16x16x32(ah[ks], bop(nt, ks), acc);
+                acc = mfma16x16x32(al[ks], bop(nt, ks), acc);
                 if constexpr (!BF16IN) acc = mfma16x16x32(ah[ks], in.bo[nt][ks], acc);
             }
             *reinterpret_cast<float4*>(cs_at(sm, nt * 16 + l16, mt * 16 + 4 * g4)) = make_float4(acc[0], acc[1], acc[2], acc[3]);
@@ -384,8 +462,9 @@ __device__ __forceinline__ int compute_unit(const UnitIn<DK, NT, BF16IN>& in, Ve
         sm.cd[lane] = cdv;
     }
     __syncthreads();
+    const int vst = STAGE ? CW : 64;                // Vs row stride (elements)
     auto v_of = [&](int i) {
-        if constexpr (BF16IN) return bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(sm.Vs)[i * 64 + lane]);
+        if constexpr (BF16IN) return bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(sm.Vs)[i * vst + lane]);
         else return reinterpret_cast<const float*>(sm.Vs)[i * 64 + lane];
     };
 
@@ -454,13 +533,33 @@ __device__ __forceinline__ void store_unit(VerifySmem<NT, BF16IN>& sm, const Lin
     __syncthreads();                                // LDS is reused by the next unit
 }
 
+// Stores the unit's state tile (held in the key order of kfirst) at its place in the state.
+template <int DK, int MTX>
+__device__ __forceinline__ void store_state_tile(const float4 (&sa)[MTX][(DK + 31) / 32][2], float* state, const UnitIds& id,
+                                                 int Hv, int dv, int MT, int g4, int l16) {
+    constexpr int KS = (DK + 31) / 32;
+    float* tile = state + (static_cast<size_t>(id.b) * Hv + id.h) * dv * DK + static_cast<size_t>(id.j0) * DK;
+#pragma unroll
+    for (int mt = 0; mt < MTX; ++mt)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                if (mt < MT && kvalid<DK>(ks, g4, h))
+                    *reinterpret_cast<float4*>(tile + (mt * 16 + l16) * DK + kfirst(ks, g4, h)) = sa[mt][ks][h];
+}
+
 // Commits the previous step's accepted path a_0 .. a_{L-1} into the unit's state tile, in
-// registers, and stores the committed tile:  S <- G S + sum_l c_l k_{a_l} delta_{a_l}^T with
-// G = prod_l g_{a_l} and c_l = prod_{l' > l} g_{a_l'} (the commit's formula).  Entries are
-// staged four at a time through LDS that the unit's own computation overwrites later.
-template <int DK, int NT, bool BF16IN>
-__device__ __forceinline__ void apply_pending(UnitIn<DK, NT, BF16IN>& in, VerifySmem<NT, BF16IN>& sm,
-                                              const LinVerifyArgs& a, int unit, int ctiles, int CW, int lane) {
+// registers:  S <- G S + sum_l c_l k_{a_l} delta_{a_l}^T with G = prod_l g_{a_l} and
+// c_l = prod_{l' > l} g_{a_l'} (the commit's formula).  Entries are staged four at a time
+// through LDS that the unit's own computation overwrites later.  `store`: the committed tile
+// is stored.  `to_bank`: the path's entries are also written to the pending bank after its
+// first `E0` entries -- the unit's channels of each captured delta, the decays (by the unit of
+// channel tile 0) and the keys (by the first value head that reads the key head).
+template <int DK, int NT, bool BF16IN, bool PRE = true, int MTX = 4>
+__device__ __forceinline__ void apply_pending(UnitIn<DK, NT, BF16IN, MTX>& in, VerifySmem<NT, BF16IN>& sm,
+                                              const LinVerifyArgs& a, int unit, int ctiles, int CW, int lane,
+                                              bool store = true, bool to_bank = false, int E0 = 0) {
     constexpr int KS = (DK + 31) / 32;
     auto& sa = in.sa;
     const UnitIds id = unit_ids(a, unit, ctiles, CW);
@@ -472,6 +571,13 @@ __device__ __forceinline__ void apply_pending(UnitIn<DK, NT, BF16IN>& in, Verify
         sm.pn[lane] = in.pnode;
         sm.pg[lane] = in.pgv;
     }
+    // the bank's slices this unit writes (wave-uniform)
+    const size_t Emax = static_cast<size_t>(a.bank_Emax);
+    const bool key_writer = to_bank && id.ct == 0 && id.h == (a.tiled ? id.kh : id.kh * a.group_div);
+    float* bdel = to_bank ? a.bank_delta + ((static_cast<size_t>(id.b) * a.Hv + id.h) * a.dv + id.j0) * Emax + E0
+                          : nullptr;
+    if (to_bank && id.ct == 0 && lane < L)
+        a.bank_g[(static_cast<size_t>(id.b) * a.Hv + id.h) * Emax + E0 + lane] = in.pgv;
     __syncthreads();
     if (lane < L) {
         float c = 1.f;
@@ -481,7 +587,7 @@ __device__ __forceinline__ void apply_pending(UnitIn<DK, NT, BF16IN>& in, Verify
     __syncthreads();
     const float G = sm.pc[0] * sm.pg[0];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int mt = 0; mt < MTX; ++mt)
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
@@ -492,38 +598,61 @@ __device__ __forceinline__ void apply_pending(UnitIn<DK, NT, BF16IN>& in, Verify
         {   // lane -> (entry q, segment s): 8 key elements and 4 channels of c_l * delta_l
             const int q = lane >> 4, s = lane & 15, l = c0 + q;
             float kv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-            float4 dv4 = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (c0 == 0) {                          // loaded with the unit's inputs
+            float4 draw = make_float4(0.f, 0.f, 0.f, 0.f);   // delta_l, this lane's 4 channels
+            if (PRE && c0 == 0) {                   // loaded with the unit's inputs
                 if (l < L) {
 #pragma unroll
                     for (int e = 0; e < 8; ++e) kv[e] = in.pkv[e];
-                    const float cl = sm.pc[l];
-                    dv4 = make_float4(cl * in.pdv.x, cl * in.pdv.y, cl * in.pdv.z, cl * in.pdv.w);
+                    draw = in.pdv;
                 }
-            } else if (l < L) {
-                const int node = sm.pn[l];
-                if (s * 8 < DK) {
-                    const size_t ko = ((static_cast<size_t>(id.b) * PN + node) * a.Hk + id.kh) * DK + s * 8;
-                    if constexpr (BF16IN) {
-                        const uint4 w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.pend_k) + ko);
-                        const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+            } else {
+                // every lane loads (clamped to entry L - 1 and to the first key / channel
+                // segment) and then selects: no lane-dependent branch around the loads
+                const int node = sm.pn[l < L ? l : L - 1];
+                const bool kok = l < L && s * 8 < DK, dok = l < L && s * 4 < CW;
+                const size_t ko = ((static_cast<size_t>(id.b) * PN + node) * a.Hk + id.kh) * DK + (s * 8 < DK ? s * 8 : 0);
+                if constexpr (BF16IN) {
+                    const uint4 w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.pend_k) + ko);
+                    const uint32_t u[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            kv[2 * e] = __uint_as_float(u[e] << 16);
-                            kv[2 * e + 1] = __uint_as_float(u[e] & 0xffff0000u);
-                        }
-                    } else {
-                        const float4 x0 = *reinterpret_cast<const float4*>(static_cast<const float*>(a.pend_k) + ko);
-                        const float4 x1 = *reinterpret_cast<const float4*>(static_cast<const float*>(a.pend_k) + ko + 4);
-                        kv[0] = x0.x; kv[1] = x0.y; kv[2] = x0.z; kv[3] = x0.w;
-                        kv[4] = x1.x; kv[5] = x1.y; kv[6] = x1.z; kv[7] = x1.w;
+                    for (int e = 0; e < 4; ++e) {
+                        kv[2 * e] = kok ? __uint_as_float(u[e] << 16) : 0.f;
+                        kv[2 * e + 1] = kok ? __uint_as_float(u[e] & 0xffff0000u) : 0.f;
                     }
+                } else {
+                    const float4 x0 = *reinterpret_cast<const float4*>(static_cast<const float*>(a.pend_k) + ko);
+                    const float4 x1 = *reinterpret_cast<const float4*>(static_cast<const float*>(a.pend_k) + ko + 4);
+                    const float xv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) kv[e] = kok ? xv[e] : 0.f;
                 }
+                const float4 d = *reinterpret_cast<const float4*>(
+                    a.pend_delta + ((static_cast<size_t>(id.b) * PN + node) * a.Hv + id.h) * a.dv + id.j0 +
+                    (s * 4 < CW ? s * 4 : 0));
+                if (dok) draw = d;
+            }
+            float4 dv4 = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (l < L) {
+                const float cl = sm.pc[l];
+                dv4 = make_float4(cl * draw.x, cl * draw.y, cl * draw.z, cl * draw.w);
+            }
+            if (to_bank && l < L) {
+                // raw entries (c_l is applied when the bank is read), at entry E0 + l
                 if (s * 4 < CW) {
-                    const float cl = sm.pc[l];
-                    const float4 d = *reinterpret_cast<const float4*>(
-                        a.pend_delta + ((static_cast<size_t>(id.b) * PN + node) * a.Hv + id.h) * a.dv + id.j0 + s * 4);
-                    dv4 = make_float4(cl * d.x, cl * d.y, cl * d.z, cl * d.w);
+                    bdel[(s * 4 + 0) * Emax + l] = draw.x;
+                    bdel[(s * 4 + 1) * Emax + l] = draw.y;
+                    bdel[(s * 4 + 2) * Emax + l] = draw.z;
+                    bdel[(s * 4 + 3) * Emax + l] = draw.w;
+                }
+                if (key_writer && s * 8 < DK) {
+                    using E = typename std::conditional<BF16IN, uint16_t, uint32_t>::type;
+                    E* kb = static_cast<E*>(a.bank_k) + ((static_cast<size_t>(id.b) * a.Hk + id.kh) * DK + s * 8) * Emax +
+                            E0 + l;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        if constexpr (BF16IN) kb[i * Emax] = static_cast<uint16_t>(__float_as_uint(kv[i]) >> 16);
+                        else kb[i * Emax] = __float_as_uint(kv[i]);
+                    }
                 }
             }
             if (s * 8 < 128) {
@@ -538,42 +667,168 @@ __device__ __forceinline__ void apply_pending(UnitIn<DK, NT, BF16IN>& in, Verify
         for (int q = 0; q < 4; ++q) {
             if (q >= nq) break;
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
+            for (int mt = 0; mt < MTX; ++mt) {
                 const float dj = sm.pd[q][(mt * 16 + l16) & 63];
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
-                    if (!kvalid<DK>(ks, g4)) continue;
-                    const float4 k0 = *reinterpret_cast<const float4*>(&sm.pk[q][ks * 32 + 8 * g4]);
-                    const float4 k1 = *reinterpret_cast<const float4*>(&sm.pk[q][ks * 32 + 8 * g4 + 4]);
-                    float4& x0 = sa[mt][ks][0];
-                    float4& x1 = sa[mt][ks][1];
-                    x0.x = fmaf(dj, k0.x, x0.x); x0.y = fmaf(dj, k0.y, x0.y);
-                    x0.z = fmaf(dj, k0.z, x0.z); x0.w = fmaf(dj, k0.w, x0.w);
-                    x1.x = fmaf(dj, k1.x, x1.x); x1.y = fmaf(dj, k1.y, x1.y);
-                    x1.z = fmaf(dj, k1.z, x1.z); x1.w = fmaf(dj, k1.w, x1.w);
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        if (!kvalid<DK>(ks, g4, h)) continue;   // keys past dk stay zero
+                        const float4 kk = *reinterpret_cast<const float4*>(&sm.pk[q][kfirst(ks, g4, h)]);
+                        float4& x = sa[mt][ks][h];
+                        x.x = fmaf(dj, kk.x, x.x); x.y = fmaf(dj, kk.y, x.y);
+                        x.z = fmaf(dj, kk.z, x.z); x.w = fmaf(dj, kk.w, x.w);
+                    }
                 }
             }
         }
         __syncthreads();
     }
-    // the committed tile, in place
-    float* tile = a.state_out + (static_cast<size_t>(id.b) * a.Hv + id.h) * a.dv * DK + static_cast<size_t>(id.j0) * DK;
+    if (store) store_state_tile<DK, MTX>(sa, a.state_out, id, a.Hv, a.dv, MT, g4, l16);
+}
+
+// Applies the pending bank's E entries (earlier steps' accepted paths, in order) to the unit's
+// state tile in registers:  S <- G S + sum_e c_e k_e delta_e^T  with G = prod_e g_e and
+// c_e = prod_{e' > e} g_e' -- the same update as committing each step's path in turn.  The
+// bank is channel-major (bank_k[b][kh][key][e], bank_delta[b][h][channel][e]), so the rank-E
+// update runs on the matrix cores with the tile itself as the accumulator: for every 16-key x
+// 16-channel piece, C[key][ch] += K^T[key][e] (c . delta)[e][ch] over 32 entries per
+// instruction (keys are the exact bf16 inputs, or fp32 split hi + lo; c_e delta_e is split into
+// bf16 hi + lo, so each term is exact to about 2^-16 relative).
+template <int DK, int NT, bool BF16IN, int MTX>
+__device__ __forceinline__ void apply_bank(UnitIn<DK, NT, BF16IN, MTX>& in, VerifySmem<NT, BF16IN>& sm,
+                                           const LinVerifyArgs& a, int unit, int ctiles, int CW, int lane) {
+    constexpr int KS = (DK + 31) / 32;
+    constexpr int ESZ = BF16IN ? 2 : 4;
+    auto& sa = in.sa;
+    const int E = in.bE;                            // in [0, Emax]
+    const int Emax = a.bank_Emax;                   // a multiple of 32, at most 256
+    if (E == 0) return;                             // an empty bank: the tile is the stored state
+    const UnitIds id = unit_ids(a, unit, ctiles, CW);
+    const int g4 = lane >> 4, l16 = lane & 15, MT = CW >> 4;
+    // suffix products of the decays: lane l holds entries 4l .. 4l+3 (decay 1 past E)
+    const float* gb = a.bank_g + (static_cast<size_t>(id.b) * a.Hv + id.h) * Emax;
+    // (every lane loads, from a clamped index, and selects: no lane-dependent branch here,
+    // where the tile and the unit's inputs hold most registers)
+    float gl[4];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int i = 0; i < 4; ++i) {
+        const float x = gb[min(4 * lane + i, Emax - 1)];
+        gl[i] = 4 * lane + i < E ? x : 1.f;
+    }
+    float inc = (gl[0] * gl[1]) * (gl[2] * gl[3]);   // becomes the product over lanes >= this one
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const float o = __shfl_down(inc, off);
+        if (lane + off < 64) inc *= o;
+    }
+    float ex = __shfl_down(inc, 1);                 // product over the lanes after this one
+    if (lane == 63) ex = 1.f;
+    const float G = __shfl(inc, 0);
+    float* cbuf = &sm.pk[0][0];                     // free until the pending path is staged
+    *reinterpret_cast<float4*>(&cbuf[4 * lane]) =
+        make_float4(gl[1] * gl[2] * gl[3] * ex, gl[2] * gl[3] * ex, gl[3] * ex, ex);
+    __syncthreads();
+#pragma unroll
+    for (int mt = 0; mt < MTX; ++mt)
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
-            if (mt < MT && kvalid<DK>(ks, g4)) {
-                float* p = tile + (mt * 16 + l16) * DK + ks * 32 + 8 * g4;
-                *reinterpret_cast<float4*>(p) = sa[mt][ks][0];
-                *reinterpret_cast<float4*>(p + 4) = sa[mt][ks][1];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                sa[mt][ks][h].x *= G; sa[mt][ks][h].y *= G; sa[mt][ks][h].z *= G; sa[mt][ks][h].w *= G;
             }
+    const uint8_t* kb = static_cast<const uint8_t*>(a.bank_k) +
+                        (static_cast<size_t>(id.b) * a.Hk + id.kh) * DK * Emax * ESZ;
+    const float* db = a.bank_delta + ((static_cast<size_t>(id.b) * a.Hv + id.h) * a.dv + id.j0) * Emax;
+    for (int e0 = 0; e0 < E; e0 += 32) {
+        const int ef = e0 + 8 * g4;                 // first of this lane's eight entries
+        const int nv = clampi(E - ef, 0, 8);        // how many of them are pending
+        // Two passes of two 16-channel pieces each (fewer live operands; the keys are re-read
+        // from the cache in the second pass).
+        const float4 c0 = *reinterpret_cast<const float4*>(&cbuf[ef]), c1 = *reinterpret_cast<const float4*>(&cbuf[ef + 4]);
+#pragma unroll
+        for (int mp = 0; mp < MTX; mp += 2) {
+            // B operands: c_e delta_e[channel] for entries ef .. ef+7 of channel mt*16 + l16
+            bf16x8 bhi[2], blo[2];
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+                const int mt = mp + m;
+                float4 d0 = make_float4(0.f, 0.f, 0.f, 0.f), d1 = d0;
+                if (mt < MT) {
+                    const float* dr = db + static_cast<size_t>(mt * 16 + l16) * Emax + ef;
+                    d0 = *reinterpret_cast<const float4*>(dr);
+                    d1 = *reinterpret_cast<const float4*>(dr + 4);
+                }
+                float4 m0, m1;                      // entries past E contribute exactly zero
+                m0.x = 0 < nv ? c0.x * d0.x : 0.f; m0.y = 1 < nv ? c0.y * d0.y : 0.f;
+                m0.z = 2 < nv ? c0.z * d0.z : 0.f; m0.w = 3 < nv ? c0.w * d0.w : 0.f;
+                m1.x = 4 < nv ? c1.x * d1.x : 0.f; m1.y = 5 < nv ? c1.y * d1.y : 0.f;
+                m1.z = 6 < nv ? c1.z * d1.z : 0.f; m1.w = 7 < nv ? c1.w * d1.w : 0.f;
+                split_bf16(m0, m1, bhi[m], blo[m]);
+            }
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    if (ks * 32 + 16 * h >= DK) continue;     // the key tile is past dk
+                    // A operand: K^T[key][ef .. ef+7] for key ks*32 + 16h + l16
+                    const uint8_t* kr = kb + (static_cast<size_t>(ks * 32 + 16 * h + l16) * Emax + ef) * ESZ;
+                    bf16x8 ahi, alo;
+                    if constexpr (BF16IN) {
+                        const uint4 w = *reinterpret_cast<const uint4*>(kr);
+                        uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            const uint32_t keep = (2 * j < nv ? 0x0000ffffu : 0u) | (2 * j + 1 < nv ? 0xffff0000u : 0u);
+                            u[j] &= keep;
+                        }
+                        u32x4 uv = {u[0], u[1], u[2], u[3]};
+                        ahi = __builtin_bit_cast(bf16x8, uv);
+                        alo = bf16x8{};
+                    } else {
+                        float4 x0 = *reinterpret_cast<const float4*>(kr), x1 = *reinterpret_cast<const float4*>(kr + 16);
+                        x0.x = 0 < nv ? x0.x : 0.f; x0.y = 1 < nv ? x0.y : 0.f; x0.z = 2 < nv ? x0.z : 0.f;
+                        x0.w = 3 < nv ? x0.w : 0.f; x1.x = 4 < nv ? x1.x : 0.f; x1.y = 5 < nv ? x1.y : 0.f;
+                        x1.z = 6 < nv ? x1.z : 0.f; x1.w = 7 < nv ? x1.w : 0.f;
+                        split_bf16(x0, x1, ahi, alo);
+                    }
+#pragma unroll
+                    for (int m = 0; m < 2; ++m) {   // mt >= MT: a zero B operand, a zero tile
+                        float4& t = sa[mp + m][ks][h];
+                        f32x4 acc = {t.x, t.y, t.z, t.w};
+                        acc = mfma16x16x32(ahi, bhi[m], acc);
+                        acc = mfma16x16x32(ahi, blo[m], acc);
+                        if constexpr (!BF16IN) acc = mfma16x16x32(alo, bhi[m], acc);
+                        t = make_float4(acc[0], acc[1], acc[2], acc[3]);
+                    }
+                }
+        }
+    }
+    __syncthreads();                                // cbuf is read before Cs is rewritten
+}
+
+// Bank mode: the committed state is the stored tile, then the bank's entries, then the
+// previous step's path.  All three are applied in registers; then either the path is
+// appended to the bank (the stored tile is left alone), or -- when it would not fit
+// (E + L > Emax) or a flush is asked for -- the committed tile is stored and the bank's
+// length is reset after the launch.  Every unit of a sequence takes the same decision.
+template <int DK, int NT, bool BF16IN, int MTX>
+__device__ __forceinline__ void commit_with_bank(UnitIn<DK, NT, BF16IN, MTX>& in, VerifySmem<NT, BF16IN>& sm,
+                                                 const LinVerifyArgs& a, int unit, int ctiles, int CW, int lane) {
+    const UnitIds id = unit_ids(a, unit, ctiles, CW);
+    in.bE = clampi(((const __attribute__((address_space(4))) int32_t*)(a.bank_len))[id.b], 0, a.bank_Emax);
+    const bool flush = a.bank_flush || in.pL > a.bank_Emax - in.bE;
+    apply_bank<DK, NT, BF16IN, MTX>(in, sm, a, unit, ctiles, CW, lane);
+    apply_pending<DK, NT, BF16IN, true, MTX>(in, sm, a, unit, ctiles, CW, lane, false, !flush, in.bE);
+    if (flush && in.bE + in.pL > 0)
+        store_state_tile<DK, MTX>(in.sa, a.state_out, id, a.Hv, a.dv, CW >> 4, lane >> 4, lane & 15);
 }
 
 // Verify for trees of up to 32 nodes: one unit per workgroup of one wave.  The hardware
 // dispatcher keeps several units resident per CU (registers allow two waves per SIMD, the
 // LDS footprint seven workgroups per CU), so one unit's memory latency hides behind
 // another's arithmetic.
-template <int DK, int NT, bool BF16IN>
+template <int DK, int NT, bool BF16IN, bool BANK>
 __global__ __launch_bounds__(64, 2) void lin_verify_kernel(LinVerifyArgs a) {
     static_assert(NT <= 4, "register walk is for trees of up to 32 nodes");
     __shared__ VerifySmem<NT, BF16IN> sm;
@@ -581,16 +836,18 @@ __global__ __launch_bounds__(64, 2) void lin_verify_kernel(LinVerifyArgs a) {
     const int CW = a.cw;
     const int ctiles = a.dv / CW;
     const int u = xcd_remap(blockIdx.x, gridDim.x);
-    UnitIn<DK, NT, BF16IN> in;
-    load_unit(in, a, u, ctiles, CW, lane);
-    if (a.pend_path_len) apply_pending<DK, NT, BF16IN>(in, sm, a, u, ctiles, CW, lane);
-    const int n = compute_unit(in, sm, a, u, ctiles, CW, lane);
+    constexpr bool STAGE = BF16IN && kStageBf16;
+    UnitIn<DK, NT, BF16IN, BANK ? kBankTiles : 4> in;
+    load_unit<DK, NT, BF16IN, STAGE>(in, sm, a, u, ctiles, CW, lane);
+    if constexpr (BANK) commit_with_bank(in, sm, a, u, ctiles, CW, lane);
+    else if (a.pend_path_len) apply_pending<DK, NT, BF16IN>(in, sm, a, u, ctiles, CW, lane);
+    const int n = compute_unit<DK, NT, BF16IN, STAGE>(in, sm, a, u, ctiles, CW, lane);
     store_unit(sm, a, u, n, ctiles, CW, lane);
 }
 
 // Verify for trees of 33..64 nodes: the same unit, with up to 512 registers per lane (one
 // wave per SIMD per workgroup slot) for the wider operand set and the longer register walk.
-template <int DK, int NT, bool BF16IN>
+template <int DK, int NT, bool BF16IN, bool BANK>
 __global__ __launch_bounds__(64, 1) void lin_verify_wide_kernel(LinVerifyArgs a) {
     static_assert(NT > 4 && NT <= 8, "wide register walk is for trees of 33..64 nodes");
     __shared__ VerifySmem<NT, BF16IN> sm;
@@ -598,10 +855,12 @@ __global__ __launch_bounds__(64, 1) void lin_verify_wide_kernel(LinVerifyArgs a)
     const int CW = a.cw;
     const int ctiles = a.dv / CW;
     const int u = xcd_remap(blockIdx.x, gridDim.x);
-    UnitIn<DK, NT, BF16IN> in;
-    load_unit(in, a, u, ctiles, CW, lane);
-    if (a.pend_path_len) apply_pending<DK, NT, BF16IN>(in, sm, a, u, ctiles, CW, lane);
-    const int n = compute_unit(in, sm, a, u, ctiles, CW, lane);
+    constexpr bool STAGE = BF16IN && kStageBf16;
+    UnitIn<DK, NT, BF16IN, BANK ? kBankTiles : 4> in;
+    load_unit<DK, NT, BF16IN, STAGE>(in, sm, a, u, ctiles, CW, lane);
+    if constexpr (BANK) commit_with_bank(in, sm, a, u, ctiles, CW, lane);
+    else if (a.pend_path_len) apply_pending<DK, NT, BF16IN>(in, sm, a, u, ctiles, CW, lane);
+    const int n = compute_unit<DK, NT, BF16IN, STAGE>(in, sm, a, u, ctiles, CW, lane);
     store_unit(sm, a, u, n, ctiles, CW, lane);
 }
 
@@ -697,6 +956,17 @@ __global__ __launch_bounds__(256) void lin_commit_kernel(LinCommitArgs a, int ro
     if (t + 256 < nvec) update(s1, t + 256);
 }
 
+// A bank verify's length update, once every unit has read the old length: 0 where the verify
+// flushed (a flush was asked for, or E + L > Emax), else E + L.
+__global__ void lin_bank_len_kernel(int32_t* bank_len, const int32_t* path_len, int Lmax, int B, int Emax,
+                                    int flush) {
+    const int b = blockIdx.x * blockDim.x + threadIdx.x;
+    if (b >= B) return;
+    const int E = clampi(bank_len[b], 0, Emax);
+    const int L = clampi(path_len[b], 0, Lmax);
+    bank_len[b] = flush || L > Emax - E ? 0 : E + L;
+}
+
 // Value channels per unit: 64 (one per lane of the walk), narrowed to 32 or 16 while the
 // launch would give fewer than two units per CU.  A narrower unit still walks the whole tree
 // (the walk's instruction count does not shrink) but loads, commits and contracts a
@@ -712,18 +982,29 @@ template <int DK, int NT>
 int launch_verify_dk_nt(const LinVerifyArgs& args, bool bf16, hipStream_t stream) {
     LinVerifyArgs a = args;
     a.cw = verify_channels(a.B, a.Hv, a.dv);
+    if (a.bank_len && a.cw > 16 * kBankTiles) a.cw = 16 * kBankTiles;
     const int CW = a.cw;
     const long long units = static_cast<long long>(a.B) * a.Hv * (a.dv / CW);
     if (units > 0x7fffffffLL) return set_error(TV_ERANGE, "lin_tree_verify: too many work units (%lld)", units);
     dim3 block(64);
+    dim3 grid(static_cast<unsigned>(units));
+    const bool bank = a.bank_len != nullptr;
     if constexpr (NT <= 4) {
-        dim3 grid(static_cast<unsigned>(units));
-        if (bf16) hipLaunchKernelGGL((lin_verify_kernel<DK, NT, true>), grid, block, 0, stream, a);
-        else hipLaunchKernelGGL((lin_verify_kernel<DK, NT, false>), grid, block, 0, stream, a);
+        if (bank) {
+            if (bf16) hipLaunchKernelGGL((lin_verify_kernel<DK, NT, true, true>), grid, block, 0, stream, a);
+            else hipLaunchKernelGGL((lin_verify_kernel<DK, NT, false, true>), grid, block, 0, stream, a);
+        } else {
+            if (bf16) hipLaunchKernelGGL((lin_verify_kernel<DK, NT, true, false>), grid, block, 0, stream, a);
+            else hipLaunchKernelGGL((lin_verify_kernel<DK, NT, false, false>), grid, block, 0, stream, a);
+        }
     } else {
-        dim3 grid(static_cast<unsigned>(units));
-        if (bf16) hipLaunchKernelGGL((lin_verify_wide_kernel<DK, NT, true>), grid, block, 0, stream, a);
-        else hipLaunchKernelGGL((lin_verify_wide_kernel<DK, NT, false>), grid, block, 0, stream, a);
+        if (bank) {
+            if (bf16) hipLaunchKernelGGL((lin_verify_wide_kernel<DK, NT, true, true>), grid, block, 0, stream, a);
+            else hipLaunchKernelGGL((lin_verify_wide_kernel<DK, NT, false, true>), grid, block, 0, stream, a);
+        } else {
+            if (bf16) hipLaunchKernelGGL((lin_verify_wide_kernel<DK, NT, true, false>), grid, block, 0, stream, a);
+            else hipLaunchKernelGGL((lin_verify_wide_kernel<DK, NT, false, false>), grid, block, 0, stream, a);
+        }
     }
     return launch_status("lin_tree_verify");
 }
@@ -749,6 +1030,13 @@ int launch_lin_verify(const LinVerifyArgs& a, bool bf16, hipStream_t stream) {
         case 128: return launch_verify_dk<128>(a, bf16, stream);
         default: return set_error(TV_EUNSUPPORTED, "lin_tree_verify: dk=%d not built (16, 32, 64, 128)", a.dk);
     }
+}
+
+int launch_lin_bank_len(int32_t* bank_len, const int32_t* path_len, int Lmax, int B, int Emax, int flush,
+                        hipStream_t stream) {
+    hipLaunchKernelGGL(lin_bank_len_kernel, dim3((B + 255) / 256), dim3(256), 0, stream, bank_len, path_len, Lmax, B,
+                       Emax, flush);
+    return launch_status("lin_tree_verify_bank");
 }
 
 int launch_lin_commit(const LinCommitArgs& a, bool bf16, hipStream_t stream) {

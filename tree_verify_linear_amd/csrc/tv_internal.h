@@ -39,6 +39,16 @@ struct LinVerifyArgs {
     const float* pend_delta;
     float* state_out;                 // == state when a commit is pending
     int cw;                           // value channels per work unit (set by the launcher)
+    // A pending bank (earlier steps' accepted entries, channel-major; see lin_tree_verify_bank):
+    // applied to each state tile before the pending path; the previous step's path is then
+    // appended to it, or, when it would not fit or a flush is asked for, the whole committed
+    // tile is stored and the bank emptied.
+    int bank_Emax;                    // entries per bank (a multiple of 32, at most 256)
+    const int32_t* bank_len;          // nullptr: no bank
+    void* bank_k;                     // [B][Hk][dk][Emax] of the input type
+    float* bank_g;                    // [B][Hv][Emax]
+    float* bank_delta;                // [B][Hv][dv][Emax]
+    int bank_flush;
 };
 int launch_lin_verify(const LinVerifyArgs& a, bool bf16, hipStream_t stream);
 
@@ -52,6 +62,10 @@ struct LinCommitArgs {
     float* state;
 };
 int launch_lin_commit(const LinCommitArgs& a, bool bf16, hipStream_t stream);
+
+// After a bank verify: each bank's new length (0 where the verify flushed, else E + L).
+int launch_lin_bank_len(int32_t* bank_len, const int32_t* path_len, int Lmax, int B, int Emax, int flush,
+                        hipStream_t stream);
 
 struct AttnArgs {
     int B, N, Hq, Hkv, D, Tcap, k_type, v_type, window;
@@ -138,6 +152,26 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
 }
 
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
+
+// Wait until at most N of this wave's vector memory operations (loads, stores and
+// global-to-LDS copies) are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// One direct global-to-LDS copy instruction: lane l moves the 16 bytes at its `src` to LDS
+// byte address lds + 16 l (lds is wave-uniform, passed in M0).  Written as a statement of its
+// own so that the compiler neither waits for it before unrelated LDS accesses nor assumes it
+// complete: the caller waits for it explicitly (wait_vm) before reading what it wrote.
+__device__ __forceinline__ void copy16_to_lds(const void* src, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" : : "s"(lds), "v"(src) : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)p));
+}
 #endif
 
 }  // namespace tv
