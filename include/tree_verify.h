@@ -58,7 +58,8 @@
  *   - Tree metadata lives in device memory and is not read back.  Kernels clamp every
  *     index taken from it (parent, n_nodes, path, path_len, n_past) into range, so a
  *     malformed tree or path can give wrong numbers but never an out-of-bounds access.
- *     Use tv_validate_tree / tv_validate_path on host copies to check them exactly.
+ *     Use tv_validate_tree / tv_validate_path on host copies to check them exactly, or
+ *     tv_check_metadata to check them on the device without reading them back.
  *
  * Tree representation (both layer types)
  *   parent  [B][N] int32, device.  parent[b][0] = -1 (node 0 is the root: the last
@@ -433,6 +434,24 @@ int conv_tree_verify(int B, int N, int C, int K, int dtype, int activation,
 int conv_tree_commit(int B, int N, int C, int K, int dtype, const int32_t* path,
                      const int32_t* path_len, int Lmax, const void* x, float* conv_state,
                      void* stream);
+
+/* Device-side check of the same metadata, for metadata that never leaves the device
+ * (PR #606 "CLI": inputs are validated, invalid ones reported rather than silently used).
+ * Enqueues one small kernel on `stream` and reads nothing back: status[b] (device int32
+ * [B]) receives a bit mask per sequence, 0 when the sequence passes every check that
+ * tv_validate_tree / tv_validate_path make.  path and path_len may both be NULL: then only
+ * the tree is checked and Lmax is ignored (else 1 <= Lmax <= N).  Each bit is judged on its
+ * own, with n_nodes[b] clamped to [0, N].  Every index read is clamped, so any metadata is
+ * safe to check.  B >= 1, 1 <= N <= 64. */
+#define TV_BAD_N_NODES   1   /* n_nodes[b] not in [1, N] */
+#define TV_BAD_ROOT      2   /* parent[b][0] != -1 */
+#define TV_BAD_PARENT    4   /* some parent[b][i], 0 < i < n_nodes[b], not in [0, i) */
+#define TV_BAD_PATH_LEN  8   /* path_len[b] not in [0, min(Lmax, n_nodes[b])] */
+#define TV_BAD_PATH_ROOT 16  /* path_len[b] > 0 and path[b][0] != 0 */
+#define TV_BAD_PATH_STEP 32  /* some path[b][m], 0 < m < path_len[b], is not a child of path[b][m-1] */
+int tv_check_metadata(const int32_t* parent, const int32_t* n_nodes, const int32_t* path,
+                      const int32_t* path_len, int B, int N, int Lmax, int32_t* status,
+                      void* stream);
 
 /* Host-side checks of tree metadata (host pointers).  TV_OK or TV_ETOPO / TV_EPATH /
  * TV_EINVAL / TV_ERANGE with a message naming the first offending entry. */

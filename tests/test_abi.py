@@ -107,6 +107,18 @@ def test_bank_argument_errors():
     assert fl(bank_delta=ctypes.c_void_p(4100)) == tvl.TV_EINVAL and b"aligned" in L.tv_last_error()
 
 
+def test_metadata_check_argument_errors():
+    L = tvl.lib()
+    f = _fake()
+    assert L.tv_check_metadata(None, f, None, None, 1, 8, 1, f, None) == tvl.TV_EINVAL
+    assert L.tv_check_metadata(f, f, f, None, 1, 8, 1, f, None) == tvl.TV_EINVAL      # path without path_len
+    assert b"both" in L.tv_last_error()
+    assert L.tv_check_metadata(f, f, None, None, 0, 8, 1, f, None) == tvl.TV_EINVAL
+    assert L.tv_check_metadata(f, f, None, None, 1, 65, 1, f, None) == tvl.TV_ERANGE
+    assert L.tv_check_metadata(f, f, f, f, 1, 8, 9, f, None) == tvl.TV_ERANGE        # Lmax > N
+    assert L.tv_check_metadata(f, f, f, f, 1, 8, 0, f, None) == tvl.TV_ERANGE
+
+
 def test_attention_argument_errors():
     L = tvl.lib()
     f = _fake()

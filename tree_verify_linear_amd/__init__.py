@@ -17,7 +17,7 @@ import torch
 __all__ = ["TreeVerifyError", "lib", "lib_path", "lin_tree_verify", "lin_tree_commit", "lin_tree_verify_commit",
            "LinBank", "lin_bank_empty", "lin_tree_verify_bank", "lin_bank_flush", "attn_tree_verify", "attn_tree_verify_noalloc", "attn_tree_workspace_bytes", "tree_accept_greedy",
            "tree_accept_workspace_bytes", "kv_tree_compact", "conv_tree_verify", "conv_tree_commit",
-           "validate_tree", "validate_path",
+           "validate_tree", "validate_path", "check_metadata",
            "abi_version", "KV_TYPES", "EXPORTS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -47,6 +47,7 @@ EXPORTS = {
     "kv_tree_compact": (_i, [_i, _i, _i, _i, _i, _i, _p, _p, _p, _i, _p, _p, _p]),
     "conv_tree_verify": (_i, [_i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p]),
     "conv_tree_commit": (_i, [_i, _i, _i, _i, _i, _p, _p, _i, _p, _p, _p]),
+    "tv_check_metadata": (_i, [_p, _p, _p, _p, _i, _i, _i, _p, _p]),
     "tv_validate_tree": (_i, [_p, _p, _i, _i]),
     "tv_validate_path": (_i, [_p, _p, _p, _p, _i, _i, _i]),
     "tv_last_error": (ctypes.c_char_p, []),
@@ -392,6 +393,29 @@ def conv_tree_commit(conv_state, x, path, path_len):
     _check(lib().conv_tree_commit(B, N, C, Km1 + 1, _in_dtype(x), _ptr(path), _ptr(path_len), path.shape[1],
                                   _ptr(x), _ptr(conv_state), _stream(x.device)))
     return conv_state
+
+
+META_BITS = {"n_nodes": 1, "root": 2, "parent": 4, "path_len": 8, "path_root": 16, "path_step": 32}
+
+
+def check_metadata(parent, n_nodes, path=None, path_len=None, status=None):
+    """Device-side check of tree (and path) metadata; returns an int32 ``[B]`` device tensor of
+    bit masks (``META_BITS``), 0 for a valid sequence.  Nothing is read back."""
+    B, N = parent.shape
+    _dev(parent, "parent", torch.int32); _dev(n_nodes, "n_nodes", torch.int32, (B,))
+    Lmax = 1
+    if path is not None or path_len is not None:
+        _dev(path, "path", torch.int32); _dev(path_len, "path_len", torch.int32, (B,))
+        if path.dim() != 2 or path.shape[0] != B:
+            raise ValueError(f"path has shape {tuple(path.shape)}, expected ({B}, Lmax)")
+        Lmax = path.shape[1]
+    if status is None:
+        status = torch.empty((B,), dtype=torch.int32, device=parent.device)
+    _dev(status, "status", torch.int32, (B,))
+    _check(lib().tv_check_metadata(_ptr(parent), _ptr(n_nodes), _ptr(path) if path is not None else None,
+                                   _ptr(path_len) if path_len is not None else None, B, N, Lmax, _ptr(status),
+                                   _stream(parent.device)))
+    return status
 
 
 def _host_i32(a, name):

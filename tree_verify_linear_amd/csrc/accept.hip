@@ -273,6 +273,36 @@ __global__ __launch_bounds__(256) void kv_compact_kernel(CompactArgs a) {
     }
 }
 
+// Device-side metadata check: one wave per sequence, lane = node (tree) and = path entry
+// (path); every lane's findings are OR-reduced across the wave and lane 0 writes the mask.
+// Every index read is clamped, so malformed metadata is reported, never dereferenced.
+__global__ __launch_bounds__(64) void check_metadata_kernel(const int32_t* parent, const int32_t* n_nodes,
+                                                            const int32_t* path, const int32_t* path_len, int N,
+                                                            int Lmax, int32_t* status) {
+    const int b = blockIdx.x, i = threadIdx.x;
+    const int nraw = n_nodes[b];
+    const int n = clampi(nraw, 0, N);
+    int bad = 0;
+    if (i == 0 && (nraw < 1 || nraw > N)) bad |= TV_BAD_N_NODES;
+    const int p = i < N ? parent[static_cast<size_t>(b) * N + i] : -1;
+    if (i == 0 && p != -1) bad |= TV_BAD_ROOT;
+    if (i > 0 && i < n && (p < 0 || p >= i)) bad |= TV_BAD_PARENT;
+    if (path) {
+        const int Lraw = path_len[b];
+        const int lim = Lmax < n ? Lmax : n;
+        if (i == 0 && (Lraw < 0 || Lraw > lim)) bad |= TV_BAD_PATH_LEN;
+        const int L = clampi(Lraw, 0, lim);
+        const int a = i < Lmax ? path[static_cast<size_t>(b) * Lmax + i] : 0;
+        if (i == 0 && L > 0 && a != 0) bad |= TV_BAD_PATH_ROOT;
+        const int pa = __shfl(p, clampi(a, 0, 63));          // parent of this entry's node
+        const int prev = __shfl(a, i > 0 ? i - 1 : 0);       // the entry before it
+        if (i > 0 && i < L && (a < 0 || a >= n || pa != prev)) bad |= TV_BAD_PATH_STEP;
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) bad |= __shfl_xor(bad, off);
+    if (i == 0) status[b] = bad;
+}
+
 }  // namespace
 
 int accept_chunks(int V, bool bf16) {
@@ -298,6 +328,13 @@ int launch_accept(const AcceptArgs& a, hipStream_t stream) {
                a.target, a.path, a.path_len, a.next_token};
     hipLaunchKernelGGL(accept_walk_kernel, dim3(static_cast<unsigned>(a.B)), dim3(64), 0, stream, w);
     return launch_status("tree_accept_greedy");
+}
+
+int launch_check_metadata(const int32_t* parent, const int32_t* n_nodes, const int32_t* path, const int32_t* path_len,
+                          int B, int N, int Lmax, int32_t* status, hipStream_t stream) {
+    hipLaunchKernelGGL(check_metadata_kernel, dim3(static_cast<unsigned>(B)), dim3(64), 0, stream, parent, n_nodes, path,
+                       path_len, N, Lmax, status);
+    return launch_status("tv_check_metadata");
 }
 
 int launch_kv_compact(const KvCompactArgs& a, hipStream_t stream) {

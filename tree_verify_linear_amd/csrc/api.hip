@@ -61,6 +61,19 @@ int tv_abi_version(void) { return TV_ABI_VERSION; }
 
 const char* tv_last_error(void) { return g_err; }
 
+int tv_check_metadata(const int32_t* parent, const int32_t* n_nodes, const int32_t* path, const int32_t* path_len,
+                      int B, int N, int Lmax, int32_t* status, void* stream) {
+    clear_error();
+    const char* fn = "tv_check_metadata";
+    if (!parent || !n_nodes || !status) return set_error(TV_EINVAL, "%s: null pointer argument", fn);
+    if ((path == nullptr) != (path_len == nullptr))
+        return set_error(TV_EINVAL, "%s: path and path_len must both be given or both be NULL", fn);
+    if (B <= 0 || N <= 0) return set_error(TV_EINVAL, "%s: B=%d N=%d must be positive", fn, B, N);
+    if (N > TV_MAX_NODES) return set_error(TV_ERANGE, "%s: N=%d exceeds %d tree nodes", fn, N, TV_MAX_NODES);
+    if (path && (Lmax < 1 || Lmax > N)) return set_error(TV_ERANGE, "%s: Lmax=%d not in [1, N=%d]", fn, Lmax, N);
+    return launch_check_metadata(parent, n_nodes, path, path_len, B, N, path ? Lmax : 1, status,
+                                 static_cast<hipStream_t>(stream));
+}
 int tv_validate_tree(const int32_t* parent, const int32_t* n_nodes, int B, int N) {
     clear_error();
     if (!parent || !n_nodes) return set_error(TV_EINVAL, "tv_validate_tree: null pointer");

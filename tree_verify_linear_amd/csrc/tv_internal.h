@@ -102,6 +102,9 @@ int accept_chunks(int V, bool bf16);
 size_t accept_workspace_bytes(int B, int N, int V, bool bf16);
 int launch_accept(const AcceptArgs& a, hipStream_t stream);
 
+int launch_check_metadata(const int32_t* parent, const int32_t* n_nodes, const int32_t* path, const int32_t* path_len,
+                          int B, int N, int Lmax, int32_t* status, hipStream_t stream);
+
 struct KvCompactArgs {
     int B, Hkv, Tcap, Lmax, rk, rv;
     const int32_t* n_past;
