@@ -148,6 +148,25 @@ def test_bank_head_sizes(dk, dv, dtype):
     run_bank(steps, 32, 1e-4 if dtype == "f32" else 2e-3, label=f"{dk}/{dv} {dtype}")
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_bank_decays_near_one(dtype):
+    """Decays in [0.95, 1): earlier entries keep almost their whole weight, so the committed
+    state is the sum of many terms of the size of the latest path's.  Ten steps of 128/128
+    heads through a 32-entry bank (it fills and flushes); the stored state must meet the
+    step's tolerance, which a c*delta rounded to two bf16 terms (2^-17 relative) would not
+    for fp32 inputs."""
+    import dataclasses
+    rng = np.random.default_rng(17)
+    steps = []
+    for L in ddtree_steps(420, 2, 2, 4, 128, 128, dtype, 10):
+        g = rng.uniform(0.95, 1.0, size=L.g.shape).astype(np.float32)
+        if dtype == "bf16":
+            g = (g.view(np.uint32) >> 16).astype(np.uint16)
+        steps.append(dataclasses.replace(L, g=g))
+    log = run_bank(steps, 32, 1e-4 if dtype == "f32" else 2e-3, label=f"decays near 1 {dtype}")
+    assert sum(int(f.sum()) for f in log) > 0
+
+
 def test_bank_tiled_heads_and_wide_trees():
     """Tiled head grouping, and 40-node trees (the wide verify kernel)."""
     steps = ddtree_steps(360, 2, 4, 12, 128, 128, "bf16", 5, budget=40)

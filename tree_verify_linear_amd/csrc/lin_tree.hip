@@ -56,6 +56,12 @@ __device__ __forceinline__ f32x4 mfma16x16x32(const bf16x8& a, const bf16x8& b, 
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// 16 x 16 x 4 in fp32: lane (g, l) holds A[l][g] and B[g][l]; the accumulator layout is that
+// of every 16 x 16 matrix-core tile (lane (g, l): rows 4g .. 4g+3 of column l).
+__device__ __forceinline__ f32x4 mfma16x16x4f32(float a, float b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
 __device__ __forceinline__ float readlane_f(float x, int lane) {
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), lane));
 }
@@ -71,6 +77,22 @@ __device__ __forceinline__ void split_bf16(const float4& x0, const float4& x1, b
     }
 }
 
+// 8 fp32 values -> three bf16 terms with x = hi + mid + lo + O(2^-24 |x|) (each residual is
+// exact in fp32).
+__device__ __forceinline__ void split3_bf16(const float4& x0, const float4& x1, bf16x8& hi, bf16x8& mid,
+                                            bf16x8& lo) {
+    const float v[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const __bf16 h = static_cast<__bf16>(v[e]);
+        const float r = v[e] - static_cast<float>(h);
+        const __bf16 m = static_cast<__bf16>(r);
+        hi[e] = h;
+        mid[e] = m;
+        lo[e] = static_cast<__bf16>(r - static_cast<float>(m));
+    }
+}
+
 // Contraction order shared by every MFMA operand over the keys: lane group g (lane / 16) of
 // K-step ks holds keys ks*32 + 4g .. 4g+3 (half 0) and ks*32 + 16 + 4g .. 16 + 4g + 3 (half 1)
 // of its row, zero past dk.  (Any order gives the same dot products; this one is also the
@@ -79,6 +101,19 @@ __device__ __forceinline__ void split_bf16(const float4& x0, const float4& x1, b
 template <int DK>
 __device__ __forceinline__ bool kvalid(int ks, int g4, int half) { return ks * 32 + 16 * half + 4 * g4 < DK; }
 __device__ __forceinline__ int kfirst(int ks, int g4, int half) { return ks * 32 + 16 * half + 4 * g4; }
+
+// A verify unit is one wave: its LDS accesses execute in issue order, so ordering them needs
+// only that the compiler keeps them in place and that their results have returned -- never a
+// wait for the wave's outstanding global stores (committed state tiles, bank entries), which
+// __syncthreads would add.
+__device__ __forceinline__ void wave_lds_sync() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0xC07F);             // lgkmcnt(0); vector memory not waited for
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Wait for every vector memory operation of the wave, the global-to-LDS row copies included.
+__device__ __forceinline__ void wait_all_vm() { asm volatile("s_waitcnt vmcnt(0)" : : : "memory"); }
 
 template <bool BF16IN>
 __device__ __forceinline__ float load_scalar(const void* base, size_t idx) {
@@ -112,15 +147,19 @@ template <int DK, int MTX>
 __device__ __forceinline__ void load_state_tile(float4 (&sa)[MTX][(DK + 31) / 32][2], const float* tile, int MT,
                                                 int l16, int g4) {
     constexpr int KS = (DK + 31) / 32;
+    // Every lane loads (channel tiles past the unit's width read its last one, keys past dk
+    // the tile's first piece) and selects zero: a load under a lane-dependent condition would
+    // make the compiler wait for it before the rest of the tile's loads are issued.
 #pragma unroll
     for (int mt = 0; mt < MTX; ++mt)
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
-                sa[mt][ks][h] = make_float4(0.f, 0.f, 0.f, 0.f);
-                if (mt < MT && kvalid<DK>(ks, g4, h))
-                    sa[mt][ks][h] = *reinterpret_cast<const float4*>(tile + (mt * 16 + l16) * DK + kfirst(ks, g4, h));
+                const bool ok = mt < MT && kvalid<DK>(ks, g4, h);
+                const int row = (mt < MT ? mt : MT - 1) * 16 + l16;
+                const float4 x = *reinterpret_cast<const float4*>(tile + row * DK + (kvalid<DK>(ks, g4, h) ? kfirst(ks, g4, h) : 0));
+                sa[mt][ks][h] = ok ? x : make_float4(0.f, 0.f, 0.f, 0.f);
             }
         }
 }
@@ -194,6 +233,7 @@ struct UnitIn {
     // the first four entries' key / delta segments (lane -> entry lane / 16, segment lane % 16)
     int pL, pnode;
     int bE;                                          // bank mode: entries already in the bank
+    float bg[4];                                     // bank mode: decays of entries 4 lane .. +3
     float pgv;
     float pkv[8];
     float4 pdv;
@@ -212,18 +252,34 @@ __device__ __forceinline__ void load_unit(UnitIn<DK, NT, BF16IN, MTX>& in, Verif
     // wave-uniform: read through the constant address space (a scalar load, counted apart
     // from the vector loads and stores, so nothing waits on them for it)
     in.nraw = N > 0 ? ((const __attribute__((address_space(4))) int32_t*)(a.n_nodes))[id.b] : 0;
+    // A pending path's entries first: the loads that depend on them (its decays, keys and
+    // deltas) are issued after the state tile's, and vector loads return in issue order, so
+    // the entries are back long before the tile (every lane loads; entries past Lmax unused).
+    int pentry = 0;
+    if (a.pend_path_len)
+        pentry = a.pend_path[static_cast<size_t>(id.b) * a.pend_Lmax + (lane < a.pend_Lmax ? lane : a.pend_Lmax - 1)];
+    if (a.bank_len) {                               // the bank's decays (entries 4 lane .. +3)
+        const float* gb = a.bank_g + (static_cast<size_t>(id.b) * a.Hv + id.h) * a.bank_Emax;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) in.bg[i] = gb[min(4 * lane + i, a.bank_Emax - 1)];
+    }
     in.praw = -1;
     in.graw = in.braw = 0u;
-    if (lane < N) {
-        in.praw = a.parent[static_cast<size_t>(id.b) * N + lane];
-        const size_t gi = (static_cast<size_t>(id.b) * N + lane) * a.Hv + id.h;
+    if (N > 0) {                                    // every lane loads (node clamped)
+        const int nd = lane < N ? lane : N - 1;
+        const int pr = a.parent[static_cast<size_t>(id.b) * N + nd];
+        const size_t gi = (static_cast<size_t>(id.b) * N + nd) * a.Hv + id.h;
+        uint32_t gr, br;
         if constexpr (BF16IN) {
-            in.graw = static_cast<const uint16_t*>(a.g)[gi];
-            in.braw = static_cast<const uint16_t*>(a.beta)[gi];
+            gr = static_cast<const uint16_t*>(a.g)[gi];
+            br = static_cast<const uint16_t*>(a.beta)[gi];
         } else {
-            in.graw = static_cast<const uint32_t*>(a.g)[gi];
-            in.braw = static_cast<const uint32_t*>(a.beta)[gi];
+            gr = static_cast<const uint32_t*>(a.g)[gi];
+            br = static_cast<const uint32_t*>(a.beta)[gi];
         }
+        in.praw = pr;                               // lanes >= n are masked where used
+        in.graw = gr;
+        in.braw = br;
     }
     if constexpr (STAGE) {
         static_assert(BF16IN, "staged rows are bf16");
@@ -286,15 +342,14 @@ __device__ __forceinline__ void load_unit(UnitIn<DK, NT, BF16IN, MTX>& in, Verif
     load_state_tile<DK, MTX>(in.sa, tile, CW >> 4, l16, g4);
     in.pL = 0;
     if (a.pend_path_len) {
-        // Issued last: the path entries, then (dependent on them) the decays and the first
-        // four entries' key and delta segments, so the other loads are already in flight.
+        // Issued last (the entries were loaded first): the decays and the first four entries'
+        // key and delta segments, so the other loads are already in flight.
         const int PN = a.pend_N;
         in.pL = clampi(((const __attribute__((address_space(4))) int32_t*)(a.pend_path_len))[id.b], 0, a.pend_Lmax);
-        int node = 0;
-        if (lane < a.pend_Lmax) node = clampi(a.pend_path[static_cast<size_t>(id.b) * a.pend_Lmax + lane], 0, PN - 1);
+        const int node = lane < a.pend_Lmax ? clampi(pentry, 0, PN - 1) : 0;
         in.pnode = node;
-        in.pgv = lane < a.pend_Lmax ? load_scalar<BF16IN>(a.pend_g, (static_cast<size_t>(id.b) * PN + node) * a.Hv + id.h)
-                                    : 0.f;
+        const float gv = load_scalar<BF16IN>(a.pend_g, (static_cast<size_t>(id.b) * PN + node) * a.Hv + id.h);
+        in.pgv = lane < a.pend_Lmax ? gv : 0.f;
         if constexpr (!PRELOAD) return;             // apply_pending loads every entry itself
         const int q = lane >> 4, sg = lane & 15;
         const int nq = __shfl(node, q);
@@ -344,14 +399,18 @@ __device__ __forceinline__ bf16x8 staged_operand(const float* rows, int c, int k
 
 template <int DK, int NT, bool BF16IN, bool STAGE, int MTX>
 __device__ __forceinline__ int compute_unit(const UnitIn<DK, NT, BF16IN, MTX>& in, VerifySmem<NT, BF16IN>& sm,
-                                            const LinVerifyArgs& a, int unit, int ctiles, int CW, int lane) {
+                                            const LinVerifyArgs& a, int unit, int ctiles, int CW, int lane,
+                                            bool staged_wait_done) {
     using U = UnitIn<DK, NT, BF16IN, MTX>;
     constexpr int KS = U::KS, NMAX = U::NMAX, GT = (NMAX + 15) / 16;
     const int g4 = lane >> 4, l16 = lane & 15;
     const int N = a.N;
     // staged rows: every copy of this wave has landed (also before an early exit, so that none
-    // is still writing LDS when the workgroup ends)
-    if constexpr (STAGE) asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
+    // is still writing LDS when the workgroup ends).  After a commit the wait was made before
+    // the commit's first store, so that this one does not wait for the stores too.
+    if constexpr (STAGE) {
+        if (!staged_wait_done) wait_all_vm();
+    }
     const int n = clampi(in.nraw, 0, N);
     if (n <= 0) return 0;
     const int MT = CW >> 4;
@@ -369,14 +428,19 @@ __device__ __forceinline__ int compute_unit(const UnitIn<DK, NT, BF16IN, MTX>& i
     };
     // this lane's node (lane < n): parent, decay and write strength; zero beyond the tree
     const bool real = lane < n;
-    const int pme = real && lane > 0 ? clampi(in.praw, 0, lane - 1) : -1;
+    // The node's raw parent, decay and strength pass through an empty asm statement here, so
+    // the compiler cannot hoist their first use (and so the wait for them) to right after
+    // their loads, ahead of the unit's other loads.
+    uint32_t praw = static_cast<uint32_t>(in.praw), graw = in.graw, braw = in.braw;
+    asm volatile("" : "+v"(praw), "+v"(graw), "+v"(braw));
+    const int pme = real && lane > 0 ? clampi(static_cast<int>(praw), 0, lane - 1) : -1;
     float gme = 0.f, bme = 0.f;
     if constexpr (BF16IN) {
-        gme = real ? bf16_bits_to_f32(static_cast<uint16_t>(in.graw)) : 0.f;
-        bme = real ? bf16_bits_to_f32(static_cast<uint16_t>(in.braw)) : 0.f;
+        gme = real ? bf16_bits_to_f32(static_cast<uint16_t>(graw)) : 0.f;
+        bme = real ? bf16_bits_to_f32(static_cast<uint16_t>(braw)) : 0.f;
     } else {
-        gme = real ? __uint_as_float(in.graw) : 0.f;
-        bme = real ? __uint_as_float(in.braw) : 0.f;
+        gme = real ? __uint_as_float(graw) : 0.f;
+        bme = real ? __uint_as_float(braw) : 0.f;
     }
 
     // 1. tree metadata and v rows into LDS; the key Gram matrix.
@@ -433,7 +497,7 @@ __device__ __forceinline__ int compute_unit(const UnitIn<DK, NT, BF16IN, MTX>& i
             *reinterpret_cast<float4*>(cs_at(sm, nt * 16 + l16, mt * 16 + 4 * g4)) = make_float4(acc[0], acc[1], acc[2], acc[3]);
         }
     }
-    __syncthreads();
+    wave_lds_sync();
 
     // 3. lane = node: ancestor set and the walk coefficients of node `lane`, written as rows
     //    of LDS so the walk reads four of them per broadcast load.
@@ -461,7 +525,7 @@ __device__ __forceinline__ int compute_unit(const UnitIn<DK, NT, BF16IN, MTX>& i
         sm.cb[lane] = a.scale * gme * run;
         sm.cd[lane] = cdv;
     }
-    __syncthreads();
+    wave_lds_sync();
     const int vst = STAGE ? CW : 64;                // Vs row stride (elements)
     auto v_of = [&](int i) {
         if constexpr (BF16IN) return bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(sm.Vs)[i * vst + lane]);
@@ -504,7 +568,7 @@ __device__ __forceinline__ int compute_unit(const UnitIn<DK, NT, BF16IN, MTX>& i
     for (int i = 0; i < NMAX; ++i) *cs_at(sm, i, lane) = dr[i];
 #pragma unroll
     for (int i = 0; i < NMAX; ++i) *cs_at(sm, N + i, lane) = orow[i];
-    __syncthreads();
+    wave_lds_sync();
 
     return n;
 }
@@ -530,7 +594,7 @@ __device__ __forceinline__ void store_unit(VerifySmem<NT, BF16IN>& sm, const Lin
             __builtin_nontemporal_store(f32x4{x.x, x.y, x.z, x.w}, reinterpret_cast<f32x4*>(dst));
         }
     }
-    __syncthreads();                                // LDS is reused by the next unit
+    wave_lds_sync();                                // LDS is reused by the next unit
 }
 
 // Stores the unit's state tile (held in the key order of kfirst) at its place in the state.
@@ -552,8 +616,8 @@ __device__ __forceinline__ void store_state_tile(const float4 (&sa)[MTX][(DK + 3
 // Commits the previous step's accepted path a_0 .. a_{L-1} into the unit's state tile, in
 // registers:  S <- G S + sum_l c_l k_{a_l} delta_{a_l}^T with G = prod_l g_{a_l} and
 // c_l = prod_{l' > l} g_{a_l'} (the commit's formula).  Entries are staged four at a time
-// through LDS that the unit's own computation overwrites later.  `store`: the committed tile
-// is stored.  `to_bank`: the path's entries are also written to the pending bank after its
+// through LDS that the unit's own computation overwrites later, and each group of four is
+// added by fp32 matrix instructions.  `store`: the committed tile is stored.  `to_bank`: the path's entries are also written to the pending bank after its
 // first `E0` entries -- the unit's channels of each captured delta, the decays (by the unit of
 // channel tile 0) and the keys (by the first value head that reads the key head).
 template <int DK, int NT, bool BF16IN, bool PRE = true, int MTX = 4>
@@ -578,13 +642,13 @@ __device__ __forceinline__ void apply_pending(UnitIn<DK, NT, BF16IN, MTX>& in, V
                           : nullptr;
     if (to_bank && id.ct == 0 && lane < L)
         a.bank_g[(static_cast<size_t>(id.b) * a.Hv + id.h) * Emax + E0 + lane] = in.pgv;
-    __syncthreads();
+    wave_lds_sync();
     if (lane < L) {
         float c = 1.f;
         for (int l = lane + 1; l < L; ++l) c *= sm.pg[l];
         sm.pc[lane] = c;
     }
-    __syncthreads();
+    wave_lds_sync();
     const float G = sm.pc[0] * sm.pg[0];
 #pragma unroll
     for (int mt = 0; mt < MTX; ++mt)
@@ -661,28 +725,29 @@ __device__ __forceinline__ void apply_pending(UnitIn<DK, NT, BF16IN, MTX>& in, V
             }
             *reinterpret_cast<float4*>(&sm.pd[q][s * 4]) = dv4;
         }
-        __syncthreads();
-        const int nq = L - c0 < 4 ? L - c0 : 4;      // entries in this chunk (wave-uniform)
+        wave_lds_sync();
+        // The rank-4 update on the matrix cores in fp32, the tile itself the accumulator:
+        // C[key][channel] += sum_q k_q[key] (c_q delta_q)[channel], one 16 x 16 x 4 instruction per
+        // 16-key x 16-channel piece, lane group q holding entry q (entries past L were staged as
+        // zeros).  Products and sums are fp32, as a fused multiply-add loop would give.
+        float bd[MTX];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            if (q >= nq) break;
+        for (int mt = 0; mt < MTX; ++mt) bd[mt] = sm.pd[g4][mt * 16 + l16];
 #pragma unroll
-            for (int mt = 0; mt < MTX; ++mt) {
-                const float dj = sm.pd[q][(mt * 16 + l16) & 63];
+        for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
+            for (int h = 0; h < 2; ++h) {
+                if (ks * 32 + 16 * h >= DK) continue;             // the key tile is past dk
+                const float ak = sm.pk[g4][ks * 32 + 16 * h + l16];
 #pragma unroll
-                    for (int h = 0; h < 2; ++h) {
-                        if (!kvalid<DK>(ks, g4, h)) continue;   // keys past dk stay zero
-                        const float4 kk = *reinterpret_cast<const float4*>(&sm.pk[q][kfirst(ks, g4, h)]);
-                        float4& x = sa[mt][ks][h];
-                        x.x = fmaf(dj, kk.x, x.x); x.y = fmaf(dj, kk.y, x.y);
-                        x.z = fmaf(dj, kk.z, x.z); x.w = fmaf(dj, kk.w, x.w);
-                    }
+                for (int mt = 0; mt < MTX; ++mt) {
+                    float4& t = sa[mt][ks][h];
+                    f32x4 acc = {t.x, t.y, t.z, t.w};
+                    acc = mfma16x16x4f32(ak, bd[mt], acc);
+                    t = make_float4(acc[0], acc[1], acc[2], acc[3]);
                 }
             }
-        }
-        __syncthreads();
+        wave_lds_sync();
     }
     if (store) store_state_tile<DK, MTX>(sa, a.state_out, id, a.Hv, a.dv, MT, g4, l16);
 }
@@ -693,8 +758,10 @@ __device__ __forceinline__ void apply_pending(UnitIn<DK, NT, BF16IN, MTX>& in, V
 // bank is channel-major (bank_k[b][kh][key][e], bank_delta[b][h][channel][e]), so the rank-E
 // update runs on the matrix cores with the tile itself as the accumulator: for every 16-key x
 // 16-channel piece, C[key][ch] += K^T[key][e] (c . delta)[e][ch] over 32 entries per
-// instruction (keys are the exact bf16 inputs, or fp32 split hi + lo; c_e delta_e is split into
-// bf16 hi + lo, so each term is exact to about 2^-16 relative).
+// instruction.  bf16 inputs: the keys enter exactly and c_e delta_e as bf16 hi + lo (each term
+// exact to about 2^-17 relative; the tolerance of a bf16 step is 2e-3).  fp32 inputs: keys and
+// c_e delta_e are each split into three bf16 terms and the six products above 2^-24 relative
+// are kept, so the update is as exact as fp32 arithmetic.
 template <int DK, int NT, bool BF16IN, int MTX>
 __device__ __forceinline__ void apply_bank(UnitIn<DK, NT, BF16IN, MTX>& in, VerifySmem<NT, BF16IN>& sm,
                                            const LinVerifyArgs& a, int unit, int ctiles, int CW, int lane) {
@@ -706,16 +773,11 @@ __device__ __forceinline__ void apply_bank(UnitIn<DK, NT, BF16IN, MTX>& in, Veri
     if (E == 0) return;                             // an empty bank: the tile is the stored state
     const UnitIds id = unit_ids(a, unit, ctiles, CW);
     const int g4 = lane >> 4, l16 = lane & 15, MT = CW >> 4;
-    // suffix products of the decays: lane l holds entries 4l .. 4l+3 (decay 1 past E)
-    const float* gb = a.bank_g + (static_cast<size_t>(id.b) * a.Hv + id.h) * Emax;
-    // (every lane loads, from a clamped index, and selects: no lane-dependent branch here,
-    // where the tile and the unit's inputs hold most registers)
+    // suffix products of the decays: lane l holds entries 4l .. 4l+3 (loaded with the unit's
+    // inputs from clamped indices; decay 1 past E, a select, not a lane-dependent branch)
     float gl[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const float x = gb[min(4 * lane + i, Emax - 1)];
-        gl[i] = 4 * lane + i < E ? x : 1.f;
-    }
+    for (int i = 0; i < 4; ++i) gl[i] = 4 * lane + i < E ? in.bg[i] : 1.f;
     float inc = (gl[0] * gl[1]) * (gl[2] * gl[3]);   // becomes the product over lanes >= this one
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -728,7 +790,7 @@ __device__ __forceinline__ void apply_bank(UnitIn<DK, NT, BF16IN, MTX>& in, Veri
     float* cbuf = &sm.pk[0][0];                     // free until the pending path is staged
     *reinterpret_cast<float4*>(&cbuf[4 * lane]) =
         make_float4(gl[1] * gl[2] * gl[3] * ex, gl[2] * gl[3] * ex, gl[3] * ex, ex);
-    __syncthreads();
+    wave_lds_sync();
 #pragma unroll
     for (int mt = 0; mt < MTX; ++mt)
 #pragma unroll
@@ -749,7 +811,8 @@ __device__ __forceinline__ void apply_bank(UnitIn<DK, NT, BF16IN, MTX>& in, Veri
 #pragma unroll
         for (int mp = 0; mp < MTX; mp += 2) {
             // B operands: c_e delta_e[channel] for entries ef .. ef+7 of channel mt*16 + l16
-            bf16x8 bhi[2], blo[2];
+            // (fp32 inputs: a third term, bmid, see below)
+            bf16x8 bhi[2], blo[2], bmid[2];
 #pragma unroll
             for (int m = 0; m < 2; ++m) {
                 const int mt = mp + m;
@@ -764,7 +827,8 @@ __device__ __forceinline__ void apply_bank(UnitIn<DK, NT, BF16IN, MTX>& in, Veri
                 m0.z = 2 < nv ? c0.z * d0.z : 0.f; m0.w = 3 < nv ? c0.w * d0.w : 0.f;
                 m1.x = 4 < nv ? c1.x * d1.x : 0.f; m1.y = 5 < nv ? c1.y * d1.y : 0.f;
                 m1.z = 6 < nv ? c1.z * d1.z : 0.f; m1.w = 7 < nv ? c1.w * d1.w : 0.f;
-                split_bf16(m0, m1, bhi[m], blo[m]);
+                if constexpr (BF16IN) split_bf16(m0, m1, bhi[m], blo[m]);
+                else split3_bf16(m0, m1, bhi[m], bmid[m], blo[m]);
             }
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks)
@@ -773,7 +837,7 @@ __device__ __forceinline__ void apply_bank(UnitIn<DK, NT, BF16IN, MTX>& in, Veri
                     if (ks * 32 + 16 * h >= DK) continue;     // the key tile is past dk
                     // A operand: K^T[key][ef .. ef+7] for key ks*32 + 16h + l16
                     const uint8_t* kr = kb + (static_cast<size_t>(ks * 32 + 16 * h + l16) * Emax + ef) * ESZ;
-                    bf16x8 ahi, alo;
+                    bf16x8 ahi, alo, amid;
                     if constexpr (BF16IN) {
                         const uint4 w = *reinterpret_cast<const uint4*>(kr);
                         uint32_t u[4] = {w.x, w.y, w.z, w.w};
@@ -790,21 +854,30 @@ __device__ __forceinline__ void apply_bank(UnitIn<DK, NT, BF16IN, MTX>& in, Veri
                         x0.x = 0 < nv ? x0.x : 0.f; x0.y = 1 < nv ? x0.y : 0.f; x0.z = 2 < nv ? x0.z : 0.f;
                         x0.w = 3 < nv ? x0.w : 0.f; x1.x = 4 < nv ? x1.x : 0.f; x1.y = 5 < nv ? x1.y : 0.f;
                         x1.z = 6 < nv ? x1.z : 0.f; x1.w = 7 < nv ? x1.w : 0.f;
-                        split_bf16(x0, x1, ahi, alo);
+                        split3_bf16(x0, x1, ahi, amid, alo);
                     }
 #pragma unroll
                     for (int m = 0; m < 2; ++m) {   // mt >= MT: a zero B operand, a zero tile
                         float4& t = sa[mp + m][ks][h];
                         f32x4 acc = {t.x, t.y, t.z, t.w};
+                        // smallest terms first; bf16 keys are exact, fp32 keys and every c delta
+                        // are split, and the terms kept are those above 2^-24 relative
+                        if constexpr (!BF16IN) {
+                            acc = mfma16x16x32(alo, bhi[m], acc);
+                            acc = mfma16x16x32(amid, bmid[m], acc);
+                            acc = mfma16x16x32(ahi, blo[m], acc);
+                            acc = mfma16x16x32(amid, bhi[m], acc);
+                            acc = mfma16x16x32(ahi, bmid[m], acc);
+                        } else {
+                            acc = mfma16x16x32(ahi, blo[m], acc);
+                        }
                         acc = mfma16x16x32(ahi, bhi[m], acc);
-                        acc = mfma16x16x32(ahi, blo[m], acc);
-                        if constexpr (!BF16IN) acc = mfma16x16x32(alo, bhi[m], acc);
                         t = make_float4(acc[0], acc[1], acc[2], acc[3]);
                     }
                 }
         }
     }
-    __syncthreads();                                // cbuf is read before Cs is rewritten
+    wave_lds_sync();                                // cbuf is read before Cs is rewritten
 }
 
 // Bank mode: the committed state is the stored tile, then the bank's entries, then the
@@ -839,9 +912,11 @@ __global__ __launch_bounds__(64, 2) void lin_verify_kernel(LinVerifyArgs a) {
     constexpr bool STAGE = BF16IN && kStageBf16;
     UnitIn<DK, NT, BF16IN, BANK ? kBankTiles : 4> in;
     load_unit<DK, NT, BF16IN, STAGE>(in, sm, a, u, ctiles, CW, lane);
+    const bool commits = BANK || a.pend_path_len != nullptr;
+    if (STAGE && commits) wait_all_vm();             // before the commit's stores (see compute_unit)
     if constexpr (BANK) commit_with_bank(in, sm, a, u, ctiles, CW, lane);
     else if (a.pend_path_len) apply_pending<DK, NT, BF16IN>(in, sm, a, u, ctiles, CW, lane);
-    const int n = compute_unit<DK, NT, BF16IN, STAGE>(in, sm, a, u, ctiles, CW, lane);
+    const int n = compute_unit<DK, NT, BF16IN, STAGE>(in, sm, a, u, ctiles, CW, lane, commits);
     store_unit(sm, a, u, n, ctiles, CW, lane);
 }
 
@@ -858,9 +933,11 @@ __global__ __launch_bounds__(64, 1) void lin_verify_wide_kernel(LinVerifyArgs a)
     constexpr bool STAGE = BF16IN && kStageBf16;
     UnitIn<DK, NT, BF16IN, BANK ? kBankTiles : 4> in;
     load_unit<DK, NT, BF16IN, STAGE>(in, sm, a, u, ctiles, CW, lane);
+    const bool commits = BANK || a.pend_path_len != nullptr;
+    if (STAGE && commits) wait_all_vm();             // before the commit's stores (see compute_unit)
     if constexpr (BANK) commit_with_bank(in, sm, a, u, ctiles, CW, lane);
     else if (a.pend_path_len) apply_pending<DK, NT, BF16IN>(in, sm, a, u, ctiles, CW, lane);
-    const int n = compute_unit<DK, NT, BF16IN, STAGE>(in, sm, a, u, ctiles, CW, lane);
+    const int n = compute_unit<DK, NT, BF16IN, STAGE>(in, sm, a, u, ctiles, CW, lane, commits);
     store_unit(sm, a, u, n, ctiles, CW, lane);
 }
 
