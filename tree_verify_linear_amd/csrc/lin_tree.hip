@@ -234,6 +234,11 @@ struct UnitIn {
     int pL, pnode;
     int bE;                                          // bank mode: entries already in the bank
     float bg[4];                                     // bank mode: decays of entries 4 lane .. +3
+    // bank mode, bf16 inputs: the first 32 entries' operands, loaded with the unit's inputs --
+    // key tile t's A operand (keys 16 t + l16, entries 8 g4 .. +7) and the deltas of channel
+    // 16 mt + l16, entries 8 g4 .. +7
+    uint4 bk[2 * KS];
+    float4 bd[MTX][2];
     float pgv;
     float pkv[8];
     float4 pdv;
@@ -242,7 +247,7 @@ struct UnitIn {
 // Issues every load of a unit.  No address depends on loaded data (the tree size n is
 // only applied at compute time; rows up to N are loaded), so a wave can issue the next
 // unit's loads without waiting for anything.
-template <int DK, int NT, bool BF16IN, bool STAGE, bool PRELOAD = true, int MTX = 4>
+template <int DK, int NT, bool BF16IN, bool STAGE, bool PRELOAD = true, int MTX = 4, bool BANK = false>
 __device__ __forceinline__ void load_unit(UnitIn<DK, NT, BF16IN, MTX>& in, VerifySmem<NT, BF16IN>& sm,
                                           const LinVerifyArgs& a, int unit, int ctiles, int CW, int lane) {
     using U = UnitIn<DK, NT, BF16IN, MTX>;
@@ -340,6 +345,23 @@ __device__ __forceinline__ void load_unit(UnitIn<DK, NT, BF16IN, MTX>& in, Verif
     }
     const float* tile = a.state + (static_cast<size_t>(id.b) * a.Hv + id.h) * a.dv * DK + static_cast<size_t>(id.j0) * DK;
     load_state_tile<DK, MTX>(in.sa, tile, CW >> 4, l16, g4);
+    if constexpr (BANK && BF16IN) {
+        // The bank's first 32 entries, whatever its length (entries past it are masked when
+        // applied; Emax >= 32, so every address is inside the bank).
+        const size_t Emax = static_cast<size_t>(a.bank_Emax);
+        const uint16_t* kb = static_cast<const uint16_t*>(a.bank_k) + (static_cast<size_t>(id.b) * a.Hk + id.kh) * DK * Emax;
+#pragma unroll
+        for (int t = 0; t < 2 * U::KS; ++t)
+            if (t * 16 < DK) in.bk[t] = *reinterpret_cast<const uint4*>(kb + static_cast<size_t>(t * 16 + l16) * Emax + 8 * g4);
+        const float* db = a.bank_delta + ((static_cast<size_t>(id.b) * a.Hv + id.h) * a.dv + id.j0) * Emax;
+        const int MT = CW >> 4;
+#pragma unroll
+        for (int mt = 0; mt < MTX; ++mt) {
+            const float* dr = db + static_cast<size_t>((mt < MT ? mt : MT - 1) * 16 + l16) * Emax + 8 * g4;
+            in.bd[mt][0] = *reinterpret_cast<const float4*>(dr);
+            in.bd[mt][1] = *reinterpret_cast<const float4*>(dr + 4);
+        }
+    }
     in.pL = 0;
     if (a.pend_path_len) {
         // Issued last (the entries were loaded first): the decays and the first four entries'
@@ -805,9 +827,26 @@ __device__ __forceinline__ void apply_bank(UnitIn<DK, NT, BF16IN, MTX>& in, Veri
     for (int e0 = 0; e0 < E; e0 += 32) {
         const int ef = e0 + 8 * g4;                 // first of this lane's eight entries
         const int nv = clampi(E - ef, 0, 8);        // how many of them are pending
-        // Two passes of two 16-channel pieces each (fewer live operands; the keys are re-read
-        // from the cache in the second pass).
         const float4 c0 = *reinterpret_cast<const float4*>(&cbuf[ef]), c1 = *reinterpret_cast<const float4*>(&cbuf[ef + 4]);
+        // bf16 inputs: this chunk's key and delta operands, in in.bk / in.bd -- the first chunk's
+        // were loaded with the unit's inputs, later ones are loaded here (e0 is wave-uniform: a
+        // scalar branch)
+        if constexpr (BF16IN) {
+            if (e0 > 0) {
+#pragma unroll
+                for (int t = 0; t < 2 * KS; ++t)
+                    if (t * 16 < DK)
+                        in.bk[t] = *reinterpret_cast<const uint4*>(kb + (static_cast<size_t>(t * 16 + l16) * Emax + ef) * ESZ);
+#pragma unroll
+                for (int mt = 0; mt < MTX; ++mt) {
+                    const float* dr = db + static_cast<size_t>((mt < MT ? mt : MT - 1) * 16 + l16) * Emax + ef;
+                    in.bd[mt][0] = *reinterpret_cast<const float4*>(dr);
+                    in.bd[mt][1] = *reinterpret_cast<const float4*>(dr + 4);
+                }
+            }
+        }
+        // Two passes of two 16-channel pieces each (fewer live operands; fp32 keys are
+        // re-read from the cache in the second pass).
 #pragma unroll
         for (int mp = 0; mp < MTX; mp += 2) {
             // B operands: c_e delta_e[channel] for entries ef .. ef+7 of channel mt*16 + l16
@@ -817,7 +856,15 @@ __device__ __forceinline__ void apply_bank(UnitIn<DK, NT, BF16IN, MTX>& in, Veri
             for (int m = 0; m < 2; ++m) {
                 const int mt = mp + m;
                 float4 d0 = make_float4(0.f, 0.f, 0.f, 0.f), d1 = d0;
-                if (mt < MT) {
+                if constexpr (BF16IN) {
+                    // mt >= MT: a zero B operand, a zero tile.  (A select on values: a
+                    // conditional between two float4 lvalues would select their addresses and
+                    // keep the unit's arrays out of registers.)
+                    const float4 x0 = in.bd[mt][0], x1 = in.bd[mt][1];
+                    const bool ok = mt < MT;
+                    d0 = make_float4(ok ? x0.x : 0.f, ok ? x0.y : 0.f, ok ? x0.z : 0.f, ok ? x0.w : 0.f);
+                    d1 = make_float4(ok ? x1.x : 0.f, ok ? x1.y : 0.f, ok ? x1.z : 0.f, ok ? x1.w : 0.f);
+                } else if (mt < MT) {
                     const float* dr = db + static_cast<size_t>(mt * 16 + l16) * Emax + ef;
                     d0 = *reinterpret_cast<const float4*>(dr);
                     d1 = *reinterpret_cast<const float4*>(dr + 4);
@@ -836,10 +883,9 @@ __device__ __forceinline__ void apply_bank(UnitIn<DK, NT, BF16IN, MTX>& in, Veri
                 for (int h = 0; h < 2; ++h) {
                     if (ks * 32 + 16 * h >= DK) continue;     // the key tile is past dk
                     // A operand: K^T[key][ef .. ef+7] for key ks*32 + 16h + l16
-                    const uint8_t* kr = kb + (static_cast<size_t>(ks * 32 + 16 * h + l16) * Emax + ef) * ESZ;
                     bf16x8 ahi, alo, amid;
                     if constexpr (BF16IN) {
-                        const uint4 w = *reinterpret_cast<const uint4*>(kr);
+                        const uint4 w = in.bk[2 * ks + h];
                         uint32_t u[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
                         for (int j = 0; j < 4; ++j) {
@@ -850,6 +896,7 @@ __device__ __forceinline__ void apply_bank(UnitIn<DK, NT, BF16IN, MTX>& in, Veri
                         ahi = __builtin_bit_cast(bf16x8, uv);
                         alo = bf16x8{};
                     } else {
+                        const uint8_t* kr = kb + (static_cast<size_t>(ks * 32 + 16 * h + l16) * Emax + ef) * ESZ;
                         float4 x0 = *reinterpret_cast<const float4*>(kr), x1 = *reinterpret_cast<const float4*>(kr + 16);
                         x0.x = 0 < nv ? x0.x : 0.f; x0.y = 1 < nv ? x0.y : 0.f; x0.z = 2 < nv ? x0.z : 0.f;
                         x0.w = 3 < nv ? x0.w : 0.f; x1.x = 4 < nv ? x1.x : 0.f; x1.y = 5 < nv ? x1.y : 0.f;
@@ -911,7 +958,7 @@ __global__ __launch_bounds__(64, 2) void lin_verify_kernel(LinVerifyArgs a) {
     const int u = xcd_remap(blockIdx.x, gridDim.x);
     constexpr bool STAGE = BF16IN && kStageBf16;
     UnitIn<DK, NT, BF16IN, BANK ? kBankTiles : 4> in;
-    load_unit<DK, NT, BF16IN, STAGE>(in, sm, a, u, ctiles, CW, lane);
+    load_unit<DK, NT, BF16IN, STAGE, true, BANK ? kBankTiles : 4, BANK>(in, sm, a, u, ctiles, CW, lane);
     const bool commits = BANK || a.pend_path_len != nullptr;
     if (STAGE && commits) wait_all_vm();             // before the commit's stores (see compute_unit)
     if constexpr (BANK) commit_with_bank(in, sm, a, u, ctiles, CW, lane);
@@ -932,7 +979,7 @@ __global__ __launch_bounds__(64, 1) void lin_verify_wide_kernel(LinVerifyArgs a)
     const int u = xcd_remap(blockIdx.x, gridDim.x);
     constexpr bool STAGE = BF16IN && kStageBf16;
     UnitIn<DK, NT, BF16IN, BANK ? kBankTiles : 4> in;
-    load_unit<DK, NT, BF16IN, STAGE>(in, sm, a, u, ctiles, CW, lane);
+    load_unit<DK, NT, BF16IN, STAGE, true, BANK ? kBankTiles : 4, BANK>(in, sm, a, u, ctiles, CW, lane);
     const bool commits = BANK || a.pend_path_len != nullptr;
     if (STAGE && commits) wait_all_vm();             // before the commit's stores (see compute_unit)
     if constexpr (BANK) commit_with_bank(in, sm, a, u, ctiles, CW, lane);
