@@ -944,12 +944,18 @@ __device__ __forceinline__ void commit_with_bank(UnitIn<DK, NT, BF16IN, MTX>& in
         store_state_tile<DK, MTX>(in.sa, a.state_out, id, a.Hv, a.dv, CW >> 4, lane >> 4, lane & 15);
 }
 
+// Waves per SIMD the verify kernel is compiled for: two, except for fp32 inputs with trees of
+// 25..32 nodes, whose k/q operands (bf16 hi + lo, held in registers: fp32 rows are not staged)
+// and 32 KiB of LDS per unit leave room for one.
+template <int NT, bool BF16IN>
+constexpr int verify_waves_per_simd() { return (!BF16IN && NT == 4) ? 1 : 2; }
+
 // Verify for trees of up to 32 nodes: one unit per workgroup of one wave.  The hardware
-// dispatcher keeps several units resident per CU (registers allow two waves per SIMD, the
-// LDS footprint seven workgroups per CU), so one unit's memory latency hides behind
-// another's arithmetic.
+// dispatcher keeps several units resident per CU (bf16 inputs: registers allow two waves per
+// SIMD, the LDS footprint eight workgroups per CU up to 24 nodes), so one unit's memory
+// latency hides behind another's arithmetic.
 template <int DK, int NT, bool BF16IN, bool BANK>
-__global__ __launch_bounds__(64, 2) void lin_verify_kernel(LinVerifyArgs a) {
+__global__ __launch_bounds__(64, (verify_waves_per_simd<NT, BF16IN>())) void lin_verify_kernel(LinVerifyArgs a) {
     static_assert(NT <= 4, "register walk is for trees of up to 32 nodes");
     __shared__ VerifySmem<NT, BF16IN> sm;
     const int lane = threadIdx.x;
