@@ -247,7 +247,8 @@ struct UnitIn {
 // Issues every load of a unit.  No address depends on loaded data (the tree size n is
 // only applied at compute time; rows up to N are loaded), so a wave can issue the next
 // unit's loads without waiting for anything.
-template <int DK, int NT, bool BF16IN, bool STAGE, bool PRELOAD = true, int MTX = 4, bool BANK = false>
+template <int DK, int NT, bool BF16IN, bool STAGE, bool PRELOAD = true, int MTX = 4, bool BANK = false,
+          bool PEND = true>
 __device__ __forceinline__ void load_unit(UnitIn<DK, NT, BF16IN, MTX>& in, VerifySmem<NT, BF16IN>& sm,
                                           const LinVerifyArgs& a, int unit, int ctiles, int CW, int lane) {
     using U = UnitIn<DK, NT, BF16IN, MTX>;
@@ -261,9 +262,9 @@ __device__ __forceinline__ void load_unit(UnitIn<DK, NT, BF16IN, MTX>& in, Verif
     // deltas) are issued after the state tile's, and vector loads return in issue order, so
     // the entries are back long before the tile (every lane loads; entries past Lmax unused).
     int pentry = 0;
-    if (a.pend_path_len)
+    if (PEND && a.pend_path_len)
         pentry = a.pend_path[static_cast<size_t>(id.b) * a.pend_Lmax + (lane < a.pend_Lmax ? lane : a.pend_Lmax - 1)];
-    if (a.bank_len) {                               // the bank's decays (entries 4 lane .. +3)
+    if (BANK && a.bank_len) {                       // the bank's decays (entries 4 lane .. +3)
         const float* gb = a.bank_g + (static_cast<size_t>(id.b) * a.Hv + id.h) * a.bank_Emax;
 #pragma unroll
         for (int i = 0; i < 4; ++i) in.bg[i] = gb[min(4 * lane + i, a.bank_Emax - 1)];
@@ -363,7 +364,7 @@ __device__ __forceinline__ void load_unit(UnitIn<DK, NT, BF16IN, MTX>& in, Verif
         }
     }
     in.pL = 0;
-    if (a.pend_path_len) {
+    if (PEND && a.pend_path_len) {
         // Issued last (the entries were loaded first): the decays and the first four entries'
         // key and delta segments, so the other loads are already in flight.
         const int PN = a.pend_N;
@@ -954,7 +955,10 @@ constexpr int verify_waves_per_simd() { return (!BF16IN && NT == 4) ? 1 : 2; }
 // dispatcher keeps several units resident per CU (bf16 inputs: registers allow two waves per
 // SIMD, the LDS footprint eight workgroups per CU up to 24 nodes), so one unit's memory
 // latency hides behind another's arithmetic.
-template <int DK, int NT, bool BF16IN, bool BANK>
+// BANK: the pending-bank call; COMMIT: the fused call (the previous step's path committed
+// first); neither: the plain verify.  Separate instantiations, so that the plain verify's
+// registers are not allocated for the commit's.
+template <int DK, int NT, bool BF16IN, bool BANK, bool COMMIT>
 __global__ __launch_bounds__(64, (verify_waves_per_simd<NT, BF16IN>())) void lin_verify_kernel(LinVerifyArgs a) {
     static_assert(NT <= 4, "register walk is for trees of up to 32 nodes");
     __shared__ VerifySmem<NT, BF16IN> sm;
@@ -964,18 +968,18 @@ __global__ __launch_bounds__(64, (verify_waves_per_simd<NT, BF16IN>())) void lin
     const int u = xcd_remap(blockIdx.x, gridDim.x);
     constexpr bool STAGE = BF16IN && kStageBf16;
     UnitIn<DK, NT, BF16IN, BANK ? kBankTiles : 4> in;
-    load_unit<DK, NT, BF16IN, STAGE, true, BANK ? kBankTiles : 4, BANK>(in, sm, a, u, ctiles, CW, lane);
-    const bool commits = BANK || a.pend_path_len != nullptr;
+    load_unit<DK, NT, BF16IN, STAGE, true, BANK ? kBankTiles : 4, BANK, BANK || COMMIT>(in, sm, a, u, ctiles, CW, lane);
+    constexpr bool commits = BANK || COMMIT;
     if (STAGE && commits) wait_all_vm();             // before the commit's stores (see compute_unit)
     if constexpr (BANK) commit_with_bank(in, sm, a, u, ctiles, CW, lane);
-    else if (a.pend_path_len) apply_pending<DK, NT, BF16IN>(in, sm, a, u, ctiles, CW, lane);
+    else if constexpr (COMMIT) apply_pending<DK, NT, BF16IN>(in, sm, a, u, ctiles, CW, lane);
     const int n = compute_unit<DK, NT, BF16IN, STAGE>(in, sm, a, u, ctiles, CW, lane, commits);
     store_unit(sm, a, u, n, ctiles, CW, lane);
 }
 
 // Verify for trees of 33..64 nodes: the same unit, with up to 512 registers per lane (one
 // wave per SIMD per workgroup slot) for the wider operand set and the longer register walk.
-template <int DK, int NT, bool BF16IN, bool BANK>
+template <int DK, int NT, bool BF16IN, bool BANK, bool COMMIT>
 __global__ __launch_bounds__(64, 1) void lin_verify_wide_kernel(LinVerifyArgs a) {
     static_assert(NT > 4 && NT <= 8, "wide register walk is for trees of 33..64 nodes");
     __shared__ VerifySmem<NT, BF16IN> sm;
@@ -985,11 +989,11 @@ __global__ __launch_bounds__(64, 1) void lin_verify_wide_kernel(LinVerifyArgs a)
     const int u = xcd_remap(blockIdx.x, gridDim.x);
     constexpr bool STAGE = BF16IN && kStageBf16;
     UnitIn<DK, NT, BF16IN, BANK ? kBankTiles : 4> in;
-    load_unit<DK, NT, BF16IN, STAGE, true, BANK ? kBankTiles : 4, BANK>(in, sm, a, u, ctiles, CW, lane);
-    const bool commits = BANK || a.pend_path_len != nullptr;
+    load_unit<DK, NT, BF16IN, STAGE, true, BANK ? kBankTiles : 4, BANK, BANK || COMMIT>(in, sm, a, u, ctiles, CW, lane);
+    constexpr bool commits = BANK || COMMIT;
     if (STAGE && commits) wait_all_vm();             // before the commit's stores (see compute_unit)
     if constexpr (BANK) commit_with_bank(in, sm, a, u, ctiles, CW, lane);
-    else if (a.pend_path_len) apply_pending<DK, NT, BF16IN>(in, sm, a, u, ctiles, CW, lane);
+    else if constexpr (COMMIT) apply_pending<DK, NT, BF16IN>(in, sm, a, u, ctiles, CW, lane);
     const int n = compute_unit<DK, NT, BF16IN, STAGE>(in, sm, a, u, ctiles, CW, lane, commits);
     store_unit(sm, a, u, n, ctiles, CW, lane);
 }
@@ -1119,21 +1123,28 @@ int launch_verify_dk_nt(const LinVerifyArgs& args, bool bf16, hipStream_t stream
     dim3 block(64);
     dim3 grid(static_cast<unsigned>(units));
     const bool bank = a.bank_len != nullptr;
+    const bool commit = a.pend_path_len != nullptr;
     if constexpr (NT <= 4) {
         if (bank) {
-            if (bf16) hipLaunchKernelGGL((lin_verify_kernel<DK, NT, true, true>), grid, block, 0, stream, a);
-            else hipLaunchKernelGGL((lin_verify_kernel<DK, NT, false, true>), grid, block, 0, stream, a);
+            if (bf16) hipLaunchKernelGGL((lin_verify_kernel<DK, NT, true, true, true>), grid, block, 0, stream, a);
+            else hipLaunchKernelGGL((lin_verify_kernel<DK, NT, false, true, true>), grid, block, 0, stream, a);
+        } else if (commit) {
+            if (bf16) hipLaunchKernelGGL((lin_verify_kernel<DK, NT, true, false, true>), grid, block, 0, stream, a);
+            else hipLaunchKernelGGL((lin_verify_kernel<DK, NT, false, false, true>), grid, block, 0, stream, a);
         } else {
-            if (bf16) hipLaunchKernelGGL((lin_verify_kernel<DK, NT, true, false>), grid, block, 0, stream, a);
-            else hipLaunchKernelGGL((lin_verify_kernel<DK, NT, false, false>), grid, block, 0, stream, a);
+            if (bf16) hipLaunchKernelGGL((lin_verify_kernel<DK, NT, true, false, false>), grid, block, 0, stream, a);
+            else hipLaunchKernelGGL((lin_verify_kernel<DK, NT, false, false, false>), grid, block, 0, stream, a);
         }
     } else {
         if (bank) {
-            if (bf16) hipLaunchKernelGGL((lin_verify_wide_kernel<DK, NT, true, true>), grid, block, 0, stream, a);
-            else hipLaunchKernelGGL((lin_verify_wide_kernel<DK, NT, false, true>), grid, block, 0, stream, a);
+            if (bf16) hipLaunchKernelGGL((lin_verify_wide_kernel<DK, NT, true, true, true>), grid, block, 0, stream, a);
+            else hipLaunchKernelGGL((lin_verify_wide_kernel<DK, NT, false, true, true>), grid, block, 0, stream, a);
+        } else if (commit) {
+            if (bf16) hipLaunchKernelGGL((lin_verify_wide_kernel<DK, NT, true, false, true>), grid, block, 0, stream, a);
+            else hipLaunchKernelGGL((lin_verify_wide_kernel<DK, NT, false, false, true>), grid, block, 0, stream, a);
         } else {
-            if (bf16) hipLaunchKernelGGL((lin_verify_wide_kernel<DK, NT, true, false>), grid, block, 0, stream, a);
-            else hipLaunchKernelGGL((lin_verify_wide_kernel<DK, NT, false, false>), grid, block, 0, stream, a);
+            if (bf16) hipLaunchKernelGGL((lin_verify_wide_kernel<DK, NT, true, false, false>), grid, block, 0, stream, a);
+            else hipLaunchKernelGGL((lin_verify_wide_kernel<DK, NT, false, false, false>), grid, block, 0, stream, a);
         }
     }
     return launch_status("lin_tree_verify");
