@@ -173,6 +173,12 @@ def test_bank_tiled_heads_and_wide_trees():
     run_bank(steps, 32, 2e-3, head_group="tiled", label="tiled 40")
 
 
+def test_bank_wide_trees_f32():
+    """fp32 inputs with 40-node trees: the wide kernel's fp32 bank instantiation."""
+    steps = ddtree_steps(365, 2, 2, 4, 128, 128, "f32", 4, budget=40)
+    run_bank(steps, 32, 1e-4, label="40 f32")
+
+
 def test_bank_batched_step_shape():
     """The batched step: 64 sequences, 22-node trees, 16/48 heads of 128, bf16; five steps
     through a 32-entry bank and a final flush.  Eight sequences (first, last and six between)

@@ -135,6 +135,12 @@ def test_fused_tree_sizes_differ_and_empty_paths():
     check(L1, L2, 2e-3, "8 -> 40")
 
 
+def test_fused_wide_trees_f32():
+    """fp32 inputs with 40-node trees in both steps: the fused call runs in the wide kernel's
+    fp32 instantiation (k/q operands in registers, one wave per SIMD)."""
+    check(*two_steps(2, 4, 128, 128, "f32", B=2, budgets=(40, 40), cfg=170), 1e-4, "40 -> 40 f32")
+
+
 @pytest.mark.parametrize("dk,dv,dtype", [(16, 16, "f32"), (32, 64, "bf16"), (64, 32, "f32"), (128, 128, "f32")])
 def test_fused_head_sizes(dk, dv, dtype):
     check(*two_steps(2, 4, dk, dv, dtype, B=2, cfg=140 + dk + dv), 1e-4 if dtype == "f32" else 2e-3, f"{dk}/{dv} {dtype}")

@@ -143,13 +143,16 @@ __device__ __forceinline__ void load_row_operand(const void* row, int ks, int g4
 }
 
 // A unit's S0 tile (MT x 16 value channels x dk) in MFMA A-operand order.
+// 16 zero bytes in global memory: the source of loads that fall outside a unit's tile.
+__device__ __align__(16) const float kZeros[4] = {0.f, 0.f, 0.f, 0.f};
+
 template <int DK, int MTX>
 __device__ __forceinline__ void load_state_tile(float4 (&sa)[MTX][(DK + 31) / 32][2], const float* tile, int MT,
                                                 int l16, int g4) {
     constexpr int KS = (DK + 31) / 32;
-    // Every lane loads (channel tiles past the unit's width read its last one, keys past dk
-    // the tile's first piece) and selects zero: a load under a lane-dependent condition would
-    // make the compiler wait for it before the rest of the tile's loads are issued.
+    // Every lane loads: pieces past the unit's width or past dk read 16 zero bytes instead (a
+    // select of the address, not of the loaded value, which the compiler may turn back into a
+    // load under a lane-dependent branch, making the wave wait for each load in turn).
 #pragma unroll
     for (int mt = 0; mt < MTX; ++mt)
 #pragma unroll
@@ -157,9 +160,8 @@ __device__ __forceinline__ void load_state_tile(float4 (&sa)[MTX][(DK + 31) / 32
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 const bool ok = mt < MT && kvalid<DK>(ks, g4, h);
-                const int row = (mt < MT ? mt : MT - 1) * 16 + l16;
-                const float4 x = *reinterpret_cast<const float4*>(tile + row * DK + (kvalid<DK>(ks, g4, h) ? kfirst(ks, g4, h) : 0));
-                sa[mt][ks][h] = ok ? x : make_float4(0.f, 0.f, 0.f, 0.f);
+                const float* src = ok ? tile + (mt * 16 + l16) * DK + kfirst(ks, g4, h) : kZeros;
+                sa[mt][ks][h] = *reinterpret_cast<const float4*>(src);
             }
         }
 }
@@ -420,7 +422,10 @@ __device__ __forceinline__ bf16x8 staged_operand(const float* rows, int c, int k
     return __builtin_bit_cast(bf16x8, u);
 }
 
-template <int DK, int NT, bool BF16IN, bool STAGE, int MTX>
+// EARLY (a plain verify, whose state tile's loads were the unit's last): the walk
+// coefficients, which need only the tree and the k/q rows, are built before the state
+// contraction, while the tile is still arriving; the wave waits for the staged rows only.
+template <int DK, int NT, bool BF16IN, bool STAGE, bool EARLY, int MTX>
 __device__ __forceinline__ int compute_unit(const UnitIn<DK, NT, BF16IN, MTX>& in, VerifySmem<NT, BF16IN>& sm,
                                             const LinVerifyArgs& a, int unit, int ctiles, int CW, int lane,
                                             bool staged_wait_done) {
@@ -430,12 +435,17 @@ __device__ __forceinline__ int compute_unit(const UnitIn<DK, NT, BF16IN, MTX>& i
     const int N = a.N;
     // staged rows: every copy of this wave has landed (also before an early exit, so that none
     // is still writing LDS when the workgroup ends).  After a commit the wait was made before
-    // the commit's first store, so that this one does not wait for the stores too.
+    // the commit's first store, so that this one does not wait for the stores too.  EARLY:
+    // the state tile's MTX * KS * 2 loads, issued after the copies, may still be in flight.
     if constexpr (STAGE) {
-        if (!staged_wait_done) wait_all_vm();
+        if constexpr (EARLY) wait_vm<MTX * KS * 2>();
+        else if (!staged_wait_done) wait_all_vm();
     }
     const int n = clampi(in.nraw, 0, N);
-    if (n <= 0) return 0;
+    if (n <= 0) {
+        if constexpr (EARLY) wait_all_vm();         // nothing left in flight when the wave ends
+        return 0;
+    }
     const int MT = CW >> 4;
     // the B operands: from the staged LDS rows, or loaded into registers with the unit's inputs
     bf16x8 opnd[STAGE ? NT : 1][KS];
@@ -501,6 +511,42 @@ __device__ __forceinline__ int compute_unit(const UnitIn<DK, NT, BF16IN, MTX>& i
         }
     }
 
+    // 3. lane = node: ancestor set and the walk coefficients of node `lane`, written as rows
+    //    of LDS so the walk reads four of them per broadcast load (after the Gram matrix;
+    //    before the contraction when EARLY).
+    auto coefficients = [&]() {
+        if (lane < NMAX) {
+            uint64_t am = 0;
+            for (int m = pme; m >= 0; m = __float_as_int(sm.Gm[m][GC + 1])) am |= 1ull << m;
+            const int li = real ? lane : 0;
+            const float cdv = a.scale * sm.Gm[li][N + li];   // before the rows below replace Gm
+            float run = 1.f;                            // product of g over ancestors below m
+            float pu[NMAX], pw[NMAX];
+#pragma unroll
+            for (int m = NMAX - 1; m >= 0; --m) {
+                const bool an = (am >> m) & 1ull;
+                pu[m] = an ? -bme * gme * run * sm.Gm[m][li] : 0.f;
+                pw[m] = an ? a.scale * gme * run * sm.Gm[m][N + li] : 0.f;
+                run = an ? run * sm.Gm[m < n ? m : 0][GC] : run;
+            }
+#pragma unroll
+            for (int m = 0; m < NMAX; m += 4) {
+                *reinterpret_cast<float4*>(&sm.Pu[lane][m]) = make_float4(pu[m], pu[m + 1], pu[m + 2], pu[m + 3]);
+                *reinterpret_cast<float4*>(&sm.Pw[lane][m]) = make_float4(pw[m], pw[m + 1], pw[m + 2], pw[m + 3]);
+            }
+            sm.cv[lane] = bme;                          // run is now G_parent
+            sm.ca[lane] = bme * gme * run;
+            sm.cb[lane] = a.scale * gme * run;
+            sm.cd[lane] = cdv;
+        }
+        wave_lds_sync();
+    };
+
+    if constexpr (EARLY) {
+        wave_lds_sync();                            // the Gram rows are in LDS
+        coefficients();
+    }
+
     // 2. S0^T x_c for the unit's channels.
 #pragma unroll
     for (int mt = 0; mt < MTX; ++mt) {
@@ -522,33 +568,7 @@ __device__ __forceinline__ int compute_unit(const UnitIn<DK, NT, BF16IN, MTX>& i
     }
     wave_lds_sync();
 
-    // 3. lane = node: ancestor set and the walk coefficients of node `lane`, written as rows
-    //    of LDS so the walk reads four of them per broadcast load.
-    if (lane < NMAX) {
-        uint64_t am = 0;
-        for (int m = pme; m >= 0; m = __float_as_int(sm.Gm[m][GC + 1])) am |= 1ull << m;
-        const int li = real ? lane : 0;
-        const float cdv = a.scale * sm.Gm[li][N + li];   // before the rows below replace Gm
-        float run = 1.f;                            // product of g over ancestors below m
-        float pu[NMAX], pw[NMAX];
-#pragma unroll
-        for (int m = NMAX - 1; m >= 0; --m) {
-            const bool an = (am >> m) & 1ull;
-            pu[m] = an ? -bme * gme * run * sm.Gm[m][li] : 0.f;
-            pw[m] = an ? a.scale * gme * run * sm.Gm[m][N + li] : 0.f;
-            run = an ? run * sm.Gm[m < n ? m : 0][GC] : run;
-        }
-#pragma unroll
-        for (int m = 0; m < NMAX; m += 4) {
-            *reinterpret_cast<float4*>(&sm.Pu[lane][m]) = make_float4(pu[m], pu[m + 1], pu[m + 2], pu[m + 3]);
-            *reinterpret_cast<float4*>(&sm.Pw[lane][m]) = make_float4(pw[m], pw[m + 1], pw[m + 2], pw[m + 3]);
-        }
-        sm.cv[lane] = bme;                          // run is now G_parent
-        sm.ca[lane] = bme * gme * run;
-        sm.cb[lane] = a.scale * gme * run;
-        sm.cd[lane] = cdv;
-    }
-    wave_lds_sync();
+    if constexpr (!EARLY) coefficients();
     const int vst = STAGE ? CW : 64;                // Vs row stride (elements)
     auto v_of = [&](int i) {
         if constexpr (BF16IN) return bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(sm.Vs)[i * vst + lane]);
@@ -973,7 +993,7 @@ __global__ __launch_bounds__(64, (verify_waves_per_simd<NT, BF16IN>())) void lin
     if (STAGE && commits) wait_all_vm();             // before the commit's stores (see compute_unit)
     if constexpr (BANK) commit_with_bank(in, sm, a, u, ctiles, CW, lane);
     else if constexpr (COMMIT) apply_pending<DK, NT, BF16IN>(in, sm, a, u, ctiles, CW, lane);
-    const int n = compute_unit<DK, NT, BF16IN, STAGE>(in, sm, a, u, ctiles, CW, lane, commits);
+    const int n = compute_unit<DK, NT, BF16IN, STAGE, !commits>(in, sm, a, u, ctiles, CW, lane, commits);
     store_unit(sm, a, u, n, ctiles, CW, lane);
 }
 
@@ -994,7 +1014,7 @@ __global__ __launch_bounds__(64, 1) void lin_verify_wide_kernel(LinVerifyArgs a)
     if (STAGE && commits) wait_all_vm();             // before the commit's stores (see compute_unit)
     if constexpr (BANK) commit_with_bank(in, sm, a, u, ctiles, CW, lane);
     else if constexpr (COMMIT) apply_pending<DK, NT, BF16IN>(in, sm, a, u, ctiles, CW, lane);
-    const int n = compute_unit<DK, NT, BF16IN, STAGE>(in, sm, a, u, ctiles, CW, lane, commits);
+    const int n = compute_unit<DK, NT, BF16IN, STAGE, false>(in, sm, a, u, ctiles, CW, lane, commits);
     store_unit(sm, a, u, n, ctiles, CW, lane);
 }
 
