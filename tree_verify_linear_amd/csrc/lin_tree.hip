@@ -145,6 +145,8 @@ __device__ __forceinline__ void load_row_operand(const void* row, int ks, int g4
 // A unit's S0 tile (MT x 16 value channels x dk) in MFMA A-operand order.
 // 16 zero bytes in global memory: the source of loads that fall outside a unit's tile.
 __device__ __align__(16) const float kZeros[4] = {0.f, 0.f, 0.f, 0.f};
+typedef const __attribute__((address_space(1))) float gfloat;
+typedef const __attribute__((address_space(1))) f32x4 gf32x4;
 
 template <int DK, int MTX>
 __device__ __forceinline__ void load_state_tile(float4 (&sa)[MTX][(DK + 31) / 32][2], const float* tile, int MT,
@@ -159,9 +161,14 @@ __device__ __forceinline__ void load_state_tile(float4 (&sa)[MTX][(DK + 31) / 32
         for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
+                // both addresses are global memory: kept in that address space, the loads stay
+                // global loads (a generic pointer would make them flat loads, whose counts the
+                // waits below cannot rely on)
                 const bool ok = mt < MT && kvalid<DK>(ks, g4, h);
-                const float* src = ok ? tile + (mt * 16 + l16) * DK + kfirst(ks, g4, h) : kZeros;
-                sa[mt][ks][h] = *reinterpret_cast<const float4*>(src);
+                const gfloat* src = ok ? (const gfloat*)(tile + (mt * 16 + l16) * DK + kfirst(ks, g4, h))
+                                       : (const gfloat*)kZeros;
+                const f32x4 x = *(const gf32x4*)src;
+                sa[mt][ks][h] = make_float4(x[0], x[1], x[2], x[3]);
             }
         }
 }
@@ -241,9 +248,11 @@ struct UnitIn {
     // 16 mt + l16, entries 8 g4 .. +7
     uint4 bk[2 * KS];
     float4 bd[MTX][2];
-    float pgv;
-    float pkv[8];
-    float4 pdv;
+    // kept as loaded (raw input bits, converted where used): a conversion or select right at
+    // the load would make the wave wait for it, and so for everything issued before it
+    uint32_t pgraw;                                  // lane l: entry l's decay
+    uint4 pkraw[BF16IN ? 1 : 2];                     // key segment (8 bf16 or 8 fp32)
+    float4 pdv;                                      // delta segment
 };
 
 // Issues every load of a unit.  No address depends on loaded data (the tree size n is
@@ -373,34 +382,30 @@ __device__ __forceinline__ void load_unit(UnitIn<DK, NT, BF16IN, MTX>& in, Verif
         in.pL = clampi(((const __attribute__((address_space(4))) int32_t*)(a.pend_path_len))[id.b], 0, a.pend_Lmax);
         const int node = lane < a.pend_Lmax ? clampi(pentry, 0, PN - 1) : 0;
         in.pnode = node;
-        const float gv = load_scalar<BF16IN>(a.pend_g, (static_cast<size_t>(id.b) * PN + node) * a.Hv + id.h);
-        in.pgv = lane < a.pend_Lmax ? gv : 0.f;
+        const size_t gi = (static_cast<size_t>(id.b) * PN + node) * a.Hv + id.h;
+        if constexpr (BF16IN) in.pgraw = static_cast<const uint16_t*>(a.pend_g)[gi];
+        else in.pgraw = static_cast<const uint32_t*>(a.pend_g)[gi];
         if constexpr (!PRELOAD) return;             // apply_pending loads every entry itself
+        // lane -> (entry q, segment sg): 8 keys and 4 channels; segments past dk or past the
+        // unit's channels read zeros (every lane loads; the address is selected, not the value)
         const int q = lane >> 4, sg = lane & 15;
         const int nq = __shfl(node, q);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) in.pkv[e] = 0.f;
-        in.pdv = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (sg * 8 < DK) {
-            const size_t ko = ((static_cast<size_t>(id.b) * PN + nq) * a.Hk + id.kh) * DK + sg * 8;
-            if constexpr (BF16IN) {
-                const uint4 w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.pend_k) + ko);
-                const uint32_t u[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    in.pkv[2 * e] = __uint_as_float(u[e] << 16);
-                    in.pkv[2 * e + 1] = __uint_as_float(u[e] & 0xffff0000u);
-                }
-            } else {
-                const float4 x0 = *reinterpret_cast<const float4*>(static_cast<const float*>(a.pend_k) + ko);
-                const float4 x1 = *reinterpret_cast<const float4*>(static_cast<const float*>(a.pend_k) + ko + 4);
-                in.pkv[0] = x0.x; in.pkv[1] = x0.y; in.pkv[2] = x0.z; in.pkv[3] = x0.w;
-                in.pkv[4] = x1.x; in.pkv[5] = x1.y; in.pkv[6] = x1.z; in.pkv[7] = x1.w;
-            }
+        const size_t ko = ((static_cast<size_t>(id.b) * PN + nq) * a.Hk + id.kh) * DK + sg * 8;
+        const gfloat* zero = (const gfloat*)kZeros;
+        if constexpr (BF16IN) {
+            const gfloat* kp = sg * 8 < DK ? (const gfloat*)(static_cast<const uint16_t*>(a.pend_k) + ko) : zero;
+            in.pkraw[0] = __builtin_bit_cast(uint4, *(const gf32x4*)kp);
+        } else {
+            const gfloat* kp = sg * 8 < DK ? (const gfloat*)(static_cast<const float*>(a.pend_k) + ko) : zero;
+            const gfloat* kp4 = sg * 8 < DK ? kp + 4 : zero;
+            in.pkraw[0] = __builtin_bit_cast(uint4, *(const gf32x4*)kp);
+            in.pkraw[1] = __builtin_bit_cast(uint4, *(const gf32x4*)kp4);
         }
-        if (sg * 4 < CW)
-            in.pdv = *reinterpret_cast<const float4*>(
-                a.pend_delta + ((static_cast<size_t>(id.b) * PN + nq) * a.Hv + id.h) * a.dv + id.j0 + sg * 4);
+        const gfloat* dp = sg * 4 < CW ? (const gfloat*)(a.pend_delta + ((static_cast<size_t>(id.b) * PN + nq) * a.Hv + id.h) * a.dv +
+                                                         id.j0 + sg * 4)
+                                       : zero;
+        const f32x4 d = *(const gf32x4*)dp;
+        in.pdv = make_float4(d[0], d[1], d[2], d[3]);
     }
 }
 
@@ -676,7 +681,7 @@ __device__ __forceinline__ void apply_pending(UnitIn<DK, NT, BF16IN, MTX>& in, V
     const int PN = a.pend_N;
     if (lane < L) {
         sm.pn[lane] = in.pnode;
-        sm.pg[lane] = in.pgv;
+        sm.pg[lane] = BF16IN ? bf16_bits_to_f32(static_cast<uint16_t>(in.pgraw)) : __uint_as_float(in.pgraw);
     }
     // the bank's slices this unit writes (wave-uniform)
     const size_t Emax = static_cast<size_t>(a.bank_Emax);
@@ -684,7 +689,8 @@ __device__ __forceinline__ void apply_pending(UnitIn<DK, NT, BF16IN, MTX>& in, V
     float* bdel = to_bank ? a.bank_delta + ((static_cast<size_t>(id.b) * a.Hv + id.h) * a.dv + id.j0) * Emax + E0
                           : nullptr;
     if (to_bank && id.ct == 0 && lane < L)
-        a.bank_g[(static_cast<size_t>(id.b) * a.Hv + id.h) * Emax + E0 + lane] = in.pgv;
+        a.bank_g[(static_cast<size_t>(id.b) * a.Hv + id.h) * Emax + E0 + lane] =
+            BF16IN ? bf16_bits_to_f32(static_cast<uint16_t>(in.pgraw)) : __uint_as_float(in.pgraw);
     wave_lds_sync();
     if (lane < L) {
         float c = 1.f;
@@ -706,12 +712,23 @@ __device__ __forceinline__ void apply_pending(UnitIn<DK, NT, BF16IN, MTX>& in, V
             const int q = lane >> 4, s = lane & 15, l = c0 + q;
             float kv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
             float4 draw = make_float4(0.f, 0.f, 0.f, 0.f);   // delta_l, this lane's 4 channels
-            if (PRE && c0 == 0) {                   // loaded with the unit's inputs
-                if (l < L) {
+            if (PRE && c0 == 0) {                   // loaded with the unit's inputs (as raw bits)
+                const bool lv = l < L;              // entries past the path: zero (selects)
+                if constexpr (BF16IN) {
+                    const uint32_t u[4] = {in.pkraw[0].x, in.pkraw[0].y, in.pkraw[0].z, in.pkraw[0].w};
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) kv[e] = in.pkv[e];
-                    draw = in.pdv;
+                    for (int e = 0; e < 4; ++e) {
+                        kv[2 * e] = lv ? __uint_as_float(u[e] << 16) : 0.f;
+                        kv[2 * e + 1] = lv ? __uint_as_float(u[e] & 0xffff0000u) : 0.f;
+                    }
+                } else {
+                    const uint32_t u[8] = {in.pkraw[0].x, in.pkraw[0].y, in.pkraw[0].z, in.pkraw[0].w,
+                                           in.pkraw[1].x, in.pkraw[1].y, in.pkraw[1].z, in.pkraw[1].w};
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) kv[e] = lv ? __uint_as_float(u[e]) : 0.f;
                 }
+                const float4 pd = in.pdv;
+                draw = make_float4(lv ? pd.x : 0.f, lv ? pd.y : 0.f, lv ? pd.z : 0.f, lv ? pd.w : 0.f);
             } else {
                 // every lane loads (clamped to entry L - 1 and to the first key / channel
                 // segment) and then selects: no lane-dependent branch around the loads
