@@ -105,3 +105,39 @@ def test_no_spill_under_a_narrowed_exec_mask(obj):
     found = _masked_spills(dis)
     assert not found, f"{os.path.basename(obj)}: {len(found)} spill accesses under a narrowed exec mask, " \
                       f"first in {found[0][0]}: {found[0][1]}"
+
+
+def _functions(dis: str):
+    funcs, cur = {}, None
+    for line in dis.split("\n"):
+        m = _FUNC.match(line)
+        if m:
+            cur = m.group(2)
+            funcs[cur] = []
+            continue
+        m = _INST.match(line)
+        if m and cur:
+            funcs[cur].append(m.group(1).strip())
+    return funcs
+
+
+def test_plain_verify_waits_for_its_row_copies():
+    """The plain bf16 verify waits for its global-to-LDS row copies by count: its first vector
+    memory wait after the last copy leaves outstanding at most as many operations as it issued
+    after the copies (the state tile's loads), so the copies themselves have landed."""
+    obj = os.path.join(OBJDIR, "lin_tree.hip.o")
+    if not os.path.exists(obj):
+        pytest.skip("needs the built linear object")
+    checked = 0
+    for name, ins in _functions(_disassemble(obj)).items():
+        if not re.search(r"lin_verify_kernelILi\d+ELi\d+ELb1ELb0ELb0E", name):
+            continue
+        first_mfma = next(i for i, x in enumerate(ins) if x.startswith("v_mfma"))
+        copies = [i for i, x in enumerate(ins[:first_mfma]) if x.startswith("global_load_lds")]
+        assert copies, name
+        w = next(i for i in range(copies[-1], first_mfma) if re.match(r"s_waitcnt .*vmcnt\(\d+\)", ins[i]))
+        allowed = int(re.search(r"vmcnt\((\d+)\)", ins[w]).group(1))
+        after = sum(1 for x in ins[copies[-1] + 1:w] if re.match(r"(global|buffer)_load_(?!lds)", x))
+        assert after >= allowed, f"{name}: waits for vmcnt({allowed}) with only {after} loads after the copies"
+        checked += 1
+    assert checked > 0

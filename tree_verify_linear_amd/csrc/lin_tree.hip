@@ -143,6 +143,11 @@ __device__ __forceinline__ void load_row_operand(const void* row, int ks, int g4
 }
 
 // A unit's S0 tile (MT x 16 value channels x dk) in MFMA A-operand order.
+// Global loads issued by load_state_tile: one per 16-key piece inside dk (dk is a multiple of
+// 16) and channel piece.
+template <int DK, int MTX>
+constexpr int state_tile_loads() { return MTX * (DK / 16); }
+
 // 16 zero bytes in global memory: the source of loads that fall outside a unit's tile.
 __device__ __align__(16) const float kZeros[4] = {0.f, 0.f, 0.f, 0.f};
 typedef const __attribute__((address_space(1))) float gfloat;
@@ -161,6 +166,11 @@ __device__ __forceinline__ void load_state_tile(float4 (&sa)[MTX][(DK + 31) / 32
         for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
+                // a 16-key piece past dk: zero, with no load (see state_tile_loads)
+                if (ks * 32 + 16 * h >= DK) {
+                    sa[mt][ks][h] = make_float4(0.f, 0.f, 0.f, 0.f);
+                    continue;
+                }
                 // both addresses are global memory: kept in that address space, the loads stay
                 // global loads (a generic pointer would make them flat loads, whose counts the
                 // waits below cannot rely on)
@@ -441,9 +451,10 @@ __device__ __forceinline__ int compute_unit(const UnitIn<DK, NT, BF16IN, MTX>& i
     // staged rows: every copy of this wave has landed (also before an early exit, so that none
     // is still writing LDS when the workgroup ends).  After a commit the wait was made before
     // the commit's first store, so that this one does not wait for the stores too.  EARLY:
-    // the state tile's MTX * KS * 2 loads, issued after the copies, may still be in flight.
+    // the state tile's loads, issued after the copies, may still be in flight (the count is
+    // checked against the code by tests/test_codegen.py).
     if constexpr (STAGE) {
-        if constexpr (EARLY) wait_vm<MTX * KS * 2>();
+        if constexpr (EARLY) wait_vm<state_tile_loads<DK, MTX>()>();
         else if (!staged_wait_done) wait_all_vm();
     }
     const int n = clampi(in.nraw, 0, N);
