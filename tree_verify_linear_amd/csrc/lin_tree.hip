@@ -265,9 +265,9 @@ struct UnitIn {
     float4 pdv;                                      // delta segment
 };
 
-// Issues every load of a unit.  No address depends on loaded data (the tree size n is
-// only applied at compute time; rows up to N are loaded), so a wave can issue the next
-// unit's loads without waiting for anything.
+// Issues every load of a unit.  Only the previous path's operands depend on loaded data (its
+// entries, loaded first, their dependent loads last); everything else is issued without
+// waiting (the tree size n is applied at compute time; rows up to N are loaded).
 template <int DK, int NT, bool BF16IN, bool STAGE, bool PRELOAD = true, int MTX = 4, bool BANK = false,
           bool PEND = true>
 __device__ __forceinline__ void load_unit(UnitIn<DK, NT, BF16IN, MTX>& in, VerifySmem<NT, BF16IN>& sm,
