@@ -41,7 +41,7 @@ inside the ramp read up to 15% slow.  ``warmup`` in the JSON line is the request
 ``warmup_steps_run`` the number of warm-up steps actually run.  ``copy_ceiling`` is a
 device-to-device copy measured on the same GPU; every kernel also reports its fraction of it.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps 100] [--warmup 3] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -74,7 +74,7 @@ KERNEL_SOURCES = {
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--min-warmup-s", type=float, default=0.3,
                     help="keep running untimed warm-up steps until this many seconds have passed (the "
