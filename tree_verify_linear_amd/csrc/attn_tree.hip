@@ -226,9 +226,6 @@ struct RowState {
     bool on;                    // the row exists
 };
 
-// Blocks of row tile 8 whose partial scores scoring wave w (1..3) computes: [first, first+count).
-__device__ __forceinline__ int t8_first(int w) { return w == 1 ? 0 : (w == 2 ? 3 : 6); }
-__device__ __forceinline__ int t8_count(int w) { return w == 0 ? 0 : (w == 3 ? 2 : 3); }
 
 // One query row (bf16) as this lane's QK operand pieces: elements kb*32 + 8*g4 .. +7 for the 8
 // blocks.  The row is pre-scaled by 2^-e, e chosen per row so that its largest magnitude lands
@@ -418,7 +415,6 @@ __global__ __launch_bounds__(THREADS, 1) void attn_kernel(AttnLaunch L) {
         // no staging, waves 1..3 two softmax tiles, the extra matrix work and staging).
         const uint32_t qflip = a.scale < 0.f ? 0x80008000u : 0u;
         const float sl2b = fabsf(a.scale) * kLog2e;
-        const int n8 = t8_count(wl), f8 = t8_first(wl);
         f16x8 qop[2][8], q8op[3];
         RowState rs[OWNMAX];
         int rlo_max[OWNMAX];
