@@ -35,9 +35,10 @@
 //     bits, so hi = RN(d*q) and lo = d*q - hi) and accumulates
 //     O += P_hi V_hi + P_hi V_lo + P_lo V_hi (the dropped P_lo V_lo is ~2^-22 relative), one
 //     tile behind the scores.
-//   * Two phases per tile step, one wave of each role per SIMD: the scoring waves' QK^T and K
-//     conversion beside the PV waves' V dequantisation and first PV row tiles, then the
-//     softmax beside the remaining PV row tiles.
+//   * One barrier per tile step, one wave of each role per SIMD: in step k the scoring waves
+//     score tile k, run its softmax and convert K of tile k+1 while the PV waves dequantise V
+//     of tile k-1 and accumulate its PV products, so the matrix work of one role runs beside
+//     the vector work of the other without a barrier between them.
 //   * Each split writes unnormalised O, its running max and sum; a combine pass rescales and
 //     sums the splits.  With a single split the kernel normalises and writes the output.
 #include <cfloat>
@@ -69,10 +70,6 @@ constexpr int THREADS = 64 * WAVES;
 constexpr int RTMAX = 9;                     // row tiles per row block
 constexpr int OWNMAX = (RTMAX + 3) / 4;      // softmax tiles owned per scoring wave
 constexpr int ROWS_PER_BLOCK = RTMAX * 16;   // 144
-#ifndef TV_PV_EARLY
-#define TV_PV_EARLY 2
-#endif
-constexpr int PV_EARLY = TV_PV_EARLY;        // PV row tiles issued in phase 1 (the rest in phase 2)
 constexpr int MAXROW = 8 * 34;               // bytes of one slot's row (Q8_0, the larger)
 // Raw K/V tiles are copied straight from HBM into rings of LDS slots by direct global-to-LDS
 // loads (1 KiB per wave instruction), DK (K) and DV (V) tiles ahead of their first use.
@@ -83,7 +80,7 @@ constexpr int MAXROW = 8 * 34;               // bytes of one slot's row (Q8_0, t
 #define TV_DV 2
 #endif
 constexpr int DK = TV_DK, DV = TV_DV;
-constexpr int RK = DK + 2, RV = DV + 1;      // ring slots (see the schedule in attn_kernel)
+constexpr int RK = DK + 2, RV = DV + 2;      // ring slots (see the schedule in attn_kernel)
 constexpr int SLOT = (TS * MAXROW + 1023) / 1024 * 1024;   // 9 KiB: whole wave instructions
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -206,7 +203,6 @@ struct AttnLaunch {
 struct AttnSmem {
     __align__(16) f16x8 kop[2][2][8][64];                   // K integers in the QK operand layout
     __align__(16) float kd[2][8][TS];                       // K block scales [block][slot]
-    __align__(16) f32x4 spart8[3][2][64];                   // row tile 8: partial scores of waves 1..3
     __align__(16) f16x8 pbuf[2][RTMAX][64];                 // P hi in the PV operand layout
     __align__(16) f16x8 pbuf_lo[2][RTMAX][64];              // P lo = P - P hi, same layout
     __align__(16) float alpha[2][RTMAX][16];                // O rescale factor per row
@@ -271,7 +267,10 @@ __device__ __forceinline__ f16x8 qrow_op(const uint4& w, int e, uint32_t qflip) 
     return o;
 }
 
-template <int KT, int VT>
+// FULL: every row block of the launch has all RTMAX row tiles (the last one more than 128
+// rows), so the row-tile count is a constant and the tile loops have no branch between row
+// tiles: the next row tile's operand loads can then be scheduled under the current MFMAs.
+template <int KT, int VT, bool FULL>
 __global__ __launch_bounds__(THREADS, 1) void attn_kernel(AttnLaunch L) {
     using KF = Fmt<KT>;
     using VF = Fmt<VT>;
@@ -304,7 +303,7 @@ __global__ __launch_bounds__(THREADS, 1) void attn_kernel(AttnLaunch L) {
     const int s1 = s0 + L.chunk < hi_b ? s0 + L.chunk : hi_b;
     const int ntiles = s1 > s0 ? (s1 - s0 + TS - 1) / TS : 0;
     const int rowbase = rb * ROWS_PER_BLOCK;
-    const int RT = (L.rows - rowbase + 15) / 16 < RTMAX ? (L.rows - rowbase + 15) / 16 : RTMAX;
+    const int RT = FULL ? RTMAX : ((L.rows - rowbase + 15) / 16 < RTMAX ? (L.rows - rowbase + 15) / 16 : RTMAX);
     const size_t part = (static_cast<size_t>(b) * a.Hkv + kvh) * L.nsplit + split;
 
     // tree metadata (depth, ancestor sets) for this sequence
@@ -404,18 +403,16 @@ __global__ __launch_bounds__(THREADS, 1) void attn_kernel(AttnLaunch L) {
     if (!scorer) wait_k(nk0 - 2);                           // tile 1 (converted in step 0)
     lds_barrier();
 
-    // Barrier sequence, identical in both roles: two above, two per tile step k = 0..ntiles
-    // (after phase 1 and after phase 2), one before the epilogue's output writes.
+    // Barrier sequence, identical in both roles: two above, one per tile step k = 0..ntiles,
+    // one before the epilogue's output writes.
     if (scorer) {
         // ------------------------------------------------------------ scoring waves
-        // Wave w scores row tiles w and w + 4 over the whole head dimension, so no partial
-        // score leaves the wave.  Row tile 8 (present only for more than 128 rows) is the
-        // exception: waves 1..3 compute its partial scores over blocks {0,1,2}, {3,4,5}, {6,7}
-        // and wave 0 adds them up and runs its softmax (wave 0 owns three softmax tiles and
-        // no staging, waves 1..3 two softmax tiles, the extra matrix work and staging).
+        // Wave w scores row tiles w and w + 4 over the whole head dimension, and wave 0 also
+        // row tile 8 (present only for more than 128 rows), so no partial score leaves a wave
+        // and a tile's scores, softmax and P need no barrier inside the tile step.
         const uint32_t qflip = a.scale < 0.f ? 0x80008000u : 0u;
         const float sl2b = fabsf(a.scale) * kLog2e;
-        f16x8 qop[2][8], q8op[3];
+        f16x8 qop[OWNMAX][8];
         RowState rs[OWNMAX];
         int rlo_max[OWNMAX];
 #pragma unroll
@@ -427,7 +424,6 @@ __global__ __launch_bounds__(THREADS, 1) void attn_kernel(AttnLaunch L) {
             rs[j].l = 0.f;
             rs[j].sl2 = FLT_MIN;
         }
-        q8op[0] = q8op[1] = q8op[2] = f16x8{};
         auto setup_row = [&](auto jc) {
             constexpr int j = decltype(jc)::value;
             const int r = j < 2 ? wl + 4 * j : 8;
@@ -438,21 +434,8 @@ __global__ __launch_bounds__(THREADS, 1) void attn_kernel(AttnLaunch L) {
                                    ((static_cast<size_t>(b) * N + (on ? node : 0)) * a.Hq + kvh * L.G + hh) * D;
             uint4 qw[8];
             const int qe = load_qrow(qrow, on, g4, qw);
-            if constexpr (j < 2) {
 #pragma unroll
-                for (int kb = 0; kb < 8; ++kb) qop[j][kb] = qrow_op(qw[kb], qe, qflip);
-            } else {
-                // blocks {0,1,2}, {3,4,5}, {6,7} for waves 1, 2, 3 (static indices, uniform branches)
-                if (wl == 1) {
-                    q8op[0] = qrow_op(qw[0], qe, qflip); q8op[1] = qrow_op(qw[1], qe, qflip);
-                    q8op[2] = qrow_op(qw[2], qe, qflip);
-                } else if (wl == 2) {
-                    q8op[0] = qrow_op(qw[3], qe, qflip); q8op[1] = qrow_op(qw[4], qe, qflip);
-                    q8op[2] = qrow_op(qw[5], qe, qflip);
-                } else if (wl == 3) {
-                    q8op[0] = qrow_op(qw[6], qe, qflip); q8op[1] = qrow_op(qw[7], qe, qflip);
-                }
-            }
+            for (int kb = 0; kb < 8; ++kb) qop[j][kb] = qrow_op(qw[kb], qe, qflip);
             rs[j].on = on;
             rs[j].node = on ? node : 0;
             rs[j].dep = on ? sm.dep[node] : 0;
@@ -464,9 +447,7 @@ __global__ __launch_bounds__(THREADS, 1) void attn_kernel(AttnLaunch L) {
         };
         setup_row(std::integral_constant<int, 0>{});
         setup_row(std::integral_constant<int, 1>{});
-        // row tile 8 is loaded by every scoring wave (wave 0 for its softmax scale, waves 1..3
-        // for their blocks of its scores)
-        if (RT > 8) setup_row(std::integral_constant<int, 2>{});
+        if (RT > 8 && wl == 0) setup_row(std::integral_constant<int, 2>{});   // row tile 8
 #pragma unroll
         for (int j = 0; j < OWNMAX; ++j) {
             // a committed tile is unmasked for this row tile when every row sees all its slots
@@ -483,26 +464,23 @@ __global__ __launch_bounds__(THREADS, 1) void attn_kernel(AttnLaunch L) {
         const bool has8 = RT > 8;
 
         // The tile loop of one scoring wave, specialised on what the wave holds so that the
-        // inner loop has no branches: NJ own row tiles (0..2), the blocks of row tile 8 whose
-        // partial scores it computes (W8 = 1, 2, 3: blocks {0,1,2}, {3,4,5}, {6,7}; 0: none)
-        // and whether it runs row tile 8's softmax (S8, wave 0).
-        auto scoring_loop = [&](auto njc, auto w8c, auto s8c) {
+        // inner loop has no branches: NJ row tiles among w, w + 4 (0..2) and, for wave 0, row
+        // tile 8 (S8).  One barrier per tile step: scores and softmax of tile k, K conversion of
+        // tile k + 1 and the copy of V tile k + DV, then the barrier that publishes P, K and V.
+        auto scoring_loop = [&](auto njc, auto s8c) {
             constexpr int NJ = decltype(njc)::value;
-            constexpr int W8 = decltype(w8c)::value;
             constexpr bool S8 = decltype(s8c)::value;
-            constexpr int F8 = W8 == 1 ? 0 : (W8 == 2 ? 3 : 6);
-            constexpr int C8 = W8 == 0 ? 0 : (W8 == 3 ? 2 : 3);
-            constexpr int NS = NJ + (S8 ? 1 : 0);          // softmax row tiles
+            constexpr int NS = NJ + (S8 ? 1 : 0);          // row tiles scored (row tile jj < 2: w + 4 jj; 2: 8)
             f32x4 own[OWNMAX][2];
             for (int k = 0; k <= ntiles; ++k) {
-                // phase 1: scores of tile k.  Per slot half: the K integers of all 8 blocks
-                // against Q on the matrix cores (independent products, issued back to back),
-                // then each block's per-slot scale applied and summed in fp32.
-                if (k < ntiles) {
+                if (k < ntiles && NS > 0) {
+                    // scores of tile k.  Per slot half: the K integers of all 8 blocks against Q
+                    // on the matrix cores (independent products, issued back to back), then each
+                    // block's per-slot scale applied and summed in fp32.
                     const int buf = k & 1;
 #pragma unroll
                     for (int st = 0; st < 2; ++st) {
-                        f32x4 sa[NJ > 0 ? NJ : 1], s8 = {0.f, 0.f, 0.f, 0.f};
+                        f32x4 sa[NS > 0 ? NS : 1];
 #pragma unroll
                         for (int h = 0; h < 4; ++h) {                // blocks 2h, 2h+1
                             f16x8 ka[2];
@@ -513,61 +491,42 @@ __global__ __launch_bounds__(THREADS, 1) void attn_kernel(AttnLaunch L) {
                                 d4[x] = *reinterpret_cast<const f32x4*>(&sm.kd[buf][2 * h + x][16 * st + 4 * g4]);
                             }
                             const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-                            f32x4 acc[NJ > 0 ? NJ : 1][2], acc8[2];
+                            f32x4 acc[NS > 0 ? NS : 1][2];
 #pragma unroll
                             for (int x = 0; x < 2; ++x) {
 #pragma unroll
-                                for (int jj = 0; jj < NJ; ++jj) acc[jj][x] = mfma_f16(ka[x], qop[jj][2 * h + x], z);
+                                for (int jj = 0; jj < NS; ++jj)
+                                    acc[jj][x] = mfma_f16(ka[x], qop[jj][2 * h + x], z);
                             }
 #pragma unroll
-                            for (int x = 0; x < 2; ++x) {
-                                const int kb = 2 * h + x;
-                                if (kb >= F8 && kb < F8 + C8) acc8[x] = mfma_f16(ka[x], q8op[kb - F8 < 3 ? kb - F8 : 0], z);
-                            }
-#pragma unroll
-                            for (int jj = 0; jj < NJ; ++jj) {
+                            for (int jj = 0; jj < NS; ++jj) {
 #pragma unroll
                                 for (int x = 0; x < 2; ++x) {
                                     if (h == 0 && x == 0) sa[jj] = d4[0] * acc[jj][0];
                                     else sa[jj] += d4[x] * acc[jj][x];
                                 }
                             }
-#pragma unroll
-                            for (int x = 0; x < 2; ++x) {
-                                const int kb = 2 * h + x;
-                                if (kb >= F8 && kb < F8 + C8) s8 += d4[x] * acc8[x];
-                            }
                         }
 #pragma unroll
-                        for (int jj = 0; jj < NJ; ++jj) own[jj][st] = sa[jj];
-                        if constexpr (C8 > 0) sm.spart8[W8 - 1][st][lane] = s8;
+                        for (int jj = 0; jj < NS; ++jj) own[jj][st] = sa[jj];
                     }
                 }
                 // K of tile k+1 into the other operand buffer (read by the scores of step k+1)
                 if (k + 1 < ntiles) convert_k(k + 1);
-                lds_barrier();
-                // phase 2: softmax of tile k for the owned row tiles
                 if (k < ntiles && NS > 0) {
+                    // softmax of tile k, one row tile after the other (each a chain of dependent
+                    // steps; the PV wave on the same SIMD fills the gaps)
                     const int t0 = s0 + k * TS;
                     const int bufk = k & 1;
-                    if constexpr (S8) {
-#pragma unroll
-                        for (int st = 0; st < 2; ++st)
-                            own[2][st] = (sm.spart8[0][st][lane] + sm.spart8[1][st][lane]) + sm.spart8[2][st][lane];
-                    }
-                    // The owned row tiles (two, three for wave 0) go through each step together,
-                    // so their independent chains interleave.
-                    float x[NS > 0 ? NS : 1][8];        // unscaled scores
 #pragma unroll
                     for (int jj = 0; jj < NS; ++jj) {
+                        const int r = jj < 2 ? wl + 4 * jj : 8;
+                        float x[8];        // unscaled scores
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
-                            x[jj][e] = own[jj][0][e];
-                            x[jj][4 + e] = own[jj][1][e];
+                            x[e] = own[jj][0][e];
+                            x[4 + e] = own[jj][1][e];
                         }
-                    }
-#pragma unroll
-                    for (int jj = 0; jj < NS; ++jj) {
                         const bool fast = t0 + TS <= (T < s1 ? T : s1) && t0 >= rlo_max[jj];
                         if (!fast) {
 #pragma unroll
@@ -581,38 +540,24 @@ __global__ __launch_bounds__(THREADS, 1) void attn_kernel(AttnLaunch L) {
                                     vis = vis && jn < TV_MAX_NODES && ((rs[jj].anc >> (jn & 63)) & 1ull) &&
                                           (W == 0 || rs[jj].dep - sm.dep[jn & 63] < W);
                                 }
-                                x[jj][e] = vis ? x[jj][e] : -INFINITY;
+                                x[e] = vis ? x[e] : -INFINITY;
                             }
                         }
-                    }
-                    // (rows past the tree are not masked on unmasked tiles: their Q is zero, so
-                    // their weights stay finite, and nothing reads their results)
-                    float mt[NS > 0 ? NS : 1];
+                        // (rows past the tree are not masked on unmasked tiles: their Q is zero, so
+                        // their weights stay finite, and nothing reads their results)
+                        float mt = x[0];
 #pragma unroll
-                    for (int jj = 0; jj < NS; ++jj) {
-                        mt[jj] = x[jj][0];
-#pragma unroll
-                        for (int e = 1; e < 8; ++e) mt[jj] = fmaxf(mt[jj], x[jj][e]);
-                    }
-                    // the row's 32 slots sit in the four lane groups: max over l, l^16, l^32
-#pragma unroll
-                    for (int jj = 0; jj < NS; ++jj) {
-                        const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(mt[jj]), __float_as_uint(mt[jj]), false, false);
-                        mt[jj] = fmaxf(__uint_as_float(s16[0]), __uint_as_float(s16[1]));
-                    }
-#pragma unroll
-                    for (int jj = 0; jj < NS; ++jj) {
-                        const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt[jj]), __float_as_uint(mt[jj]), false, false);
-                        mt[jj] = fmaxf(__uint_as_float(s32[0]), __uint_as_float(s32[1])) * rs[jj].sl2;
-                    }
-#pragma unroll
-                    for (int jj = 0; jj < NS; ++jj) {
-                        const int r = jj < 2 ? wl + 4 * jj : 8;
+                        for (int e = 1; e < 8; ++e) mt = fmaxf(mt, x[e]);
+                        // the row's 32 slots sit in the four lane groups: max over l, l^16, l^32
+                        const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(mt), __float_as_uint(mt), false, false);
+                        mt = fmaxf(__uint_as_float(s16[0]), __uint_as_float(s16[1]));
+                        const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt), false, false);
+                        mt = fmaxf(__uint_as_float(s32[0]), __uint_as_float(s32[1])) * rs[jj].sl2;
                         // Lazy rescaling: P is taken against a reference max that moves only when
                         // the row max grows by more than 2^8 (so P <= 256); alpha is 1 otherwise.
-                        const bool grow = mt[jj] > rs[jj].m + 8.f;
+                        const bool grow = mt > rs[jj].m + 8.f;
                         const bool anyg = __builtin_amdgcn_ballot_w64(grow) != 0;
-                        const float mnew = grow ? mt[jj] : rs[jj].m;
+                        const float mnew = grow ? mt : rs[jj].m;
                         const float al = rs[jj].m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(rs[jj].m - mnew);
                         rs[jj].m = mnew;
                         const float m = mnew == -INFINITY ? 0.f : mnew;      // then every x is -inf
@@ -622,7 +567,7 @@ __global__ __launch_bounds__(THREADS, 1) void attn_kernel(AttnLaunch L) {
                         float ps = 0.f;
 #pragma unroll
                         for (int e = 0; e < 8; ++e) {
-                            pe[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[jj][e], rs[jj].sl2, -m));
+                            pe[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[e], rs[jj].sl2, -m));
                             ps += pe[e];
                         }
                         uint32_t ph[4], pl[4];
@@ -633,10 +578,12 @@ __global__ __launch_bounds__(THREADS, 1) void attn_kernel(AttnLaunch L) {
                         *reinterpret_cast<uint4*>(&sm.pbuf_lo[bufk][r][lane]) = make_uint4(pl[0], pl[1], pl[2], pl[3]);
                         if (g4 == 0) sm.alpha[bufk][r][l16] = al;          // row l16's factor
                         if (lane == 0) sm.grow[bufk][r] = anyg;
+                        __builtin_amdgcn_sched_barrier(0);
                     }
                 }
-                // copy V tile k+DV (its slot's tile k-1 was dequantised in phase 1); V tile k is
-                // dequantised in phase 1 of the next step
+                // copy V tile k+DV into the slot of tile k-2 (dequantised in step k-1; the PV
+                // waves read tile k-1's slot during this step); V tile k is dequantised in the
+                // next step
                 if (k + DV < ntiles) dma_v(k + DV);
                 wait_v(ntiles - 1 - k < DV ? ntiles - 1 - k : DV);
                 lds_barrier();
@@ -645,20 +592,16 @@ __global__ __launch_bounds__(THREADS, 1) void attn_kernel(AttnLaunch L) {
         using I0 = std::integral_constant<int, 0>;
         using I1 = std::integral_constant<int, 1>;
         using I2 = std::integral_constant<int, 2>;
-        using I3 = std::integral_constant<int, 3>;
         using BF = std::integral_constant<bool, false>;
         using BT = std::integral_constant<bool, true>;
-        if (has8) {
-            if (wl == 0) scoring_loop(I2{}, I0{}, BT{});
-            else if (wl == 1) scoring_loop(I2{}, I1{}, BF{});
-            else if (wl == 2) scoring_loop(I2{}, I2{}, BF{});
-            else scoring_loop(I2{}, I3{}, BF{});
+        if (has8 && wl == 0) {
+            scoring_loop(I2{}, BT{});
         } else if (own1) {
-            scoring_loop(I2{}, I0{}, BF{});
+            scoring_loop(I2{}, BF{});
         } else if (own0) {
-            scoring_loop(I1{}, I0{}, BF{});        // small trees: one row tile
+            scoring_loop(I1{}, BF{});              // small trees: one row tile
         } else {
-            scoring_loop(I0{}, I0{}, BF{});        // no row tile: staging and barriers only
+            scoring_loop(I0{}, BF{});              // no row tile: staging and barriers only
         }
         // epilogue: row maxima and sums for the PV waves (and the split partials)
 #pragma unroll
@@ -710,7 +653,7 @@ __global__ __launch_bounds__(THREADS, 1) void attn_kernel(AttnLaunch L) {
         using R7 = std::integral_constant<int, 7>;
         using R8 = std::integral_constant<int, 8>;
         for (int k = 0; k <= ntiles; ++k) {
-            // phase 1: this wave's 64 columns of V for tile k-1 as the PV B operands, fp16
+            // this wave's 64 columns of V for tile k-1 as the PV B operands, fp16
             // hi/lo, straight from the raw rows into registers.  Column tile jj, lane (g4, l16)
             // holds column 4*l16 + jj of the wave's 64 (four adjacent columns = one dword per
             // slot) at the slots of the P operand's lane
@@ -758,8 +701,7 @@ __global__ __launch_bounds__(THREADS, 1) void attn_kernel(AttnLaunch L) {
                         bl[c][2 * pp + 1] = l[1];
                     }
                 }
-                // O rescale for tile k-1, then its first PV_EARLY row tiles: the matrix cores
-                // are shared with the scoring waves' QK^T work in this phase
+                // O rescale for tile k-1, then O += P V for its row tiles
                 const int bufp = (k - 1) & 1;
                 int anyg = 0;
 #pragma unroll
@@ -773,15 +715,8 @@ __global__ __launch_bounds__(THREADS, 1) void attn_kernel(AttnLaunch L) {
                         for (int jj = 0; jj < 4; ++jj) oacc[r][jj] *= al;
                     }
                 }
-                if constexpr (PV_EARLY > 0) pv_rowtile(R0{}, bufp, bh, bl);
-                if constexpr (PV_EARLY > 1) pv_rowtile(R1{}, bufp, bh, bl);
-            }
-            lds_barrier();
-            // phase 2: O += P V for tile k-1
-            if (k >= 1) {
-                const int bufp = (k - 1) & 1;
-                if constexpr (PV_EARLY < 1) pv_rowtile(R0{}, bufp, bh, bl);
-                if constexpr (PV_EARLY < 2) pv_rowtile(R1{}, bufp, bh, bl);
+                pv_rowtile(R0{}, bufp, bh, bl);
+                pv_rowtile(R1{}, bufp, bh, bl);
                 pv_rowtile(R2{}, bufp, bh, bl);
                 pv_rowtile(R3{}, bufp, bh, bl);
                 pv_rowtile(R4{}, bufp, bh, bl);
@@ -790,8 +725,8 @@ __global__ __launch_bounds__(THREADS, 1) void attn_kernel(AttnLaunch L) {
                 pv_rowtile(R7{}, bufp, bh, bl);
                 pv_rowtile(R8{}, bufp, bh, bl);
             }
-            // copy K tile k+2+DK (its slot's tile k was converted in phase 1 of step k-1); K
-            // tile k+2 is converted in phase 1 of the next step
+            // copy K tile k+2+DK (its slot's tile k was converted in step k-1); K tile k+2 is
+            // converted in the next step
             if (k + 2 + DK < ntiles) dma_k(k + 2 + DK);
             wait_k(ntiles - 3 - k < DK ? ntiles - 3 - k : DK);
             lds_barrier();
@@ -927,7 +862,9 @@ size_t workspace_for(const SplitPlan& p, int B, int Hkv, int D_) {
 
 template <int KT, int VT>
 void launch_pair(const AttnLaunch& L, unsigned wgs, hipStream_t stream) {
-    hipLaunchKernelGGL((attn_kernel<KT, VT>), dim3(wgs), dim3(THREADS), 0, stream, L);
+    const bool full = L.rows - (L.rblocks - 1) * ROWS_PER_BLOCK > (RTMAX - 1) * 16;
+    if (full) hipLaunchKernelGGL((attn_kernel<KT, VT, true>), dim3(wgs), dim3(THREADS), 0, stream, L);
+    else hipLaunchKernelGGL((attn_kernel<KT, VT, false>), dim3(wgs), dim3(THREADS), 0, stream, L);
 }
 
 }  // namespace
