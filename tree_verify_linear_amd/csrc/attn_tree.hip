@@ -112,17 +112,6 @@ __device__ __forceinline__ _Float16 block_scale(const uint8_t* blk) {
 
 __device__ __forceinline__ uint32_t lds_u32(const uint8_t* p) { return *reinterpret_cast<const uint32_t*>(p); }
 
-// Four bytes at the even byte offset `o` of an LDS row, read as aligned dwords.  The integer
-// part of a block starts two bytes after its scale, so it is dword aligned in odd blocks and
-// two bytes off in even ones (34- and 18-byte blocks alike).
-template <bool ALIGNED>
-__device__ __forceinline__ uint32_t bytes4(const uint8_t* row, int o) {
-    if constexpr (ALIGNED) {
-        return lds_u32(row + o);
-    } else {
-        return __builtin_amdgcn_alignbyte(lds_u32(row + o + 2), lds_u32(row + o - 2), 2u);
-    }
-}
 // The same with the alignment known only at run time (o % 4 is 0 or 2).
 __device__ __forceinline__ uint32_t bytes4_rt(const uint8_t* row, int o) {
     const uint8_t* p = row + (o & ~3);
@@ -148,19 +137,43 @@ __device__ __forceinline__ uint32_t to_biased(uint32_t w, int nib_shift) {
 template <int TYPE>
 constexpr float ints_bias() { return TYPE == TV_Q8_0 ? 1152.f : 1032.f; }
 
-// Elements 8g .. 8g+7 of block kb of a slot row, as exact fp16 integers (the MFMA operand of
-// lane group g).  Block kb is even iff !ODD.
+// Elements 8g .. 8g+7 of block kb of a slot row (the MFMA operand of lane group g) are 8 bytes
+// (Q8_0) or the low or high nibbles of 8 bytes (Q4_0: elements 16.. are the high nibbles of
+// bytes 0..).  The integer part of a block starts two bytes after its scale, so it is dword
+// aligned in odd blocks and two bytes off in even ones (34- and 18-byte blocks alike): KRaw
+// holds the aligned dwords covering those bytes, two or three, loaded ahead of the conversion.
+template <bool ODD>
+struct KRaw {
+    uint32_t d[ODD ? 2 : 3];
+};
 template <int TYPE, bool ODD>
-__device__ __forceinline__ f16x8 block_ints8(const uint8_t* row, int kb, int g) {
-    int o, sh = 0;
-    if constexpr (TYPE == TV_Q8_0) {
-        o = 34 * kb + 2 + 8 * g;
+__device__ __forceinline__ KRaw<ODD> load_kraw(const uint8_t* row, int kb, int g) {
+    const int o = TYPE == TV_Q8_0 ? 34 * kb + 2 + 8 * g : 18 * kb + 2 + 8 * (g & 1);
+    KRaw<ODD> r;
+    if constexpr (ODD) {
+        r.d[0] = lds_u32(row + o);
+        r.d[1] = lds_u32(row + o + 4);
     } else {
-        o = 18 * kb + 2 + 8 * (g & 1);      // elements 16.. are the high nibbles of bytes 0..
-        sh = g >= 2 ? 4 : 0;
+        r.d[0] = lds_u32(row + o - 2);
+        r.d[1] = lds_u32(row + o + 2);
+        r.d[2] = lds_u32(row + o + 6);
     }
-    const uint32_t w0 = to_biased<TYPE>(bytes4<ODD>(row, o), sh);
-    const uint32_t w1 = to_biased<TYPE>(bytes4<ODD>(row, o + 4), sh);
+    return r;
+}
+// Those elements as exact fp16 integers.  Block kb is even iff !ODD.
+template <int TYPE, bool ODD>
+__device__ __forceinline__ f16x8 kraw_ints8(const KRaw<ODD>& r, int g) {
+    const int sh = TYPE == TV_Q8_0 ? 0 : (g >= 2 ? 4 : 0);
+    uint32_t a, b;
+    if constexpr (ODD) {
+        a = r.d[0];
+        b = r.d[1];
+    } else {
+        a = __builtin_amdgcn_alignbyte(r.d[1], r.d[0], 2u);
+        b = __builtin_amdgcn_alignbyte(r.d[2], r.d[1], 2u);
+    }
+    const uint32_t w0 = to_biased<TYPE>(a, sh);
+    const uint32_t w1 = to_biased<TYPE>(b, sh);
     const f16x2 bias = static_cast<_Float16>(ints_bias<TYPE>());
     const f16x2 p0 = biased_lo(w0) - bias, p1 = biased_hi(w0) - bias;
     const f16x2 p2 = biased_lo(w1) - bias, p3 = biased_hi(w1) - bias;
@@ -376,17 +389,29 @@ __global__ __launch_bounds__(THREADS, 1) void attn_kernel(AttnLaunch L) {
     // Lane (g4, l16) of slot half st holds slot 16 st + l16, elements 8 g4 .. 8 g4 + 7 of the
     // block: exactly the MFMA A operand of that (half, block), so the scoring waves read it
     // back with one conflict-free 16-byte load per lane.
+    // Every LDS read of a conversion is issued before its first write (one round trip, not one
+    // per block); lanes g4 < 2 convert the scale of block 2w + g4.
     auto convert_k = [&](int tile) {
         const int buf = tile & 1;
+        const int kbs = 2 * wl + (g4 & 1);
+        KRaw<false> re[2];
+        KRaw<true> ro[2];
+        _Float16 sc[2];
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
             const uint8_t* krow = &ringk[tile % RK][(16 * st + l16) * KF::ROW];
-            sm.kop[buf][st][2 * wl][lane] = block_ints8<KT, false>(krow, 2 * wl, g4);
-            sm.kop[buf][st][2 * wl + 1][lane] = block_ints8<KT, true>(krow, 2 * wl + 1, g4);
-            if (g4 < 2) {
-                const int kb = 2 * wl + g4;
-                sm.kd[buf][kb][16 * st + l16] = static_cast<float>(block_scale(krow + kb * KF::BLK));
-            }
+            re[st] = load_kraw<KT, false>(krow, 2 * wl, g4);
+            ro[st] = load_kraw<KT, true>(krow, 2 * wl + 1, g4);
+            sc[st] = block_scale(krow + kbs * KF::BLK);
+        }
+        // (the scales are used only by lanes g4 < 2; keep their loads with the others rather
+        // than inside the branch that writes them)
+        asm volatile("" : : "v"(sc[0]), "v"(sc[1]));
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+            sm.kop[buf][st][2 * wl][lane] = kraw_ints8<KT, false>(re[st], g4);
+            sm.kop[buf][st][2 * wl + 1][lane] = kraw_ints8<KT, true>(ro[st], g4);
+            if (g4 < 2) sm.kd[buf][kbs][16 * st + l16] = static_cast<float>(sc[st]);
         }
     };
 
@@ -514,19 +539,21 @@ __global__ __launch_bounds__(THREADS, 1) void attn_kernel(AttnLaunch L) {
                 // K of tile k+1 into the other operand buffer (read by the scores of step k+1)
                 if (k + 1 < ntiles) convert_k(k + 1);
                 if (k < ntiles && NS > 0) {
-                    // softmax of tile k, one row tile after the other (each a chain of dependent
-                    // steps; the PV wave on the same SIMD fills the gaps)
+                    // softmax of tile k for the row tiles scored (two, three for wave 0), which go
+                    // through each step together, so their independent chains interleave
                     const int t0 = s0 + k * TS;
                     const int bufk = k & 1;
+                    float x[NS > 0 ? NS : 1][8];        // unscaled scores
 #pragma unroll
                     for (int jj = 0; jj < NS; ++jj) {
-                        const int r = jj < 2 ? wl + 4 * jj : 8;
-                        float x[8];        // unscaled scores
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
-                            x[e] = own[jj][0][e];
-                            x[4 + e] = own[jj][1][e];
+                            x[jj][e] = own[jj][0][e];
+                            x[jj][4 + e] = own[jj][1][e];
                         }
+                    }
+#pragma unroll
+                    for (int jj = 0; jj < NS; ++jj) {
                         const bool fast = t0 + TS <= (T < s1 ? T : s1) && t0 >= rlo_max[jj];
                         if (!fast) {
 #pragma unroll
@@ -540,24 +567,38 @@ __global__ __launch_bounds__(THREADS, 1) void attn_kernel(AttnLaunch L) {
                                     vis = vis && jn < TV_MAX_NODES && ((rs[jj].anc >> (jn & 63)) & 1ull) &&
                                           (W == 0 || rs[jj].dep - sm.dep[jn & 63] < W);
                                 }
-                                x[e] = vis ? x[e] : -INFINITY;
+                                x[jj][e] = vis ? x[jj][e] : -INFINITY;
                             }
                         }
-                        // (rows past the tree are not masked on unmasked tiles: their Q is zero, so
-                        // their weights stay finite, and nothing reads their results)
-                        float mt = x[0];
+                    }
+                    // (rows past the tree are not masked on unmasked tiles: their Q is zero, so
+                    // their weights stay finite, and nothing reads their results)
+                    float mt[NS > 0 ? NS : 1];
 #pragma unroll
-                        for (int e = 1; e < 8; ++e) mt = fmaxf(mt, x[e]);
-                        // the row's 32 slots sit in the four lane groups: max over l, l^16, l^32
-                        const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(mt), __float_as_uint(mt), false, false);
-                        mt = fmaxf(__uint_as_float(s16[0]), __uint_as_float(s16[1]));
-                        const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt), false, false);
-                        mt = fmaxf(__uint_as_float(s32[0]), __uint_as_float(s32[1])) * rs[jj].sl2;
+                    for (int jj = 0; jj < NS; ++jj) {
+                        mt[jj] = x[jj][0];
+#pragma unroll
+                        for (int e = 1; e < 8; ++e) mt[jj] = fmaxf(mt[jj], x[jj][e]);
+                    }
+                    // the row's 32 slots sit in the four lane groups: max over l, l^16, l^32
+#pragma unroll
+                    for (int jj = 0; jj < NS; ++jj) {
+                        const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(mt[jj]), __float_as_uint(mt[jj]), false, false);
+                        mt[jj] = fmaxf(__uint_as_float(s16[0]), __uint_as_float(s16[1]));
+                    }
+#pragma unroll
+                    for (int jj = 0; jj < NS; ++jj) {
+                        const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt[jj]), __float_as_uint(mt[jj]), false, false);
+                        mt[jj] = fmaxf(__uint_as_float(s32[0]), __uint_as_float(s32[1])) * rs[jj].sl2;
+                    }
+#pragma unroll
+                    for (int jj = 0; jj < NS; ++jj) {
+                        const int r = jj < 2 ? wl + 4 * jj : 8;
                         // Lazy rescaling: P is taken against a reference max that moves only when
                         // the row max grows by more than 2^8 (so P <= 256); alpha is 1 otherwise.
-                        const bool grow = mt > rs[jj].m + 8.f;
+                        const bool grow = mt[jj] > rs[jj].m + 8.f;
                         const bool anyg = __builtin_amdgcn_ballot_w64(grow) != 0;
-                        const float mnew = grow ? mt : rs[jj].m;
+                        const float mnew = grow ? mt[jj] : rs[jj].m;
                         const float al = rs[jj].m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(rs[jj].m - mnew);
                         rs[jj].m = mnew;
                         const float m = mnew == -INFINITY ? 0.f : mnew;      // then every x is -inf
@@ -567,7 +608,7 @@ __global__ __launch_bounds__(THREADS, 1) void attn_kernel(AttnLaunch L) {
                         float ps = 0.f;
 #pragma unroll
                         for (int e = 0; e < 8; ++e) {
-                            pe[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[e], rs[jj].sl2, -m));
+                            pe[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[jj][e], rs[jj].sl2, -m));
                             ps += pe[e];
                         }
                         uint32_t ph[4], pl[4];
@@ -578,7 +619,6 @@ __global__ __launch_bounds__(THREADS, 1) void attn_kernel(AttnLaunch L) {
                         *reinterpret_cast<uint4*>(&sm.pbuf_lo[bufk][r][lane]) = make_uint4(pl[0], pl[1], pl[2], pl[3]);
                         if (g4 == 0) sm.alpha[bufk][r][l16] = al;          // row l16's factor
                         if (lane == 0) sm.grow[bufk][r] = anyg;
-                        __builtin_amdgcn_sched_barrier(0);
                     }
                 }
                 // copy V tile k+DV into the slot of tile k-2 (dequantised in step k-1; the PV
