@@ -340,23 +340,28 @@ __global__ __launch_bounds__(THREADS, 1) void attn_kernel(AttnLaunch L) {
     // the scoring waves copy V, so no wave reads a ring it has copies in flight for: waits are
     // explicit (wait_vm before the barrier that publishes a tile), never implied by a read.
     constexpr int NIK = (TS * KF::ROW + 1023) / 1024, NIV = (TS * VF::ROW + 1023) / 1024;
-    // instructions per tile issued by this wave (i = wl, wl + 4, ...): the same count for every
-    // tile, so a fixed number of tiles still in flight is a fixed vmcnt
-    const int cntk = (NIK - wl + 3) / 4, cntv = (NIV - wl + 3) / 4;
-    auto dma_tile = [&](const uint8_t* base, int rowbytes, int nch, uint8_t* slot, int tile) {
+    // Staging work of the scoring waves (V copies, K conversion).  When wave 0 scores three row
+    // tiles (more than 128 rows) it stages nothing and waves 1..3 share its part; otherwise
+    // every scoring wave takes a quarter.  A wave issues instructions i = first, first + step,
+    // ... of each tile: the same count for every tile, so a fixed number of tiles still in
+    // flight is a fixed vmcnt.
+    const bool has8 = RT > 8;
+    const int vfirst = has8 ? (wl == 0 ? NIV : wl - 1) : wl, vstep = has8 ? 3 : 4;
+    const int cntk = (NIK - wl + 3) / 4, cntv = vfirst < NIV ? (NIV - vfirst + vstep - 1) / vstep : 0;
+    auto dma_tile = [&](const uint8_t* base, int rowbytes, int nch, uint8_t* slot, int tile, int first, int step) {
         const int t0 = s0 + tile * TS;
         const int last = (a.Tcap - t0 < TS ? a.Tcap - t0 : TS) * rowbytes / 16 - 1;   // t0 < Tcap
         const uint8_t* src = base + static_cast<size_t>(t0) * rowbytes;
         const int ni = (TS * rowbytes + 1023) / 1024;
-        for (int i = wl; i < ni; i += 4) {
+        for (int i = first; i < ni; i += step) {
             int c = i * 64 + lane;
             c = c < nch ? c : nch - 1;
             c = c < last ? c : last;
             copy16_to_lds(src + c * 16, __builtin_amdgcn_readfirstlane(lds_address(slot + i * 1024)));
         }
     };
-    auto dma_k = [&](int tile) { dma_tile(kbase, KF::ROW, KCH, &ringk[tile % RK][0], tile); };
-    auto dma_v = [&](int tile) { dma_tile(vbase, VF::ROW, VCH, &ringv[tile % RV][0], tile); };
+    auto dma_k = [&](int tile) { dma_tile(kbase, KF::ROW, KCH, &ringk[tile % RK][0], tile, wl, 4); };
+    auto dma_v = [&](int tile) { dma_tile(vbase, VF::ROW, VCH, &ringv[tile % RV][0], tile, vfirst, vstep); };
     // Wait for a copied tile: `after` tiles copied since by this wave may stay in flight; a
     // count short of the steady state (the last tiles) waits for everything.
     auto wait_k = [&](int after) {
@@ -385,34 +390,49 @@ __global__ __launch_bounds__(THREADS, 1) void attn_kernel(AttnLaunch L) {
         }
     };
     // K integers of tile `tile` (raw rows in its ring slot) into the QK operand buffer
-    // kop[tile&1] and their block scales into kd[tile&1]: scoring wave w converts blocks 2w, 2w+1.
-    // Lane (g4, l16) of slot half st holds slot 16 st + l16, elements 8 g4 .. 8 g4 + 7 of the
-    // block: exactly the MFMA A operand of that (half, block), so the scoring waves read it
-    // back with one conflict-free 16-byte load per lane.
-    // Every LDS read of a conversion is issued before its first write (one round trip, not one
-    // per block); lanes g4 < 2 convert the scale of block 2w + g4.
-    auto convert_k = [&](int tile) {
+    // kop[tile&1] and their block scales into kd[tile&1], NB consecutive blocks from kb0 (odd
+    // iff ODD0) per wave: blocks 2w, 2w + 1, or with wave 0 not staging, {0,1,2}, {3,4,5},
+    // {6,7} for waves 1..3.  Lane (g4, l16) of slot half st holds slot 16 st + l16, elements
+    // 8 g4 .. 8 g4 + 7 of the block: exactly the MFMA A operand of that (half, block), so the
+    // scoring waves read it back with one conflict-free 16-byte load per lane.  Every LDS read
+    // of a conversion is issued before its first write (one round trip, not one per block);
+    // lanes g4 < NB convert the scale of block kb0 + g4.
+    auto convert_blocks = [&](int tile, int kb0, auto nbc, auto odd0c) {
+        constexpr int NB = decltype(nbc)::value;
+        constexpr bool ODD0 = decltype(odd0c)::value;
         const int buf = tile & 1;
-        const int kbs = 2 * wl + (g4 & 1);
-        KRaw<false> re[2];
-        KRaw<true> ro[2];
+        const int kbs = kb0 + (g4 < NB ? g4 : NB - 1);
+        KRaw<ODD0> r0[2], r2[2];
+        KRaw<!ODD0> r1[2];
         _Float16 sc[2];
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
             const uint8_t* krow = &ringk[tile % RK][(16 * st + l16) * KF::ROW];
-            re[st] = load_kraw<KT, false>(krow, 2 * wl, g4);
-            ro[st] = load_kraw<KT, true>(krow, 2 * wl + 1, g4);
+            r0[st] = load_kraw<KT, ODD0>(krow, kb0, g4);
+            r1[st] = load_kraw<KT, !ODD0>(krow, kb0 + 1, g4);
+            if constexpr (NB > 2) r2[st] = load_kraw<KT, ODD0>(krow, kb0 + 2, g4);
             sc[st] = block_scale(krow + kbs * KF::BLK);
         }
-        // (the scales are used only by lanes g4 < 2; keep their loads with the others rather
+        // (the scales are used only by lanes g4 < NB; keep their loads with the others rather
         // than inside the branch that writes them)
         asm volatile("" : : "v"(sc[0]), "v"(sc[1]));
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
-            sm.kop[buf][st][2 * wl][lane] = kraw_ints8<KT, false>(re[st], g4);
-            sm.kop[buf][st][2 * wl + 1][lane] = kraw_ints8<KT, true>(ro[st], g4);
-            if (g4 < 2) sm.kd[buf][kbs][16 * st + l16] = static_cast<float>(sc[st]);
+            sm.kop[buf][st][kb0][lane] = kraw_ints8<KT, ODD0>(r0[st], g4);
+            sm.kop[buf][st][kb0 + 1][lane] = kraw_ints8<KT, !ODD0>(r1[st], g4);
+            if constexpr (NB > 2) sm.kop[buf][st][kb0 + 2][lane] = kraw_ints8<KT, ODD0>(r2[st], g4);
+            if (g4 < NB) sm.kd[buf][kbs][16 * st + l16] = static_cast<float>(sc[st]);
         }
+    };
+    auto convert_k = [&](int tile) {
+        using N2 = std::integral_constant<int, 2>;
+        using N3 = std::integral_constant<int, 3>;
+        using EV = std::integral_constant<bool, false>;
+        using OD = std::integral_constant<bool, true>;
+        if (!has8) convert_blocks(tile, 2 * wl, N2{}, EV{});
+        else if (wl == 1) convert_blocks(tile, 0, N3{}, EV{});
+        else if (wl == 2) convert_blocks(tile, 3, N3{}, OD{});
+        else if (wl == 3) convert_blocks(tile, 6, N2{}, EV{});
     };
 
     // Prologue: K tiles 0 .. DK+1 and V tiles 0 .. DV-1 in flight; K tile 0 converted.
@@ -486,7 +506,6 @@ __global__ __launch_bounds__(THREADS, 1) void attn_kernel(AttnLaunch L) {
             rlo_max[j] = __builtin_amdgcn_readfirstlane(rm);
         }
         const bool own0 = wl < RT, own1 = wl + 4 < RT;       // wave-uniform
-        const bool has8 = RT > 8;
 
         // The tile loop of one scoring wave, specialised on what the wave holds so that the
         // inner loop has no branches: NJ row tiles among w, w + 4 (0..2) and, for wave 0, row
