@@ -141,3 +141,21 @@ def test_plain_verify_waits_for_its_row_copies():
         assert after >= allowed, f"{name}: waits for vmcnt({allowed}) with only {after} loads after the copies"
         checked += 1
     assert checked > 0
+
+
+def test_attention_kernels_keep_everything_in_registers():
+    """No attention kernel touches scratch memory.  Its PV accumulators are a register array
+    indexed by row tile; a loop over row tiles that the compiler cannot unroll completely (an
+    early exit on the run-time row-tile count, say) turns them into scratch memory, which
+    keeps the results right and makes the kernel several times slower."""
+    obj = os.path.join(OBJDIR, "attn_tree.hip.o")
+    if not os.path.exists(obj):
+        pytest.skip("needs the built attention object")
+    checked = 0
+    for name, ins in _functions(_disassemble(obj)).items():
+        if "attn_kernel" not in name:
+            continue
+        bad = [x for x in ins if x.startswith(("scratch_", "buffer_load", "buffer_store"))]
+        assert not bad, f"{name}: {len(bad)} scratch accesses, first {bad[0]}"
+        checked += 1
+    assert checked >= 8

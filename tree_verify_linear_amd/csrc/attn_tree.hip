@@ -85,6 +85,14 @@ constexpr int SLOT = (TS * MAXROW + 1023) / 1024 * 1024;   // 9 KiB: whole wave 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
+// LDS offset of a generic pointer into a __shared__ array: its low 32 bits (a generic LDS
+// address is the shared aperture base plus the offset).  Taken this way rather than by a cast
+// to the LDS address space, whose null check this compiler has been seen to miscompile
+// ("operand has incorrect register class" on the aperture register) in some inlining contexts.
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
+}
+
 __device__ __forceinline__ f32x4 mfma_f16(const f16x8& a, const f16x8& b, const f32x4& c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
@@ -205,7 +213,8 @@ struct AttnLaunch {
     int G;              // query heads per KV head
     int rows;           // N * G
     int rows_pad;       // rows rounded up to row tiles of 16, per KV head
-    int rblocks;        // row blocks of ROWS_PER_BLOCK rows
+    int rblocks;        // row blocks (at most ROWS_PER_BLOCK rows each)
+    int rtb;            // row tiles per row block (<= RTMAX; the last block may hold fewer)
     int nsplit;         // KV splits per (sequence, KV head)
     int chunk;          // slots per split (multiple of TS)
     float* opart;       // [B][Hkv][nsplit][rows_pad][D]
@@ -315,8 +324,8 @@ __global__ __launch_bounds__(THREADS, 1) void attn_kernel(AttnLaunch L) {
     const int s0 = lo_b + split * L.chunk;
     const int s1 = s0 + L.chunk < hi_b ? s0 + L.chunk : hi_b;
     const int ntiles = s1 > s0 ? (s1 - s0 + TS - 1) / TS : 0;
-    const int rowbase = rb * ROWS_PER_BLOCK;
-    const int RT = FULL ? RTMAX : ((L.rows - rowbase + 15) / 16 < RTMAX ? (L.rows - rowbase + 15) / 16 : RTMAX);
+    const int rowbase = rb * L.rtb * 16;
+    const int RT = FULL ? RTMAX : ((L.rows - rowbase + 15) / 16 < L.rtb ? (L.rows - rowbase + 15) / 16 : L.rtb);
     const size_t part = (static_cast<size_t>(b) * a.Hkv + kvh) * L.nsplit + split;
 
     // tree metadata (depth, ancestor sets) for this sequence
@@ -357,7 +366,7 @@ __global__ __launch_bounds__(THREADS, 1) void attn_kernel(AttnLaunch L) {
             int c = i * 64 + lane;
             c = c < nch ? c : nch - 1;
             c = c < last ? c : last;
-            copy16_to_lds(src + c * 16, __builtin_amdgcn_readfirstlane(lds_address(slot + i * 1024)));
+            copy16_to_lds(src + c * 16, __builtin_amdgcn_readfirstlane(lds_offset(slot + i * 1024)));
         }
     };
     auto dma_k = [&](int tile) { dma_tile(kbase, KF::ROW, KCH, &ringk[tile % RK][0], tile, wl, 4); };
@@ -889,7 +898,7 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(AttnLaunch L) {
 // parallelism).  Depends only on host-known sizes (n_past lives on the device), using the
 // widest visible span.
 struct SplitPlan {
-    int G, rows, rows_pad, rblocks, nsplit, chunk;
+    int G, rows, rows_pad, rblocks, rtb, nsplit, chunk;
 };
 SplitPlan plan_splits(int B, int N, int Hq, int Hkv, int Tcap, int window, int cus) {
     SplitPlan p;
@@ -897,6 +906,8 @@ SplitPlan plan_splits(int B, int N, int Hq, int Hkv, int Tcap, int window, int c
     p.rows = N * p.G;
     p.rows_pad = (p.rows + 15) / 16 * 16;
     p.rblocks = (p.rows + ROWS_PER_BLOCK - 1) / ROWS_PER_BLOCK;
+    // the row tiles spread evenly over the blocks (240 rows: 8 + 7 tiles, not 9 + 6)
+    p.rtb = (p.rows_pad / 16 + p.rblocks - 1) / p.rblocks;
     long long span = window ? static_cast<long long>(window) - 1 + N : Tcap;
     if (span > Tcap) span = Tcap;
     if (span < 1) span = 1;
@@ -921,7 +932,7 @@ size_t workspace_for(const SplitPlan& p, int B, int Hkv, int D_) {
 
 template <int KT, int VT>
 void launch_pair(const AttnLaunch& L, unsigned wgs, hipStream_t stream) {
-    const bool full = L.rows - (L.rblocks - 1) * ROWS_PER_BLOCK > (RTMAX - 1) * 16;
+    const bool full = L.rtb == RTMAX && L.rows - (L.rblocks - 1) * ROWS_PER_BLOCK > (RTMAX - 1) * 16;
     if (full) hipLaunchKernelGGL((attn_kernel<KT, VT, true>), dim3(wgs), dim3(THREADS), 0, stream, L);
     else hipLaunchKernelGGL((attn_kernel<KT, VT, false>), dim3(wgs), dim3(THREADS), 0, stream, L);
 }
@@ -978,6 +989,7 @@ int launch_attn(const AttnArgs& a, hipStream_t stream) {
     L.rows = p.rows;
     L.rows_pad = p.rows_pad;
     L.rblocks = p.rblocks;
+    L.rtb = p.rtb;
     L.nsplit = p.nsplit;
     L.chunk = p.chunk;
     const size_t parts = static_cast<size_t>(a.B) * a.Hkv * p.nsplit * p.rows_pad;
