@@ -23,10 +23,11 @@
 //     each block's fp16 scale as fp32).  The QK^T product of each 32-element block is one
 //     v_mfma_f32_16x16x32_f16 (K integers x Q), and the block's per-slot scale is applied to
 //     the fp32 result: scores are exact products summed in fp32.
-//   * Scoring waves (4): wave w owns row tiles w and w + 4 over the whole head dimension, so
-//     no partial score leaves the wave.  Row tile 8 (more than 128 rows) is the exception:
-//     waves 1..3 compute its partial scores over blocks {0,1,2}, {3,4,5}, {6,7} and wave 0
-//     adds them and runs its softmax.  Each wave masks its rows, runs an online softmax in
+//   * Scoring waves (4): wave w owns row tiles w and w + 4 over the whole head dimension, and
+//     wave 0 also row tile 8 (more than 128 rows; it then leaves its share of the K
+//     conversion and V copies to waves 1..3), so no partial score leaves a wave.  The row
+//     tiles of a sequence's rows are spread evenly over its row blocks.  Each wave masks its
+//     rows, runs an online softmax in
 //     the exp2 domain (the reference max moves only when a row max grows by more than 2^8; O
 //     is then rescaled) and writes P as an fp16 pair hi + lo (P to about 2^-22) to LDS in the
 //     PV A-operand layout (the score layout of S^T already is that layout).
