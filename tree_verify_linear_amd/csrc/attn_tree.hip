@@ -832,10 +832,11 @@ __global__ __launch_bounds__(THREADS, 1) void attn_kernel(AttnLaunch L) {
     }
 }
 
-// Merges the splits of one row: O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.  The max and
-// the sum run across the wave's lanes (split s on lane s mod 64); the output loop keeps eight
-// splits' loads in flight per lane, so the merge costs a few memory round trips, not one per
-// split.
+// Merges the splits of one row: O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.  Lane t
+// takes splits t, t + 64, ... and merges their (max, sum) pairs online, so one pass of loads
+// gives the row's M and sum (one memory round trip up to 64 splits); the wave then broadcasts
+// each split's weight from the lane that holds it and loads the partial outputs of up to 32
+// splits at once (four columns per lane), so the merge costs two or three round trips.
 __global__ __launch_bounds__(64) void attn_combine_kernel(AttnLaunch L) {
     const AttnArgs& a = L.a;
     const int t = threadIdx.x;
@@ -844,43 +845,53 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(AttnLaunch L) {
     wg /= L.rows;
     const int kvh = wg % a.Hkv;
     const int b = wg / a.Hkv;
-    const int n = clampi(a.n_nodes[b], 0, a.N);
     const int node = r / L.G, hh = r - node * L.G;
-    if (node >= n) return;
     const size_t p0 = (static_cast<size_t>(b) * a.Hkv + kvh) * L.nsplit;
     const int ns = L.nsplit;
-    float M = -INFINITY;
-    for (int s = t; s < ns; s += 64) M = fmaxf(M, L.mpart[(p0 + s) * L.rows_pad + r]);
+    // pass 1: this lane's splits, merged online (the first one is this lane's own split t)
+    float mt = -INFINITY, lt = 0.f;
+    for (int s = t; s < ns; s += 64) {
+        const float ms = L.mpart[(p0 + s) * L.rows_pad + r];
+        const float ls = L.lpart[(p0 + s) * L.rows_pad + r];
+        if (ms == -INFINITY) continue;
+        const float mn = fmaxf(mt, ms);
+        lt = (mt == -INFINITY ? 0.f : lt * exp2f(mt - mn)) + ls * exp2f(ms - mn);
+        mt = mn;
+    }
+    float M = mt;
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-    float Lsum = 0.f;
-    if (M != -INFINITY) {
-        for (int s = t; s < ns; s += 64) {
-            const float ms = L.mpart[(p0 + s) * L.rows_pad + r];
-            if (ms != -INFINITY) Lsum += exp2f(ms - M) * L.lpart[(p0 + s) * L.rows_pad + r];
-        }
-    }
+    float Lsum = M == -INFINITY || mt == -INFINITY ? 0.f : lt * exp2f(mt - M);
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) Lsum += __shfl_xor(Lsum, o);
+    const int n = clampi(a.n_nodes[b], 0, a.N);
+    if (node >= n) return;
+    // weight of split t (lane t's first split); splits past 64 reload their max
+    const float m0 = t < ns ? L.mpart[(p0 + t) * L.rows_pad + r] : -INFINITY;
+    const float w0 = m0 == -INFINITY || M == -INFINITY ? 0.f : exp2f(m0 - M);
     float acc[D / 64];
 #pragma unroll
     for (int k = 0; k < D / 64; ++k) acc[k] = 0.f;
     if (M != -INFINITY) {
-        constexpr int U = 8;
+        constexpr int U = 32;
         for (int s0 = 0; s0 < ns; s0 += U) {
-            float ms[U], ov[U][D / 64];
+            float ov[U][D / 64];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int s = s0 + u < ns ? s0 + u : ns - 1;
-                ms[u] = L.mpart[(p0 + s) * L.rows_pad + r];
                 const float* op = L.opart + ((p0 + s) * L.rows_pad + r) * D;
 #pragma unroll
                 for (int k = 0; k < D / 64; ++k) ov[u][k] = op[k * 64 + t];
             }
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                if (s0 + u >= ns || ms[u] == -INFINITY) continue;
-                const float w = exp2f(ms[u] - M);
+                const int s = s0 + u;
+                if (s >= ns) break;
+                float w = __shfl(w0, s & 63);
+                if (s >= 64) {
+                    const float ms = L.mpart[(p0 + s) * L.rows_pad + r];
+                    w = ms == -INFINITY ? 0.f : exp2f(ms - M);
+                }
 #pragma unroll
                 for (int k = 0; k < D / 64; ++k) acc[k] += w * ov[u][k];
             }
