@@ -84,6 +84,18 @@ def test_ragged_history_and_other_grouping():
     check(A, "ragged")
 
 
+@pytest.mark.parametrize("nodes", [64, 50])
+def test_many_row_blocks(nodes):
+    """Trees whose rows (nodes x 6 query heads) need three row blocks: 384 rows as 8 + 8 + 8
+    row tiles, 300 rows as 7 + 7 + 5; every row against the oracle, window 0 and a short
+    window."""
+    rng = np.random.default_rng(11 + nodes)
+    parents = [tree_ddtree(rng, budget=nodes, max_depth=20, topk=6), tree_chain(nodes)]
+    for window in (0, 37):
+        A = gen_attn(83, parents, 24, 4, 256, [300, 129], "q8_0", "q4_0", window)
+        check(A, f"{nodes} nodes w{window}")
+
+
 @pytest.mark.parametrize("window", [0, 2048])
 def test_long_context_all_rows(window):
     """131072 committed Q4_0 slots (K and V), window 0 and 2048: every row of the layer (22
