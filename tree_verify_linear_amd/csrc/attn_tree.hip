@@ -25,7 +25,7 @@
 //     the fp32 result: scores are exact products summed in fp32.
 //   * Scoring waves (4): wave w owns row tiles w and w + 4 over the whole head dimension, and
 //     wave 0 also row tile 8 (more than 128 rows; it then leaves its share of the K
-//     conversion and V copies to waves 1..3), so no partial score leaves a wave.  The row
+//     conversion to waves 1..3), so no partial score leaves a wave.  The row
 //     tiles of a sequence's rows are spread evenly over its row blocks.  Each wave masks its
 //     rows, runs an online softmax in
 //     the exp2 domain (the reference max moves only when a row max grows by more than 2^8; O
@@ -350,28 +350,27 @@ __global__ __launch_bounds__(THREADS, 1) void attn_kernel(AttnLaunch L) {
     // the scoring waves copy V, so no wave reads a ring it has copies in flight for: waits are
     // explicit (wait_vm before the barrier that publishes a tile), never implied by a read.
     constexpr int NIK = (TS * KF::ROW + 1023) / 1024, NIV = (TS * VF::ROW + 1023) / 1024;
-    // Staging work of the scoring waves (V copies, K conversion).  When wave 0 scores three row
-    // tiles (more than 128 rows) it stages nothing and waves 1..3 share its part; otherwise
-    // every scoring wave takes a quarter.  A wave issues instructions i = first, first + step,
-    // ... of each tile: the same count for every tile, so a fixed number of tiles still in
-    // flight is a fixed vmcnt.
+    // Staging work of the scoring waves: the V copies (a quarter each) and the K conversion
+    // (a quarter each, except that a wave 0 scoring three row tiles, with more than 128 rows,
+    // leaves its K blocks to waves 1..3).  A wave issues copy instructions i = w, w + 4, ... of
+    // each tile: the same count for every tile, so a fixed number of tiles still in flight is
+    // a fixed vmcnt.
     const bool has8 = RT > 8;
-    const int vfirst = has8 ? (wl == 0 ? NIV : wl - 1) : wl, vstep = has8 ? 3 : 4;
-    const int cntk = (NIK - wl + 3) / 4, cntv = vfirst < NIV ? (NIV - vfirst + vstep - 1) / vstep : 0;
-    auto dma_tile = [&](const uint8_t* base, int rowbytes, int nch, uint8_t* slot, int tile, int first, int step) {
+    const int cntk = (NIK - wl + 3) / 4, cntv = (NIV - wl + 3) / 4;
+    auto dma_tile = [&](const uint8_t* base, int rowbytes, int nch, uint8_t* slot, int tile) {
         const int t0 = s0 + tile * TS;
         const int last = (a.Tcap - t0 < TS ? a.Tcap - t0 : TS) * rowbytes / 16 - 1;   // t0 < Tcap
         const uint8_t* src = base + static_cast<size_t>(t0) * rowbytes;
         const int ni = (TS * rowbytes + 1023) / 1024;
-        for (int i = first; i < ni; i += step) {
+        for (int i = wl; i < ni; i += 4) {
             int c = i * 64 + lane;
             c = c < nch ? c : nch - 1;
             c = c < last ? c : last;
             copy16_to_lds(src + c * 16, __builtin_amdgcn_readfirstlane(lds_offset(slot + i * 1024)));
         }
     };
-    auto dma_k = [&](int tile) { dma_tile(kbase, KF::ROW, KCH, &ringk[tile % RK][0], tile, wl, 4); };
-    auto dma_v = [&](int tile) { dma_tile(vbase, VF::ROW, VCH, &ringv[tile % RV][0], tile, vfirst, vstep); };
+    auto dma_k = [&](int tile) { dma_tile(kbase, KF::ROW, KCH, &ringk[tile % RK][0], tile); };
+    auto dma_v = [&](int tile) { dma_tile(vbase, VF::ROW, VCH, &ringv[tile % RV][0], tile); };
     // Wait for a copied tile: `after` tiles copied since by this wave may stay in flight; a
     // count short of the steady state (the last tiles) waits for everything.
     auto wait_k = [&](int after) {
